@@ -1,0 +1,196 @@
+/*
+ * lrc.h -- C ABI of liblrc.so: chunked prefill of recurrent sequence mixers
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Each kernel takes an incoming recurrent state and a chunk of at most
+ * LRC_MAX_ROWS rows, writes every row's output and the outgoing state, and
+ * agrees with the token-by-token recurrence.  The prefill drivers run whole
+ * prompts of any length, packed one after another along the row axis, as
+ * consecutive chunks of LRC_MAX_ROWS rows with the state carried between
+ * chunks on the device.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller, except where an
+ *    argument is marked "host".  Tensors are dense, row-major, innermost
+ *    dimension last, and 16-byte aligned.  Outputs must not overlap inputs
+ *    unless an argument says it may alias.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *    asynchronous on that stream, allocates no memory and keeps no state
+ *    between calls.  Calls on distinct buffers are thread-safe.
+ *  - All arguments are validated on the host before anything is enqueued,
+ *    without any HIP call.  On a validation error nothing is launched, no
+ *    buffer is written, and lrc_last_error() (thread-local) explains it.
+ *  - If a launch fails, the call returns LRC_ERR_LAUNCH after synchronizing
+ *    the stream (so no queued work still reads the caller's buffers).  The
+ *    recurrent states are then undefined and the caller must reset them;
+ *    there is no rollback.
+ *  - Rows = 0 (or an empty batch) is valid: outputs are untouched and the
+ *    outgoing state equals the incoming one.
+ *
+ * Sources (page title, section):
+ *  [mamba] "perf(mamba): prefill text prompts in multi-token chunks",
+ *          Implementation.
+ *  [rwkv]  "perf(rwkv): prefill text prompts in multi-token chunks",
+ *          Implementation.
+ *  [qwen]  "perf(qwen3_5): prefill text prompts in multi-token chunks",
+ *          Implementation.
+ */
+#ifndef LRC_H
+#define LRC_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest chunk: the pages bound a chunk at 64 rows (the static padding of
+   the triangular solve [qwen]; the doubling scan [mamba]; the [S+1, S]
+   exponent tensor [rwkv]).  A chunk call with more rows is rejected. */
+#define LRC_MAX_ROWS 64
+/* Largest number of prompts in one prefill-driver call (prompt offsets
+   travel to the device by value, inside the kernel arguments). */
+#define LRC_MAX_PROMPTS 256
+/* Largest depthwise conv width. */
+#define LRC_MAX_CONV_K 8
+
+typedef enum {
+    LRC_OK = 0,
+    LRC_ERR_NULL = 1,   /* a required pointer is NULL */
+    LRC_ERR_ROWS = 2,   /* chunk rows < 0 or > LRC_MAX_ROWS, or a prompt length < 0 */
+    LRC_ERR_SHAPE = 3,  /* a size is outside the supported range */
+    LRC_ERR_DTYPE = 4,  /* unsupported element type for this call */
+    LRC_ERR_ALIGN = 5,  /* a tensor pointer is not 16-byte aligned */
+    LRC_ERR_LAUNCH = 6, /* a HIP launch or runtime call failed */
+    LRC_ERR_ALIAS = 7   /* an output overlaps an input it may not alias */
+} lrc_status;
+
+typedef enum { LRC_F32 = 0, LRC_BF16 = 1 } lrc_dtype;
+
+/* ------------------------------------------------------------------------
+ * K0  Depthwise causal short conv over rows  [mamba], [qwen]
+ *
+ * The window of row t is the previous K-1 rows followed by the chunk rows:
+ * xt = concat(state_in[K-1 rows], x[S rows]) along time, and
+ *     y[t][c] = bias[c] + sum_{j<K} w[c][j] * xt[t+j][c]
+ * (a causal cross-correlation: tap K-1 multiplies the current row).  No
+ * activation.  The new conv state is the last K-1 rows of xt; for S < K-1
+ * that keeps K-1-S of the old state rows.
+ *
+ *  x, y        [B, S, C]   dtype (F32, or BF16 with FP32 accumulation)
+ *  state_in    [B, K-1, C] dtype
+ *  state_out   [B, K-1, C] dtype; may alias state_in (in-place update)
+ *  w           [C, K] float; bias [C] float or NULL
+ *  1 <= K <= LRC_MAX_CONV_K, C >= 1, 0 <= S <= LRC_MAX_ROWS, B >= 0.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_conv_rows(const void* x, void* y, const void* state_in, void* state_out,
+                         const float* w, const float* bias, int B, int S, int C, int K,
+                         lrc_dtype dt, void* stream);
+
+/* K0 driver.  x, y [R, C] hold P prompts packed along rows, prompt p owning
+   lens_host[p] consecutive rows (R = sum of lens).  state [P, K-1, C] is
+   read and updated in place.  Same result as lrc_conv_rows over consecutive
+   64-row chunks of every prompt.  1 <= P <= LRC_MAX_PROMPTS. */
+lrc_status lrc_conv_prefill(const void* x, void* y, void* state, const float* w, const float* bias,
+                            const int* lens_host, int P, int C, int K, lrc_dtype dt, void* stream);
+
+/* ------------------------------------------------------------------------
+ * K1  Selective scan over rows  [mamba]
+ *
+ * For every state element e (E = D * N of them) independently:
+ *     h_t = a_t h_{t-1} + b_t,  t = 0 .. S-1, starting from h0,
+ * evaluated per chunk as a log-step parallel (doubling) scan of the pairs
+ * (a, b) under (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) with the carried
+ * state applied last: h_t = A_t h0 + B_t.  All FP32.  Output is every h_t;
+ * the outgoing state is h at the last row.
+ *
+ *  a, b, h     [B, S, D, N] float
+ *  h0          [B, D, N] float (incoming)
+ *  hS          [B, D, N] float (outgoing); may alias h0
+ *  D, N >= 1, 0 <= S <= LRC_MAX_ROWS, B >= 0.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_scan_rows(const float* a, const float* b, float* h, const float* h0, float* hS,
+                         int B, int S, int D, int N, void* stream);
+
+/* K1 driver: a, b, h [R, D, N] packed rows; state [P, D, N] in place. */
+lrc_status lrc_scan_prefill(const float* a, const float* b, float* h, float* state,
+                            const int* lens_host, int P, int D, int N, void* stream);
+
+/* ------------------------------------------------------------------------
+ * K2  RWKV-4 WKV over rows  [rwkv]
+ *
+ * Per channel c the state keeps A = num e^max and B = den e^max of
+ * A_t = e^w A_{t-1} + e^{k_t} v_t,  B_t = e^w B_{t-1} + e^{k_t}   (w < 0),
+ * and row t of a chunk outputs
+ *     wkv_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t}).
+ * Relative to the incoming state, row t combines three kinds of exponents:
+ * max_0 + t w (the state), k_i + (t-1-i) w for earlier rows i < t, and the
+ * bonus u + k_t; every row shifts by its largest exponent before exp.  The
+ * outgoing triple is the "row S" of that form: (num, den, max) with max the
+ * largest exponent of the rows seen.  A fresh channel is (0, 0, -1e38).
+ *
+ *  k, v, wkv   [B, S, C] float
+ *  w, u        [C] float (w < 0)
+ *  num, den, mx [B, C] float, read and updated in place
+ *  C >= 1, 0 <= S <= LRC_MAX_ROWS, B >= 0.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_wkv4_rows(const float* k, const float* v, const float* w, const float* u, float* wkv,
+                         float* num, float* den, float* mx, int B, int S, int C, void* stream);
+
+/* K2 driver: k, v, wkv [R, C] packed rows; num, den, mx [P, C] in place. */
+lrc_status lrc_wkv4_prefill(const float* k, const float* v, const float* w, const float* u, float* wkv,
+                            float* num, float* den, float* mx, const int* lens_host, int P, int C,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * K3  Gated DeltaNet chunk  [qwen]
+ *
+ * For value head h (key head h / (Hv/Hk)) and a chunk of S rows with
+ * gamma_t = sum_{i<=t} g_i (chunk-local, inclusive) and Gamma = e^gamma:
+ *   A_ij = beta_i e^{gamma_i - gamma_j} k_i.k_j   (j < i), else 0
+ *   (I + A) U = diag(beta) V - diag(beta Gamma) K S_0
+ *   O   = diag(Gamma) Q S_0 + (e^{gamma_t - gamma_i} q_t.k_i)_{i <= t} U
+ *   S_S = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
+ * gamma_S is the last cumulative sum.  I + A is inverted on a 64-row
+ * padding (padded rows identity): 8x8 diagonal blocks by the Neumann
+ * product (I+N)^-1 = (I-N)(I+N^2)(I+N^4), then 2x2 block inversion level by
+ * level (16, 32, 64 rows).  Decay factors are formed element by element from
+ * gamma differences, never as ratios of Gamma.  No scale is applied to q.
+ *
+ *  q, k        [B, S, Hk, dk]  dtype
+ *  v           [B, S, Hv, dv]  dtype
+ *  beta, g     [B, S, Hv]      float (g <= 0)
+ *  o           [B, S, Hv, dv]  float
+ *  S_in        [B, Hv, dk, dv] float
+ *  S_out       [B, Hv, dk, dv] float; may alias S_in
+ *  dk, dv in {32, 64, 128}; Hk >= 1; Hv a multiple of Hk.
+ *  dtype F32: FP32 arithmetic throughout.  dtype BF16: bf16 q/k/v, FP32
+ *  state, decays, inverse and accumulation.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_gdn_chunk(const void* q, const void* k, const void* v, const float* beta,
+                         const float* g, float* o, const float* S_in, float* S_out, int B, int S,
+                         int Hk, int Hv, int dk, int dv, lrc_dtype dt, void* stream);
+
+/* K3 driver: q, k [R, Hk, dk], v [R, Hv, dv], beta, g [R, Hv], o [R, Hv, dv]
+   packed rows; state [P, Hv, dk, dv] in place. */
+lrc_status lrc_gdn_prefill(const void* q, const void* k, const void* v, const float* beta,
+                           const float* g, float* o, float* state, const int* lens_host, int P,
+                           int Hk, int Hv, int dk, int dv, lrc_dtype dt, void* stream);
+
+/* The triangular inverse of K3 on its own, at the precision K3 uses (FP32):
+   T = (I + strictly_lower(A))^-1 for `batch` matrices of n x n, n <= 64,
+   padded to 64 rows with identity.  A, T [batch, n, n] float; T must not
+   overlap A.  [qwen] */
+lrc_status lrc_unit_lower_inverse(const float* A, float* T, int batch, int n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+const char* lrc_status_string(lrc_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* lrc_last_error(void);
+/* (major << 16) | (minor << 8) | patch */
+int lrc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LRC_H */

@@ -1,0 +1,47 @@
+// Internal declarations shared by the HIP sources of liblrc.so.
+// Not installed; the public surface is include/lrc.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lrc.h"
+
+namespace lrc {
+
+// Prompt layout of one launch, passed to kernels by value.  Either every
+// prompt has `uniform` rows and prompt p starts at row p * uniform, or
+// (uniform < 0) prompt p owns rows [row_off[p], row_off[p + 1]).  `order`
+// lists prompt indices longest first; kernels map blockIdx.y to order[y] so
+// that the longest sequential chains are dispatched first.
+struct Batch {
+    int P;
+    int uniform;
+    int row_off[LRC_MAX_PROMPTS + 1];
+    int order[LRC_MAX_PROMPTS];
+};
+
+__host__ __device__ inline int batch_prompt(const Batch& b, int slot) {
+    return b.uniform >= 0 ? slot : b.order[slot];
+}
+__host__ __device__ inline int batch_row0(const Batch& b, int p) {
+    return b.uniform >= 0 ? p * b.uniform : b.row_off[p];
+}
+__host__ __device__ inline int batch_len(const Batch& b, int p) {
+    return b.uniform >= 0 ? b.uniform : b.row_off[p + 1] - b.row_off[p];
+}
+
+// Kernel launchers (one per op), defined next to their kernels.  They
+// assume validated arguments and return the launch status.
+hipError_t launch_conv(const void* x, void* y, const void* state_in, void* state_out, const float* w,
+                       const float* bias, const Batch& bt, int C, int K, lrc_dtype dt, hipStream_t st);
+hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt,
+                       long E, hipStream_t st);
+hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
+                       float* den, float* mx, const Batch& bt, int C, hipStream_t st);
+hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
+                      const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
+                      lrc_dtype dt, hipStream_t st);
+hipError_t launch_unit_lower_inverse(const float* A, float* T, int batch, int n, hipStream_t st);
+
+}  // namespace lrc

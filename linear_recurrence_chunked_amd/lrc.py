@@ -1,0 +1,255 @@
+"""ctypes binding of liblrc.so (include/lrc.h), one Python function per C entry point.
+
+Argument marshalling only: each function checks that the torch tensors it is
+given are CUDA (HIP) tensors of the right dtype, contiguous and of matching
+shapes, reads the sizes off them, and passes raw device pointers and the
+current stream to the C ABI.  Outputs are caller-allocated tensors, written in
+place.  Every step of the computation runs in the HIP kernels; there is no
+fallback.  Importing this module raises if liblrc.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblrc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m linear_recurrence_chunked_amd.build` "
+        "(hipcc, gfx950). There is no CPU fallback.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+MAX_ROWS = 64
+MAX_PROMPTS = 256
+MAX_CONV_K = 8
+F32, BF16 = 0, 1
+
+STATUS = {0: "LRC_OK", 1: "LRC_ERR_NULL", 2: "LRC_ERR_ROWS", 3: "LRC_ERR_SHAPE", 4: "LRC_ERR_DTYPE",
+          5: "LRC_ERR_ALIGN", 6: "LRC_ERR_LAUNCH", 7: "LRC_ERR_ALIAS"}
+
+_P, _I, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int
+_IP = ctypes.POINTER(ctypes.c_int)
+
+_SIGS = {
+    "lrc_conv_rows": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P],
+    "lrc_conv_prefill": [_P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _P],
+    "lrc_scan_rows": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "lrc_scan_prefill": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
+    "lrc_wkv4_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "lrc_wkv4_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _P],
+    "lrc_gdn_chunk": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P],
+    "lrc_gdn_prefill": [_P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _I, _I, _P],
+    "lrc_unit_lower_inverse": [_P, _P, _I, _I, _P],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _S
+lib.lrc_status_string.argtypes = [_S]
+lib.lrc_status_string.restype = ctypes.c_char_p
+lib.lrc_last_error.argtypes = []
+lib.lrc_last_error.restype = ctypes.c_char_p
+lib.lrc_version.argtypes = []
+lib.lrc_version.restype = ctypes.c_int
+
+
+class LrcError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LrcError(status, lib.lrc_last_error().decode())
+
+
+def version() -> tuple[int, int, int]:
+    v = lib.lrc_version()
+    return (v >> 16) & 0xff, (v >> 8) & 0xff, v & 0xff
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(*ts: torch.Tensor | None) -> None:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("liblrc takes device tensors only (no CPU path)")
+        if not t.is_contiguous():
+            raise ValueError("liblrc takes contiguous tensors only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, dtype, shape, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _lens(lens):
+    lens = [int(x) for x in lens]
+    return (ctypes.c_int * len(lens))(*lens), len(lens), sum(max(x, 0) for x in lens)
+
+
+# ------------------------------------------------------------------ K0 conv
+def conv_rows(x, y, state_in, state_out, w, bias=None):
+    """x, y [B, S, C]; state_in, state_out [B, K-1, C] (may be the same tensor); w [C, K] f32."""
+    _dev(x, y, state_in, state_out, w, bias)
+    B, S, C = x.shape
+    K = w.shape[1]
+    _need(y, x.dtype, x.shape, "y")
+    _need(w, torch.float32, (C, K), "w")
+    _need(state_in, x.dtype, (B, K - 1, C), "state_in")
+    _need(state_out, x.dtype, (B, K - 1, C), "state_out")
+    if bias is not None:
+        _need(bias, torch.float32, (C,), "bias")
+    _check(lib.lrc_conv_rows(_ptr(x), _ptr(y), _ptr(state_in), _ptr(state_out), _ptr(w), _ptr(bias),
+                             B, S, C, K, _dtype_code(x), _stream(x)))
+
+
+def conv_prefill(x, y, state, w, lens, bias=None):
+    """x, y [R, C] packed rows of len(lens) prompts; state [P, K-1, C] updated in place."""
+    _dev(x, y, state, w, bias)
+    R, C = x.shape
+    K = w.shape[1]
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but x has {R} rows")
+    _need(y, x.dtype, x.shape, "y")
+    _need(w, torch.float32, (C, K), "w")
+    _need(state, x.dtype, (P, K - 1, C), "state")
+    if bias is not None:
+        _need(bias, torch.float32, (C,), "bias")
+    _check(lib.lrc_conv_prefill(_ptr(x), _ptr(y), _ptr(state), _ptr(w), _ptr(bias), arr, P, C, K,
+                                _dtype_code(x), _stream(x)))
+
+
+# ------------------------------------------------------------------ K1 scan
+def scan_rows(a, b, h, h0, hS):
+    """a, b, h [B, S, D, N] f32; h0, hS [B, D, N] f32 (may be the same tensor)."""
+    _dev(a, b, h, h0, hS)
+    B, S, D, N = a.shape
+    for t, n in ((b, "b"), (h, "h")):
+        _need(t, torch.float32, a.shape, n)
+    _need(a, torch.float32, a.shape, "a")
+    _need(h0, torch.float32, (B, D, N), "h0")
+    _need(hS, torch.float32, (B, D, N), "hS")
+    _check(lib.lrc_scan_rows(_ptr(a), _ptr(b), _ptr(h), _ptr(h0), _ptr(hS), B, S, D, N, _stream(a)))
+
+
+def scan_prefill(a, b, h, state, lens):
+    """a, b, h [R, D, N] f32 packed rows; state [P, D, N] f32 updated in place."""
+    _dev(a, b, h, state)
+    R, D, N = a.shape
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but a has {R} rows")
+    for t, n in ((a, "a"), (b, "b"), (h, "h")):
+        _need(t, torch.float32, (R, D, N), n)
+    _need(state, torch.float32, (P, D, N), "state")
+    _check(lib.lrc_scan_prefill(_ptr(a), _ptr(b), _ptr(h), _ptr(state), arr, P, D, N, _stream(a)))
+
+
+# ------------------------------------------------------------------ K2 wkv
+def wkv4_rows(k, v, w, u, wkv, num, den, mx):
+    """k, v, wkv [B, S, C] f32; w, u [C]; num, den, mx [B, C] updated in place."""
+    _dev(k, v, w, u, wkv, num, den, mx)
+    B, S, C = k.shape
+    for t, n in ((k, "k"), (v, "v"), (wkv, "wkv")):
+        _need(t, torch.float32, (B, S, C), n)
+    for t, n in ((w, "w"), (u, "u")):
+        _need(t, torch.float32, (C,), n)
+    for t, n in ((num, "num"), (den, "den"), (mx, "max")):
+        _need(t, torch.float32, (B, C), n)
+    _check(lib.lrc_wkv4_rows(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(wkv), _ptr(num), _ptr(den), _ptr(mx),
+                             B, S, C, _stream(k)))
+
+
+def wkv4_prefill(k, v, w, u, wkv, num, den, mx, lens):
+    """k, v, wkv [R, C] packed rows; num, den, mx [P, C] updated in place."""
+    _dev(k, v, w, u, wkv, num, den, mx)
+    R, C = k.shape
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but k has {R} rows")
+    for t, n in ((k, "k"), (v, "v"), (wkv, "wkv")):
+        _need(t, torch.float32, (R, C), n)
+    for t, n in ((w, "w"), (u, "u")):
+        _need(t, torch.float32, (C,), n)
+    for t, n in ((num, "num"), (den, "den"), (mx, "max")):
+        _need(t, torch.float32, (P, C), n)
+    _check(lib.lrc_wkv4_prefill(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(wkv), _ptr(num), _ptr(den), _ptr(mx),
+                                arr, P, C, _stream(k)))
+
+
+# ------------------------------------------------------------------ K3 gdn
+def gdn_chunk(q, k, v, beta, g, o, S_in, S_out):
+    """q, k [B, S, Hk, dk]; v [B, S, Hv, dv] (f32 or bf16); beta, g [B, S, Hv] f32;
+    o [B, S, Hv, dv] f32; S_in, S_out [B, Hv, dk, dv] f32 (may be the same tensor)."""
+    _dev(q, k, v, beta, g, o, S_in, S_out)
+    B, S, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    _need(k, q.dtype, q.shape, "k")
+    _need(v, q.dtype, (B, S, Hv, dv), "v")
+    _need(beta, torch.float32, (B, S, Hv), "beta")
+    _need(g, torch.float32, (B, S, Hv), "g")
+    _need(o, torch.float32, (B, S, Hv, dv), "o")
+    _need(S_in, torch.float32, (B, Hv, dk, dv), "S_in")
+    _need(S_out, torch.float32, (B, Hv, dk, dv), "S_out")
+    _check(lib.lrc_gdn_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o), _ptr(S_in), _ptr(S_out),
+                             B, S, Hk, Hv, dk, dv, _dtype_code(q), _stream(q)))
+
+
+def gdn_prefill(q, k, v, beta, g, o, state, lens):
+    """q, k [R, Hk, dk]; v [R, Hv, dv]; beta, g [R, Hv]; o [R, Hv, dv] packed rows;
+    state [P, Hv, dk, dv] f32 updated in place."""
+    _dev(q, k, v, beta, g, o, state)
+    R, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but q has {R} rows")
+    _need(k, q.dtype, q.shape, "k")
+    _need(v, q.dtype, (R, Hv, dv), "v")
+    _need(beta, torch.float32, (R, Hv), "beta")
+    _need(g, torch.float32, (R, Hv), "g")
+    _need(o, torch.float32, (R, Hv, dv), "o")
+    _need(state, torch.float32, (P, Hv, dk, dv), "state")
+    _check(lib.lrc_gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o), _ptr(state), arr, P,
+                               Hk, Hv, dk, dv, _dtype_code(q), _stream(q)))
+
+
+def unit_lower_inverse(A, T):
+    """A, T [batch, n, n] f32: T = (I + strictly_lower(A))^-1, n <= 64."""
+    _dev(A, T)
+    batch, n, _ = A.shape
+    _need(A, torch.float32, (batch, n, n), "A")
+    _need(T, torch.float32, (batch, n, n), "T")
+    _check(lib.lrc_unit_lower_inverse(_ptr(A), _ptr(T), batch, n, _stream(A)))

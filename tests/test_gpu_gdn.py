@@ -1,0 +1,176 @@
+"""GPU parity of K3 (Gated DeltaNet chunk) and of its triangular inverse
+against the float64 oracle.
+
+Workloads: small (8 heads, dk = dv = 64, 75 rows as 64 + 11) in fp32 (tol
+1e-4) and bf16 (tol 2e-2); the stress case of nearly parallel keys
+(cosine > 0.999) with beta = 0.99, for 16, 32 and 64 such keys; the 9B-like
+shape (32 value heads on 16 key heads, 128 x 128, 2048 rows as 32 x 64 chunks,
+bf16, decays from -1e-3 to -8 per row); ragged batches.  The inverse is
+checked on its own at the precision the chunk uses (FP32), on full 64-row
+matrices of nearly parallel keys, against forward substitution.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import chunks, f64, require_gpu, to_dev
+from helpers import TOL_BF16, TOL_F32, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    require_gpu()
+    from linear_recurrence_chunked_amd import lrc
+
+    return lrc
+
+
+def _run_chunked(L, d, splits):
+    q, k, v, beta, g, S0 = (to_dev(d[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+    R, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    o = torch.empty((R, Hv, dv), device=q.device)
+    st = S0.clone().unsqueeze(0)
+    for r, n in chunks(R, splits):
+        oc = torch.empty((1, n, Hv, dv), device=q.device)
+        L.gdn_chunk(q[r:r + n][None].contiguous(), k[r:r + n][None].contiguous(), v[r:r + n][None].contiguous(),
+                    beta[r:r + n][None].contiguous(), g[r:r + n][None].contiguous(), oc, st, st)
+        o[r:r + n] = oc[0]
+    torch.cuda.synchronize()
+    return o, st[0]
+
+
+def _run_prefill(L, d):
+    q, k, v, beta, g, S0 = (to_dev(d[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+    R = q.shape[0]
+    Hv, dv = v.shape[1], v.shape[2]
+    o = torch.empty((R, Hv, dv), device=q.device)
+    st = S0.clone().unsqueeze(0)
+    L.gdn_prefill(q, k, v, beta, g, o, st, [R])
+    torch.cuda.synchronize()
+    return o, st[0]
+
+
+def _oracle(orc, d):
+    return orc.gdn(*(f64(d[n]) for n in ("q", "k", "v", "beta", "g", "S0")))
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)])
+@pytest.mark.parametrize("splits", [[64, 11], [7, 4, 64], [1] * 11 + [64]])
+def test_gdn_small_chunked(L, orc, dtype, tol, splits):
+    from linear_recurrence_chunked_amd import inputs
+
+    d = inputs.gdn_small(dtype=dtype)
+    ref_o, ref_s = _oracle(orc, d)
+    o, s = _run_chunked(L, d, splits)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    assert rel_err(f64(o), ref_o) < tol
+    assert rel_err(f64(s), ref_s) < tol
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)])
+def test_gdn_small_prefill_and_determinism(L, orc, dtype, tol):
+    from linear_recurrence_chunked_amd import inputs
+
+    d = inputs.gdn_small(dtype=dtype)
+    ref_o, ref_s = _oracle(orc, d)
+    o1, s1 = _run_prefill(L, d)
+    o2, s2 = _run_prefill(L, d)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert rel_err(f64(o1), ref_o) < tol
+    assert rel_err(f64(s1), ref_s) < tol
+
+
+@pytest.mark.parametrize("nkeys", [16, 32, 64])
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)])
+def test_gdn_nearly_parallel_keys_beta_near_one(L, orc, nkeys, dtype, tol):
+    from linear_recurrence_chunked_amd import inputs
+
+    start = 24 if nkeys == 16 else 0
+    d = inputs.gdn_small(dtype=dtype, parallel_keys=nkeys, parallel_start=start, beta_const=0.99)
+    kk = f64(d["k"])[start:start + nkeys, 0]
+    cos = kk @ kk.T
+    assert cos.min() > 0.999
+    ref_o, ref_s = _oracle(orc, d)
+    o, s = _run_prefill(L, d)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    assert rel_err(f64(o), ref_o) < tol
+    assert rel_err(f64(s), ref_s) < tol
+
+
+def test_gdn_9b_shape_full(L, orc):
+    from linear_recurrence_chunked_amd import inputs
+
+    d = inputs.gdn_9b()
+    ref_o, ref_s = _oracle(orc, d)
+    o, s = _run_prefill(L, d)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    assert rel_err(f64(o), ref_o) < TOL_BF16
+    assert rel_err(f64(s), ref_s) < TOL_BF16
+    # the head with g = -8 per row: gamma reaches -512 inside a chunk
+    assert rel_err(f64(o[:, 31]), ref_o[:, 31]) < TOL_BF16
+    assert rel_err(f64(s[31]), ref_s[31]) < TOL_BF16
+
+
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(32, 32, 2, 4), (64, 32, 1, 3), (128, 64, 2, 2), (32, 128, 1, 2)])
+def test_gdn_ragged_batch(L, orc, dk, dv, Hk, Hv):
+    rng = np.random.default_rng(300 + dk + dv + Hv)
+    lens = [1, 64, 0, 65, 130, 7]
+    R, P = sum(lens), len(lens)
+    q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((R, Hv, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((R, Hv))))
+    g = -np.logaddexp(0, rng.standard_normal((R, Hv))) * 0.5
+    S0 = rng.normal(0, 0.1, (P, Hv, dk, dv))
+    t = {n: torch.from_numpy(a).float() for n, a in dict(q=q, k=k, v=v, beta=beta, g=g, S0=S0).items()}
+    dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+    o = torch.full((R, Hv, dv), float("nan"), device="cuda")
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+    torch.cuda.synchronize()
+    r = 0
+    for p, n in enumerate(lens):
+        sl = slice(r, r + n)
+        ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
+                               f64(t["g"][sl]), f64(t["S0"][p]))
+        if n:
+            assert rel_err(f64(o[sl]), ref_o) < TOL_F32
+        assert rel_err(f64(dS[p]), ref_s) < TOL_F32
+        r += n
+
+
+def test_gdn_rejects_65_rows(L):
+    q = torch.randn(1, 65, 1, 32, device="cuda")
+    v = torch.randn(1, 65, 1, 32, device="cuda")
+    b = torch.rand(1, 65, 1, device="cuda")
+    S = torch.zeros(1, 1, 32, 32, device="cuda")
+    with pytest.raises(L.LrcError) as ei:
+        L.gdn_chunk(q, q.clone(), v, b, -b, torch.empty_like(v), S, S)
+    assert ei.value.name == "LRC_ERR_ROWS"
+
+
+def _near_parallel_A(rng, n, nkeys, beta=0.99, dk=64):
+    k = rng.standard_normal((n, dk))
+    k[:nkeys] = rng.standard_normal(dk) + 1e-3 * rng.standard_normal((nkeys, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    g = -np.logaddexp(0.0, rng.standard_normal(n)) * 0.01
+    gam = np.cumsum(g)
+    A = beta * np.exp(np.tril(gam[:, None] - gam[None, :], -1)) * (k @ k.T)
+    return np.tril(A, -1)
+
+
+@pytest.mark.parametrize("n,nkeys", [(64, 64), (64, 32), (64, 16), (37, 37), (8, 8), (1, 1)])
+def test_inverse_full_chunk_production_precision(L, orc, n, nkeys):
+    rng = np.random.default_rng(400 + n + nkeys)
+    A = np.stack([_near_parallel_A(rng, n, nkeys) for _ in range(8)]).astype(np.float32)
+    tA = to_dev(torch.from_numpy(A))
+    T = torch.empty_like(tA)
+    L.unit_lower_inverse(tA, T)
+    torch.cuda.synchronize()
+    ref = orc.unit_lower_inverse(A.astype(np.float64))
+    got = f64(T)
+    for b in range(8):
+        assert rel_err(got[b], ref[b]) < TOL_F32
+    assert np.all(np.triu(got, 1) == 0) and np.all(np.diagonal(got, axis1=1, axis2=2) == 1)

@@ -1,0 +1,119 @@
+"""GPU parity of K2 (RWKV-4 WKV rows) against the float64 oracle.
+
+Workload: 169M-like, 768 x 12 independent channels, 128 rows as 2 x 64, fp32,
+decays w = -exp(U(-6, 2)), bonuses U(-2, 2), keys N(0, 3) with 1% set to
++-30, incoming (num, den, max) from 32 warm-up steps run by the oracle.
+
+The state triple is defined only up to a common scale ("the same A and B at
+another scale"), so it is compared scale-free: num / den, and num, den
+rescaled to the oracle's max, e^{max - max_oracle}.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import chunks, f64, require_gpu, to_dev
+from helpers import TOL_F32, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    require_gpu()
+    from linear_recurrence_chunked_amd import lrc
+
+    return lrc
+
+
+@pytest.fixture(scope="module")
+def cfg(orc):
+    from linear_recurrence_chunked_amd import inputs
+
+    d = inputs.rwkv_169m()
+    C = d["k"].shape[1]
+    _, n, de, m = orc.wkv4(f64(d["warm_k"]), f64(d["warm_v"]), f64(d["w"]), f64(d["u"]), *orc.empty_wkv_state(C))
+    # both sides start from the fp32 triple
+    d["num0"] = torch.from_numpy(n).float()
+    d["den0"] = torch.from_numpy(de).float()
+    d["max0"] = torch.from_numpy(m).float()
+    return d
+
+
+def _check_state(num, den, mx, rn, rd, rm):
+    num, den, mx = f64(num), f64(den), f64(mx)
+    assert np.all(np.isfinite(num)) and np.all(np.isfinite(den)) and np.all(np.isfinite(mx))
+    assert rel_err(num / den, rn / rd) < TOL_F32
+    f = np.exp(mx - rm)
+    assert rel_err(num * f, rn) < TOL_F32
+    assert rel_err(den * f, rd) < TOL_F32
+
+
+@pytest.mark.parametrize("splits", [[64, 64], [128], [1] * 128, [11, 64, 53]])
+def test_wkv_169m_chunked(L, orc, cfg, splits):
+    d = cfg
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    R, C = k.shape
+    num, den, mx = (to_dev(d[n]).unsqueeze(0).clone() for n in ("num0", "den0", "max0"))
+    out = torch.empty_like(k)
+    for r, n in chunks(R, splits):
+        o = torch.empty((1, n, C), device=k.device)
+        L.wkv4_rows(k[r:r + n].unsqueeze(0).contiguous(), v[r:r + n].unsqueeze(0).contiguous(), w, u, o,
+                    num, den, mx)
+        out[r:r + n] = o[0]
+    torch.cuda.synchronize()
+    ref, rn, rd, rm = orc.wkv4(f64(d["k"]), f64(d["v"]), f64(d["w"]), f64(d["u"]),
+                               f64(d["num0"]), f64(d["den0"]), f64(d["max0"]))
+    assert rel_err(f64(out), ref) < TOL_F32
+    assert torch.isfinite(out).all()
+    _check_state(num[0], den[0], mx[0], rn, rd, rm)
+
+
+def test_wkv_prefill_ragged_fresh_state_and_determinism(L, orc):
+    from linear_recurrence_chunked_amd import inputs
+
+    lens = [128, 1, 0, 75, 64, 200]
+    d = inputs.rwkv_169m(rows=sum(lens), channels=300, seed=7)
+    k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+    P, C = len(lens), k.shape[1]
+    results = []
+    for _ in range(2):
+        num = torch.zeros((P, C), device=k.device)
+        den = torch.zeros((P, C), device=k.device)
+        mx = torch.full((P, C), -1e38, device=k.device)
+        out = torch.empty_like(k)
+        L.wkv4_prefill(k, v, w, u, out, num, den, mx, lens)
+        torch.cuda.synchronize()
+        results.append((out.clone(), num.clone(), den.clone(), mx.clone()))
+    for a, b in zip(results[0], results[1]):
+        assert torch.equal(a, b)
+    out, num, den, mx = results[0]
+    r = 0
+    for p, n in enumerate(lens):
+        ref, rn, rd, rm = orc.wkv4(f64(d["k"][r:r + n]), f64(d["v"][r:r + n]), f64(d["w"]), f64(d["u"]),
+                                   *orc.empty_wkv_state(C))
+        if n:
+            assert rel_err(f64(out[r:r + n]), ref) < TOL_F32
+            assert torch.equal(out[r], v[r])  # a fresh state outputs v_0 exactly
+            _check_state(num[p], den[p], mx[p], rn, rd, rm)
+        else:
+            assert torch.all(mx[p] == -1e38) and torch.all(num[p] == 0)
+        r += n
+
+
+def test_wkv_extreme_keys_and_decays_stay_finite(L, orc):
+    C, S = 64, 64
+    w = -torch.exp(torch.linspace(-6.0, 2.0, C))
+    u = torch.linspace(-2.0, 2.0, C)
+    k = torch.where((torch.arange(S)[:, None] + torch.arange(C)[None]) % 3 == 0, 30.0, -30.0).float()
+    v = torch.cos(torch.arange(S * C, dtype=torch.float32)).view(S, C)
+    tk, tv, tw, tu = (to_dev(t) for t in (k, v, w, u))
+    num, den = torch.zeros((1, C), device="cuda"), torch.zeros((1, C), device="cuda")
+    mx = torch.full((1, C), -1e38, device="cuda")
+    out = torch.empty((1, S, C), device="cuda")
+    L.wkv4_rows(tk[None], tv[None], tw, tu, out, num, den, mx)
+    torch.cuda.synchronize()
+    ref, rn, rd, rm = orc.wkv4(f64(k), f64(v), f64(w), f64(u), *orc.empty_wkv_state(C))
+    assert torch.isfinite(out).all()
+    assert rel_err(f64(out[0]), ref) < TOL_F32
+    _check_state(num[0], den[0], mx[0], rn, rd, rm)
