@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark: chunked prefill of recurrent mixers on one MI355X.
+
+One step = one pass of the whole hot path over the batched mixed workload:
+16 prompts of U{1..4096} rows (seeded), each prefilled in 64-row chunks with
+its state carried between chunks, through
+  1. the Mamba short conv   (K=4, 5120 fp32 channels)
+  2. the Mamba selective scan (d_inner 5120 x d_state 16, fp32)
+  3. RWKV-4 WKV             (hidden 2560, fp32)
+  4. the DeltaNet short conv (K=4, 2*16*128 + 32*128 = 8192 bf16 channels)
+  5. the Gated DeltaNet chunk (32 value heads on 16 key heads, 128 x 128, bf16 in, fp32 state)
+Inputs are synthetic and already resident in HBM when timing starts.
+
+Prints ONE JSON line.  `value` is prompt rows per second through the whole
+step.  Per-kernel times come from HIP events on the stream the kernels run
+on; `roofline` covers the kernel with the largest share of the step.
+`cpu_baseline` times the float64 oracle (test infrastructure) on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VEC_PEAK_TFS = 157.3    # MI355X fp32 vector, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle work")
+    ap.add_argument("--only", default="", help="comma list of kernels to run (profiling aid)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 4 GiB device copy (for scaling HBM counters) and exit")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- workload
+def make_workload(dev):
+    import torch
+
+    from linear_recurrence_chunked_amd import inputs
+
+    lens = inputs.mixed_lengths()
+    sh = inputs.MIXED_SHAPES
+    m = inputs.mixed_mamba(lens, dev)
+    r = inputs.mixed_rwkv(lens, dev)
+    g = inputs.mixed_gdn(lens, dev)
+    R = sum(lens)
+    D, N = sh["mamba_d_inner"], sh["mamba_d_state"]
+    W = {
+        "lens": lens, "R": R,
+        # Mamba conv + scan
+        "xm": m["conv_x"], "ym": torch.empty_like(m["conv_x"]), "sm": m["conv_state"], "wm": m["conv_w"],
+        "a": m["a"].view(R, D, N), "b": m["b"].view(R, D, N), "h": torch.empty((R, D, N), device=dev),
+        "hs": m["h0"].view(len(lens), D, N),
+        # RWKV-4
+        "k": r["k"], "v": r["v"], "w": r["w"], "u": r["u"], "wkv": torch.empty_like(r["k"]),
+        "num": r["num"], "den": r["den"], "max": r["max"],
+        # DeltaNet conv + chunk
+        "xg": g["conv_x"], "yg": torch.empty_like(g["conv_x"]), "sg": g["conv_state"], "wg": g["conv_w"],
+        "q": g["q"], "gk": g["k"], "gv": g["v"], "beta": g["beta"], "g": g["g"],
+        "o": torch.empty((R, sh["gdn_hv"], sh["gdn_dv"]), device=dev), "S": g["S0"],
+    }
+    return W
+
+
+KERNELS = ["conv_mamba", "scan", "wkv4", "conv_gdn", "gdn"]
+
+
+def run_kernel(lrc, W, name):
+    lens = W["lens"]
+    if name == "conv_mamba":
+        lrc.conv_prefill(W["xm"], W["ym"], W["sm"], W["wm"], lens)
+    elif name == "scan":
+        lrc.scan_prefill(W["a"], W["b"], W["h"], W["hs"], lens)
+    elif name == "wkv4":
+        lrc.wkv4_prefill(W["k"], W["v"], W["w"], W["u"], W["wkv"], W["num"], W["den"], W["max"], lens)
+    elif name == "conv_gdn":
+        lrc.conv_prefill(W["xg"], W["yg"], W["sg"], W["wg"], lens)
+    elif name == "gdn":
+        lrc.gdn_prefill(W["q"], W["gk"], W["gv"], W["beta"], W["g"], W["o"], W["S"], lens)
+    else:
+        raise KeyError(name)
+
+
+def algorithmic_work(W):
+    """Bytes (and flops for the DeltaNet chunk) one launch of each kernel must move/do."""
+    from linear_recurrence_chunked_amd import inputs
+
+    sh = inputs.MIXED_SHAPES
+    lens, R, P = W["lens"], W["R"], len(W["lens"])
+    K = sh["conv_k"]
+    Cm, Cg, Cr = sh["mamba_conv_c"], sh["gdn_conv_c"], sh["rwkv_c"]
+    E = sh["mamba_d_inner"] * sh["mamba_d_state"]
+    Hk, Hv, dk, dv = sh["gdn_hk"], sh["gdn_hv"], sh["gdn_dk"], sh["gdn_dv"]
+    grp = Hv // Hk
+    work = {
+        # rows in + rows out, state rows read + written, taps once
+        "conv_mamba": {"bytes": R * Cm * 8 + P * 2 * (K - 1) * Cm * 4 + Cm * K * 4},
+        "scan": {"bytes": R * E * 12 + P * E * 8},
+        "wkv4": {"bytes": R * Cr * 12 + P * Cr * 24 + Cr * 8},
+        "conv_gdn": {"bytes": R * Cg * 4 + P * 2 * (K - 1) * Cg * 2 + Cg * K * 4},
+        "gdn": {"bytes": R * (2 * Hk * dk * 2 + Hv * dv * 2 + Hv * 8 + Hv * dv * 4) + P * Hv * dk * dv * 8},
+    }
+    # Dense-contraction flops the chunk form prescribes, per value head and
+    # chunk of r rows: K K^T and Q K^T (shared by the value heads of a key
+    # head), K S0, Q S0, the state update, T (I+A)^-1 applied to the right-
+    # hand side, P U, plus the 64-row block inverse.
+    inv = 8 * 4 * 2 * 8 ** 3 + sum((64 // (2 * s)) * 2 * 2 * s ** 3 for s in (8, 16, 32))
+    fl = 0
+    for L in lens:
+        for c0 in range(0, L, 64):
+            r = min(64, L - c0)
+            per_head = (2 * 2 * r * r * dk) / grp + 3 * 2 * r * dk * dv + 2 * 2 * r * r * dv + inv
+            fl += per_head * Hv
+    work["gdn"]["flops"] = fl
+    return work
+
+
+# ----------------------------------------------------------------------------- oracle sample
+def cpu_baseline(W, lrc_outputs_fresh, budget_s):
+    """Time the float64 oracle on a bounded sample of the workload (every prompt,
+    a strided subset of channels / state elements / heads of each kernel), scale
+    each kernel's time by its sampled fraction, and report rows/s for the whole
+    step.  Also returns the GPU's max rel err on the same sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    from linear_recurrence_chunked_amd import inputs
+
+    oracle.build(force=False)
+    sh = inputs.MIXED_SHAPES
+    lens, R = W["lens"], W["R"]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    fresh = lrc_outputs_fresh
+    # sample fractions (fraction of the kernel's independent units)
+    Cm, Cg, Cr = sh["mamba_conv_c"], sh["gdn_conv_c"], sh["rwkv_c"]
+    E = sh["mamba_d_inner"] * sh["mamba_d_state"]
+    Hk, Hv = sh["gdn_hk"], sh["gdn_hv"]
+    sel = {
+        "conv_mamba": np.arange(0, Cm, 16),
+        "scan": np.arange(0, E, 64),
+        "wkv4": np.arange(0, Cr, 8),
+        "conv_gdn": np.arange(0, Cg, 32),
+        "gdn_keyheads": np.array([0, Hk - 1]),  # key heads 0 and 15 -> value heads 0, 1, 30, 31
+    }
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    t_kernel, err = {}, {}
+
+    def rel(got, ref):
+        s = np.max(np.abs(ref)) if ref.size else 0.0
+        return float(np.max(np.abs(got - ref)) / (s if s else 1.0)) if ref.size else 0.0
+
+    # conv (Mamba, fp32) -- fresh state is zero
+    c = torch.as_tensor(sel["conv_mamba"], device=W["xm"].device)
+    x = f64(W["xm"][:, c]); wt = f64(W["wm"][c]); y = fresh["ym"]
+    t0 = time.perf_counter(); e = 0.0
+    for p in range(len(lens)):
+        ry, _ = oracle.conv_rows(x[offs[p]:offs[p + 1]], np.zeros((3, len(c))), wt)
+        e = max(e, rel(y[offs[p]:offs[p + 1]], ry) if lens[p] else 0.0)
+    t_kernel["conv_mamba"] = (time.perf_counter() - t0) * Cm / len(c); err["conv_mamba"] = e
+    # scan
+    ci = torch.as_tensor(sel["scan"], device=W["a"].device)
+    a = f64(W["a"].view(R, -1)[:, ci]); b = f64(W["b"].view(R, -1)[:, ci]); h = fresh["h"]
+    t0 = time.perf_counter(); e = 0.0
+    for p in range(len(lens)):
+        rh, _ = oracle.scan(a[offs[p]:offs[p + 1]], b[offs[p]:offs[p + 1]], np.zeros(len(ci)))
+        e = max(e, rel(h[offs[p]:offs[p + 1]], rh) if lens[p] else 0.0)
+    t_kernel["scan"] = (time.perf_counter() - t0) * E / len(ci); err["scan"] = e
+    del a, b
+    # wkv
+    ci = torch.as_tensor(sel["wkv4"], device=W["k"].device)
+    k = f64(W["k"][:, ci]); v = f64(W["v"][:, ci]); w = f64(W["w"][ci]); u = f64(W["u"][ci]); o = fresh["wkv"]
+    t0 = time.perf_counter(); e = 0.0
+    for p in range(len(lens)):
+        ro, *_ = oracle.wkv4(k[offs[p]:offs[p + 1]], v[offs[p]:offs[p + 1]], w, u, *oracle.empty_wkv_state(len(ci)))
+        e = max(e, rel(o[offs[p]:offs[p + 1]], ro) if lens[p] else 0.0)
+    t_kernel["wkv4"] = (time.perf_counter() - t0) * Cr / len(ci); err["wkv4"] = e
+    # conv (DeltaNet, bf16)
+    c = torch.as_tensor(sel["conv_gdn"], device=W["xg"].device)
+    x = f64(W["xg"][:, c]); wt = f64(W["wg"][c]); y = fresh["yg"]
+    t0 = time.perf_counter(); e = 0.0
+    for p in range(len(lens)):
+        ry, _ = oracle.conv_rows(x[offs[p]:offs[p + 1]], np.zeros((3, len(c))), wt)
+        e = max(e, rel(y[offs[p]:offs[p + 1]], ry) if lens[p] else 0.0)
+    t_kernel["conv_gdn"] = (time.perf_counter() - t0) * Cg / len(c); err["conv_gdn"] = e
+    # gated deltanet: two key heads and their value heads
+    kh = torch.as_tensor(sel["gdn_keyheads"], device=W["q"].device)
+    vh = torch.as_tensor(np.concatenate([[2 * i, 2 * i + 1] for i in sel["gdn_keyheads"]]), device=W["q"].device)
+    q = f64(W["q"][:, kh]); kk = f64(W["gk"][:, kh]); vv = f64(W["gv"][:, vh])
+    be = f64(W["beta"][:, vh]); gg = f64(W["g"][:, vh]); o = fresh["o"]
+    dk, dv = q.shape[2], vv.shape[2]
+    t0 = time.perf_counter(); eo = 0.0
+    for p in range(len(lens)):
+        sl = slice(offs[p], offs[p + 1])
+        ro, _ = oracle.gdn(q[sl], kk[sl], vv[sl], be[sl], gg[sl], np.zeros((len(vh), dk, dv)))
+        eo = max(eo, rel(o[sl], ro) if lens[p] else 0.0)
+    t_kernel["gdn"] = (time.perf_counter() - t0) * Hv / len(vh); err["gdn"] = eo
+    total = sum(t_kernel.values())
+    sample_s = sum(t_kernel[n] * frac for n, frac in [
+        ("conv_mamba", len(sel["conv_mamba"]) / Cm), ("scan", len(sel["scan"]) / E),
+        ("wkv4", len(sel["wkv4"]) / Cr), ("conv_gdn", len(sel["conv_gdn"]) / Cg), ("gdn", len(vh) / Hv)])
+    return {
+        "value": R / total, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+        "sample": (f"all {len(lens)} prompts ({R} rows); every 16th Mamba conv channel, every 64th scan state "
+                   f"element, every 8th RWKV channel, every 32nd DeltaNet conv channel, value heads 0,1,30,31 "
+                   f"of the DeltaNet chunk; {sample_s:.1f} s of oracle time scaled by the sampled fraction "
+                   f"of each kernel"),
+        "seconds_per_step_estimated": total,
+        "per_kernel_s": {n: round(t, 3) for n, t in t_kernel.items()},
+    }, err
+
+
+def fresh_outputs_sample(lrc, W):
+    """Run one step from fresh states and keep host copies of the sampled outputs."""
+    import numpy as np
+    import torch
+
+    from linear_recurrence_chunked_amd import inputs
+
+    sh = inputs.MIXED_SHAPES
+    E = sh["mamba_d_inner"] * sh["mamba_d_state"]
+    for k in KERNELS:
+        run_kernel(lrc, W, k)
+    torch.cuda.synchronize()
+    Hk = sh["gdn_hk"]
+    vh = np.concatenate([[2 * i, 2 * i + 1] for i in (0, Hk - 1)])
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    return {
+        "ym": f64(W["ym"][:, ::16]),
+        "h": f64(W["h"].view(W["R"], E)[:, ::64]),
+        "wkv": f64(W["wkv"][:, ::8]),
+        "yg": f64(W["yg"][:, ::32]),
+        "o": f64(W["o"][:, torch.as_tensor(vh, device=W["o"].device)]),
+    }
+
+
+def reset_states(W):
+    W["sm"].zero_(); W["hs"].zero_(); W["num"].zero_(); W["den"].zero_(); W["max"].fill_(-1e38)
+    W["sg"].zero_(); W["S"].zero_()
+
+
+def calibrate_copy():
+    import torch
+
+    n = 1 << 30  # 4 GiB of fp32
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels shard over prompts/channels/heads with no communication; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    from linear_recurrence_chunked_amd import lrc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = make_workload(dev)
+    torch.cuda.synchronize()
+    kernels = [k for k in KERNELS if not args.only or k in args.only.split(",")]
+
+    fresh = None if args.no_cpu_baseline else fresh_outputs_sample(lrc, W)
+    reset_states(W)
+    for _ in range(args.warmup):
+        for k in kernels:
+            run_kernel(lrc, W, k)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, k in enumerate(kernels):
+            run_kernel(lrc, W, k)
+            ev[s][i + 1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_k = {k: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+             for i, k in enumerate(kernels)}
+    ms_per_step = total_ms / args.steps
+    R = W["R"]
+    work = algorithmic_work(W)
+
+    kern = {}
+    for k in kernels:
+        ms = per_k[k]
+        d = {"ms": round(ms, 4), "rows_per_s": R / (ms * 1e-3), "GBps": work[k]["bytes"] / (ms * 1e-3) / 1e9}
+        d["hbm_frac"] = d["GBps"] / HBM_PEAK_GBS
+        if "flops" in work[k]:
+            d["TFLOPs"] = work[k]["flops"] / (ms * 1e-3) / 1e12
+            d["mfma_bf16_frac"] = d["TFLOPs"] / MFMA_BF16_PEAK_TFS
+        kern[k] = d
+    dom = max(kernels, key=lambda k: per_k[k])
+    if dom == "gdn":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": kern[dom]["mfma_bf16_frac"], "traffic": None,
+                "algorithmic_per_launch": work[dom]["flops"]}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern[dom]["hbm_frac"], "traffic": None, "algorithmic_per_launch": work[dom]["bytes"]}
+    roof["avg_launch_ms"] = per_k[dom]
+
+    out = {
+        "metric": "prefill rows/s per kernel at 1 GPU; % HBM or MFMA peak; max rel err vs oracle",
+        "value": R / (ms_per_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "batched mixed prefill: 16 prompts of U{1..4096} rows, 64-row chunks, through "
+                               "Mamba conv (5120 fp32) + scan (5120x16 fp32), RWKV-4 WKV (2560 fp32), "
+                               "DeltaNet conv (8192 bf16) + Gated DeltaNet (32x128x128, bf16 in, fp32 state)",
+                   "prompts": len(W["lens"]), "rows": R, "lens": W["lens"], "kernels": kernels},
+        "roofline": roof,
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline and set(kernels) == set(KERNELS):
+        cb, err = cpu_baseline(W, fresh, args.cpu_budget)
+        out["cpu_baseline"] = cb
+        out["max_rel_err_sample"] = err
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

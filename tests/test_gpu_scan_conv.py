@@ -126,7 +126,7 @@ def _conv_chunked(L, x, st0, w, splits, bias=None):
 
 
 @pytest.mark.parametrize("zero_state", [False, True])
-@pytest.mark.parametrize("splits", [[64, 11], [1] * 75, [2, 1, 72], [75]])
+@pytest.mark.parametrize("splits", [[64, 11], [1] * 75, [2, 1, 64, 8], [11, 64]])
 def test_conv_mamba_tiny(L, orc, splits, zero_state):
     from linear_recurrence_chunked_amd import inputs
 
@@ -136,6 +136,11 @@ def test_conv_mamba_tiny(L, orc, splits, zero_state):
     y, s = _conv_chunked(L, x, st, w, splits)
     assert rel_err(f64(y), ref_y) < TOL_F32
     assert np.array_equal(f64(s), ref_s)  # the state is a copy of input rows
+    yp = torch.empty_like(x)
+    sp = st.clone()[None]
+    L.conv_prefill(x, yp, sp, w, [x.shape[0]])
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y) and torch.equal(sp[0], s)  # chunking changes no bit
 
 
 def test_conv_bf16_deltanet_width(L, orc):

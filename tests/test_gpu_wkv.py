@@ -49,7 +49,7 @@ def _check_state(num, den, mx, rn, rd, rm):
     assert rel_err(den * f, rd) < TOL_F32
 
 
-@pytest.mark.parametrize("splits", [[64, 64], [128], [1] * 128, [11, 64, 53]])
+@pytest.mark.parametrize("splits", [[64, 64], [64, 1, 63], [1] * 128, [11, 64, 53]])
 def test_wkv_169m_chunked(L, orc, cfg, splits):
     d = cfg
     k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
