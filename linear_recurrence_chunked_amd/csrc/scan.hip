@@ -7,111 +7,173 @@
 // followed by h_t = a_t h_0 + b_t for the incoming state.  Every factor is a
 // decay in (0, 1], so the products stay finite.
 //
-// Mapping on CDNA4: one wave64 owns 16 consecutive state elements of one
-// prompt and walks that prompt's 64-row chunks; lane t holds row t of the
-// chunk, so the whole chunk is one wave-wide scan.  Each lane reads and
-// writes its row's 16 elements as four 16-byte vectors (a 64-byte run per
-// row; the four waves of a block cover 256 contiguous bytes of every row).
-// The six doubling rounds run on DPP: rounds k = 1, 2, 4, 8 shift within each
-// 16-lane row (row_shr), then two row-broadcast rounds carry each row's
-// running pair into the rows after it (row_bcast:15, row_bcast:31), which is
-// the wave64 form of the k = 16, 32 rounds.  Lanes past the chunk's last row
-// and lanes without a source take the identity pair (1, 0).  The carried
-// state of each element stays in registers from chunk to chunk and is read
-// back from lane S-1 of the chunk.
+// Mapping on CDNA4.  A workgroup (4 waves) owns 64 consecutive state
+// elements of one prompt and walks that prompt's 64-row chunks, keeping the
+// carried state of its elements in registers:
+//  1. The chunk's a and b tiles [64 rows x 64 elements] are read with
+//     row-contiguous 16-byte loads (256 bytes per row, 2 full cache lines)
+//     and written to LDS; the next chunk's loads are issued before this
+//     chunk is scanned, so their latency hides behind the arithmetic.
+//  2. Each wave reads 16 element columns out of LDS with lane t = row t and
+//     scans each column across the wave in six rounds.  Rounds k = 1, 2, 4, 8
+//     shift within each 16-lane row of the wave (DPP row_shr); the last two
+//     rounds carry each 16-lane row's running pair into the rows after it
+//     (DPP row_bcast:15, row_bcast:31), the wave64 form of rounds k = 16, 32.
+//     The DPP reads are folded into the arithmetic (v_fmac_f32_dpp,
+//     v_mul_f32_dpp); a lane whose source is out of range keeps its pair,
+//     which is the identity (1, 0) step.  Lanes past the chunk's last row
+//     hold the identity pair.  Four columns are interleaved so that no DPP
+//     read follows the write of its source too closely.
+//  3. h_t = A_t h0 + B_t; the new carried state is read from lane S-1; the
+//     h column goes back to LDS and leaves as row-contiguous 16-byte stores.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
 namespace lrc {
 namespace {
 
-constexpr int kCols = 16;
-constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = 256;
+constexpr int kTileCols = 64;        // state elements per workgroup
+constexpr int kColsPerWave = 16;
+constexpr int kLd = kTileCols + 1;   // LDS row stride (floats): column reads hit distinct banks
 
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void scan_round(float& a, float& b) {
-    const float ap = dpp_move<CTRL, ROW_MASK>(1.0f, a);
-    const float bp = dpp_move<CTRL, ROW_MASK>(0.0f, b);
-    b = fmaf(a, bp, b);
-    a = a * ap;
-}
+#define LRC_SCAN_ROUND(CTRL)                                   \
+    "v_fmac_f32_dpp %0, %0, %4 " CTRL "\n"                    \
+    "v_fmac_f32_dpp %1, %1, %5 " CTRL "\n"                    \
+    "v_fmac_f32_dpp %2, %2, %6 " CTRL "\n"                    \
+    "v_fmac_f32_dpp %3, %3, %7 " CTRL "\n"                    \
+    "v_mul_f32_dpp %4, %4, %4 " CTRL "\n"                     \
+    "v_mul_f32_dpp %5, %5, %5 " CTRL "\n"                     \
+    "v_mul_f32_dpp %6, %6, %6 " CTRL "\n"                     \
+    "v_mul_f32_dpp %7, %7, %7 " CTRL "\n"
 
-// Inclusive scan of the pairs held by the 64 lanes (lane = row).
-__device__ __forceinline__ void wave_scan(float& a, float& b) {
-    scan_round<kRowShr1, 0xf>(a, b);
-    scan_round<kRowShr2, 0xf>(a, b);
-    scan_round<kRowShr4, 0xf>(a, b);
-    scan_round<kRowShr8, 0xf>(a, b);
-    scan_round<kRowBcast15, 0xa>(a, b);
-    scan_round<kRowBcast31, 0xc>(a, b);
+// Inclusive wave scan of four independent columns of (a, b) pairs (lane = row).
+// Each round computes b <- b + a * b_src and then a <- a * a_src, where
+// (a_src, b_src) is the pair the DPP pattern routes to the lane.
+__device__ __forceinline__ void wave_scan4(float (&a)[4], float (&b)[4]) {
+    asm volatile(
+        "s_nop 1\n"
+        LRC_SCAN_ROUND("row_shr:1 row_mask:0xf bank_mask:0xf")
+        LRC_SCAN_ROUND("row_shr:2 row_mask:0xf bank_mask:0xf")
+        LRC_SCAN_ROUND("row_shr:4 row_mask:0xf bank_mask:0xf")
+        LRC_SCAN_ROUND("row_shr:8 row_mask:0xf bank_mask:0xf")
+        LRC_SCAN_ROUND("row_bcast:15 row_mask:0xa bank_mask:0xf")
+        LRC_SCAN_ROUND("row_bcast:31 row_mask:0xc bank_mask:0xf")
+        : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
 }
+#undef LRC_SCAN_ROUND
 
 template <bool VEC4>
-__global__ __launch_bounds__(256) void scan_rows_kernel(const float* __restrict__ a, const float* __restrict__ b,
-                                                        float* __restrict__ h, const float* h0, float* hS, Batch bt,
-                                                        long E) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const long col0 = ((long)blockIdx.x * kWavesPerBlock + wave) * kCols;
-    if (col0 >= E) return;
-    const int ncol = (int)min((long)kCols, E - col0);
+__global__ __launch_bounds__(kThreads) void scan_rows_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                            float* __restrict__ h, const float* h0, float* hS,
+                                                            Batch bt, long E) {
+    __shared__ float As[kWave * kLd];
+    __shared__ float Bs[kWave * kLd];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const long tile0 = (long)blockIdx.x * kTileCols;
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
 
-    float carry[kCols];
-    const float* h0p = h0 + (long)p * E + col0;
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) carry[j] = j < ncol ? h0p[j] : 0.0f;
+    // Load-phase mapping: thread -> (row lr + 16 r, 4 columns at lc).
+    const int lr = tid >> 4;
+    const int lc = (tid & 15) * 4;
+    const bool lcol_ok = tile0 + lc < E;
 
-    float A[kCols], B[kCols];
+    // Column-phase mapping: this wave's 16 columns start at cw.
+    const int cw = wave * kColsPerWave;
+    float carry[kColsPerWave];
+#pragma unroll
+    for (int j = 0; j < kColsPerWave; ++j) {
+        const long col = tile0 + cw + j;
+        carry[j] = col < E ? h0[(long)p * E + col] : 0.f;
+    }
+
+    float ra[4][4], rb[4][4];  // [row group][column] of the chunk in flight
+    auto issue_loads = [&](int c0) {
+        const int S = min(kWave, L - c0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = lr + 16 * r;
+            const long off = (row0 + c0 + row) * E + tile0 + lc;
+            if (VEC4) {
+                float4 va = make_float4(1.f, 1.f, 1.f, 1.f), vb = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (row < S && lcol_ok) {
+                    va = *reinterpret_cast<const float4*>(a + off);
+                    vb = *reinterpret_cast<const float4*>(b + off);
+                }
+                ra[r][0] = va.x; ra[r][1] = va.y; ra[r][2] = va.z; ra[r][3] = va.w;
+                rb[r][0] = vb.x; rb[r][1] = vb.y; rb[r][2] = vb.z; rb[r][3] = vb.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = row < S && tile0 + lc + i < E;
+                    ra[r][i] = ok ? a[off + i] : 1.f;
+                    rb[r][i] = ok ? b[off + i] : 0.f;
+                }
+            }
+        }
+    };
+
+    if (L > 0) issue_loads(0);
     for (int c0 = 0; c0 < L; c0 += kWave) {
         const int S = min(kWave, L - c0);
-        const bool valid = lane < S;
-        const long base = (row0 + c0 + lane) * E + col0;
-        if (VEC4) {
+        __syncthreads();  // the previous chunk's h rows have left LDS
 #pragma unroll
-            for (int q = 0; q < kCols / 4; ++q) {
-                float4 va = make_float4(1.f, 1.f, 1.f, 1.f), vb = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (valid && 4 * q < ncol) {
-                    va = *reinterpret_cast<const float4*>(a + base + 4 * q);
-                    vb = *reinterpret_cast<const float4*>(b + base + 4 * q);
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                As[(lr + 16 * r) * kLd + lc + i] = ra[r][i];
+                Bs[(lr + 16 * r) * kLd + lc + i] = rb[r][i];
+            }
+        if (c0 + kWave < L) issue_loads(c0 + kWave);
+        __syncthreads();
+
+        // Column phase: lane = row.
+#pragma unroll
+        for (int g = 0; g < kColsPerWave; g += 4) {
+            float A[4], B[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                A[i] = As[lane * kLd + cw + g + i];
+                B[i] = Bs[lane * kLd + cw + g + i];
+            }
+            wave_scan4(A, B);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float hv = fmaf(A[i], carry[g + i], B[i]);
+                carry[g + i] = readlane_f(hv, S - 1);
+                As[lane * kLd + cw + g + i] = hv;
+            }
+        }
+        __syncthreads();
+
+        // Row phase: h rows leave as 16-byte stores.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = lr + 16 * r;
+            if (row < S) {
+                const long off = (row0 + c0 + row) * E + tile0 + lc;
+                const float* src = &As[row * kLd + lc];
+                if (VEC4) {
+                    if (lcol_ok) *reinterpret_cast<float4*>(h + off) = make_float4(src[0], src[1], src[2], src[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (tile0 + lc + i < E) h[off + i] = src[i];
                 }
-                A[4 * q] = va.x; A[4 * q + 1] = va.y; A[4 * q + 2] = va.z; A[4 * q + 3] = va.w;
-                B[4 * q] = vb.x; B[4 * q + 1] = vb.y; B[4 * q + 2] = vb.z; B[4 * q + 3] = vb.w;
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kCols; ++j) {
-                const bool ok = valid && j < ncol;
-                A[j] = ok ? a[base + j] : 1.0f;
-                B[j] = ok ? b[base + j] : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kCols; ++j) {
-            wave_scan(A[j], B[j]);
-            const float hv = fmaf(A[j], carry[j], B[j]);
-            carry[j] = readlane_f(hv, S - 1);
-            A[j] = hv;
-        }
-        if (VEC4) {
-#pragma unroll
-            for (int q = 0; q < kCols / 4; ++q)
-                if (valid && 4 * q < ncol)
-                    *reinterpret_cast<float4*>(h + base + 4 * q) =
-                        make_float4(A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kCols; ++j)
-                if (valid && j < ncol) h[base + j] = A[j];
         }
     }
     if (lane == 0) {
-        float* hSp = hS + (long)p * E + col0;
 #pragma unroll
-        for (int j = 0; j < kCols; ++j)
-            if (j < ncol) hSp[j] = carry[j];
+        for (int j = 0; j < kColsPerWave; ++j) {
+            const long col = tile0 + cw + j;
+            if (col < E) hS[(long)p * E + col] = carry[j];
+        }
     }
 }
 
@@ -119,13 +181,11 @@ __global__ __launch_bounds__(256) void scan_rows_kernel(const float* __restrict_
 
 hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt, long E,
                        hipStream_t st) {
-    const long per_block = (long)kCols * kWavesPerBlock;
-    const dim3 grid((unsigned)((E + per_block - 1) / per_block), (unsigned)bt.P);
-    const bool vec4 = (E % 4) == 0;
-    if (vec4)
-        hipLaunchKernelGGL(scan_rows_kernel<true>, grid, dim3(256), 0, st, a, b, h, h0, hS, bt, E);
+    const dim3 grid((unsigned)((E + kTileCols - 1) / kTileCols), (unsigned)bt.P);
+    if (E % 4 == 0)
+        hipLaunchKernelGGL(scan_rows_kernel<true>, grid, dim3(kThreads), 0, st, a, b, h, h0, hS, bt, E);
     else
-        hipLaunchKernelGGL(scan_rows_kernel<false>, grid, dim3(256), 0, st, a, b, h, h0, hS, bt, E);
+        hipLaunchKernelGGL(scan_rows_kernel<false>, grid, dim3(kThreads), 0, st, a, b, h, h0, hS, bt, E);
     return hipGetLastError();
 }
 
