@@ -12,8 +12,9 @@
 // formed element by element from differences of gamma (never as ratios of
 // Gamma, which under- and overflow at large decays).
 //
-// This file holds the FP32 path: every contraction is an FP32 FMA loop over
-// tiles staged in LDS.  A workgroup owns one value head and a DVT-wide slice
+// This file holds the FP32-input path (bf16 inputs run on the matrix cores,
+// in gdn_mfma.hip): every contraction is an FP32 FMA loop over tiles staged
+// in LDS.  A workgroup owns one value head and a DVT-wide slice
 // of dv for one prompt, keeps that slice of the state resident in LDS while
 // it walks the prompt's chunks, and writes the state back once at the end.
 #include "lrc_device.h"
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void tri_inverse_kernel(const float* __re
 hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                       const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv, lrc_dtype dt,
                       hipStream_t st) {
-    if (dt == LRC_BF16) return dispatch_dk<uint16_t>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    if (dt == LRC_BF16) return launch_gdn_bf16_mfma(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
     return dispatch_dk<float>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
 }
 

@@ -42,6 +42,9 @@ hipError_t launch_wkv4(const float* k, const float* v, const float* w, const flo
 hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                       const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
                       lrc_dtype dt, hipStream_t st);
+hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                                float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
+                                int dv, hipStream_t st);
 hipError_t launch_unit_lower_inverse(const float* A, float* T, int batch, int n, hipStream_t st);
 
 }  // namespace lrc
