@@ -12,20 +12,68 @@
 //        [[T11, 0], [L21, T22]]  ->  T21 = -T22 (L21 T11),
 //    where T11, T22 are the inverted s x s blocks of the previous level and
 //    L21 is the untouched block of A below T11.
+// All loops have compile-time trip counts and read 16-byte row segments, so
+// the loads of a level issue together instead of one dependent load at a
+// time.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace lrc {
 
-constexpr int kTriLd = 65;  // row stride of the 64x64 matrix in LDS (floats)
+constexpr int kTriLd = 68;  // row stride of the 64x64 matrix in LDS (floats), 16-byte aligned rows
 
-// Scratch: 3 x 8 x 64 floats for the Neumann stage, 32 x 32 for the levels.
+// Scratch: 3 x 8 x 64 floats for the Neumann stage, up to 32 x 32 for the levels.
 constexpr int kTriScratch = 3 * 8 * 64;
 
-// In:  M[i * kTriLd + j] holds A_ij for j < i (the strictly lower part);
-//      entries on and above the diagonal are ignored.
-// Out: M holds T = (I + A)^-1 in full (ones on the diagonal, zeros above).
+template <int s>
+__device__ __forceinline__ void tri_level(float* M, float* Y) {
+    constexpr int quads = 8 * s;            // (64 / 2s) blocks x s*s/4 output quads
+    constexpr int per = s * s / 4;          // quads per block
+    const int tid = threadIdx.x;
+    int b = 0, r = 0, c = 0, base = 0;
+    if (tid < quads) {
+        b = tid / per;
+        r = (tid % per) / (s / 4);
+        c = (tid % (s / 4)) * 4;
+        base = b * 2 * s;
+        // Y_b = L21_b T11_b (entries of T11 above its diagonal are zero)
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float* l21 = M + (base + s + r) * kTriLd + base;
+#pragma unroll
+        for (int m = 0; m < s; ++m) {
+            const float l = l21[m];
+            const float4 t = *reinterpret_cast<const float4*>(M + (base + m) * kTriLd + base + c);
+            acc.x = fmaf(l, t.x, acc.x);
+            acc.y = fmaf(l, t.y, acc.y);
+            acc.z = fmaf(l, t.z, acc.z);
+            acc.w = fmaf(l, t.w, acc.w);
+        }
+        *reinterpret_cast<float4*>(Y + b * s * s + r * s + c) = acc;
+    }
+    __syncthreads();
+    if (tid < quads) {
+        // T21_b = -T22_b Y_b, written over L21_b (entries of T22 above its diagonal are zero)
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float* t22 = M + (base + s + r) * kTriLd + base + s;
+#pragma unroll
+        for (int m = 0; m < s; ++m) {
+            const float t = t22[m];
+            const float4 y = *reinterpret_cast<const float4*>(Y + b * s * s + m * s + c);
+            acc.x = fmaf(t, y.x, acc.x);
+            acc.y = fmaf(t, y.y, acc.y);
+            acc.z = fmaf(t, y.z, acc.z);
+            acc.w = fmaf(t, y.w, acc.w);
+        }
+        *reinterpret_cast<float4*>(M + (base + s + r) * kTriLd + base + c) =
+            make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
+    }
+    __syncthreads();
+}
+
+// In:  M[i * kTriLd + j] holds A_ij for j < i; entries above the diagonal
+//      must be zero; diagonal entries are ignored.
+// Out: M holds T = (I + A)^-1 (ones on the diagonal, zeros above).
 // All 256 threads of the block must call it; it begins and ends with a
 // barrier.
 __device__ inline void tri_inverse64(float* M, float* scratch) {
@@ -35,7 +83,7 @@ __device__ inline void tri_inverse64(float* M, float* scratch) {
     float* N2 = scratch;
     float* N4 = scratch + 512;
     float* X = scratch + 1024;
-    auto Nb = [&](int blk, int r, int c) -> float {  // strictly lower part of diagonal block
+    auto Nb = [&](int blk, int r, int c) -> float {  // strictly lower part of a diagonal block
         return c < r ? M[(blk * 8 + r) * kTriLd + blk * 8 + c] : 0.f;
     };
 #pragma unroll
@@ -79,41 +127,11 @@ __device__ inline void tri_inverse64(float* M, float* scratch) {
         const int e = tid * 2 + e2, blk = e >> 6, r = (e >> 3) & 7, c = e & 7;
         M[(blk * 8 + r) * kTriLd + blk * 8 + c] = tnew[e2];
     }
-    // ---- Levels: s = 8, 16, 32.
-    float* Y = scratch;  // holds L21 T11 for every block of the level (64 * s / 2 <= 1024 floats)
-#pragma unroll
-    for (int s = 8; s <= 32; s *= 2) {
-        const int nblk = 64 / (2 * s);
-        const int per = s * s;  // entries per block
-        __syncthreads();
-        // Y_b = L21_b T11_b
-        for (int e = tid; e < nblk * per; e += 256) {
-            const int b = e / per, r = (e % per) / s, c = e % s;
-            const int base = b * 2 * s;
-            const float* l21 = M + (base + s + r) * kTriLd + base;
-            float acc = 0.f;
-            for (int m = c; m < s; ++m) acc = fmaf(l21[m], M[(base + m) * kTriLd + base + c], acc);  // T11 lower
-            Y[e] = acc;
-        }
-        __syncthreads();
-        // T21_b = -T22_b Y_b, written over L21_b
-        for (int e = tid; e < nblk * per; e += 256) {
-            const int b = e / per, r = (e % per) / s, c = e % s;
-            const int base = b * 2 * s;
-            const float* t22 = M + (base + s + r) * kTriLd + base + s;
-            const float* y = Y + b * per;
-            float acc = 0.f;
-            for (int m = 0; m <= r; ++m) acc = fmaf(t22[m], y[m * s + c], acc);  // T22 lower
-            M[(base + s + r) * kTriLd + base + c] = -acc;
-        }
-    }
     __syncthreads();
-    // Upper triangle to zero (the diagonal already holds ones).
-    for (int e = tid; e < 64 * 64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        if (c > r) M[r * kTriLd + c] = 0.f;
-    }
-    __syncthreads();
+    // ---- Levels s = 8, 16, 32 (two barriers each, the last one closes the routine).
+    tri_level<8>(M, scratch);
+    tri_level<16>(M, scratch);
+    tri_level<32>(M, scratch);
 }
 
 }  // namespace lrc
