@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void gdn_f32_kernel(const TIN* __restrict
                 }
         }
         // ---- T = (I + A)^-1 (barriers inside)
-        tri_inverse64(sm.M, sm.scratch);
+        tri_inverse64<kThreads / 64>(sm.M, sm.scratch);
 
         // ---- RHS = diag(beta) V - diag(beta Gamma) K S_0, in registers
         float rhs[4][CPT];
@@ -322,14 +322,14 @@ hipError_t dispatch_dk(const void* q, const void* k, const void* v, const float*
 // Standalone inverse: one workgroup per matrix.
 __global__ __launch_bounds__(kThreads) void tri_inverse_kernel(const float* __restrict__ A, float* __restrict__ T,
                                                               int n) {
-    __shared__ float M[64 * kTriLd];
-    __shared__ float scratch[kTriScratch];
+    __shared__ __align__(16) float M[64 * kTriLd];
+    __shared__ __align__(16) float scratch[kTriScratch];
     const long base = (long)blockIdx.x * n * n;
     for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
         const int r = e >> 6, c = e & 63;
         M[r * kTriLd + c] = (r < n && c < r) ? A[base + (long)r * n + c] : 0.f;
     }
-    tri_inverse64(M, scratch);
+    tri_inverse64<kThreads / 64>(M, scratch);
     for (int e = threadIdx.x; e < n * n; e += kThreads) {
         const int r = e / n, c = e % n;
         T[base + e] = M[r * kTriLd + c];

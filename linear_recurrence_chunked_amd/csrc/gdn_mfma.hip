@@ -8,35 +8,39 @@
 //   U    = (I + A)^-1 (diag(beta) V - diag(beta Gamma) K S_0)
 //   O    = diag(Gamma) Q S_0 + (e^{gamma_t - gamma_i} q_t.k_i)_{i <= t} U
 //   S_S  = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
-// gamma_S is the last entry of the same cumulative sum; the decay factors
-// are formed element by element from differences of gamma.
+// gamma_S is the last entry of the same cumulative sum.
 //
-// Work split.  A workgroup (4 waves) owns value head h and a DVT-wide slice
-// of dv for one prompt and walks the prompt's chunks.  Wave w owns 16 state
-// columns; its [dk x 16] state slice, and its columns of RHS, U and Q S_0,
-// stay in MFMA accumulators in registers for the whole prompt.  Only the
-// operands every wave needs sit in LDS: the chunk's K, Q, V, K^T, the FP32
-// matrix A -> T for the inverse, T and P.  After the inverse no barrier is
-// needed until the next chunk.
+// Work split.  A workgroup owns a DVT-wide slice (DVT = min(dv, 64)) of one
+// value head of one prompt and walks the prompt's chunks; it has DVT/16 waves
+// and wave w owns state columns 16w .. 16w+15 of the slice.  A wave's [dk x 16] state slice, and its columns of RHS, U
+// and Q S_0, stay in MFMA accumulators in registers for the whole prompt.
+// Only operands every wave needs sit in LDS: the chunk's K, Q, V, K^T, the
+// FP32 matrix A -> T for the inverse, T and P.  The waves share the
+// per-chunk work that does not depend on the column (the masked products,
+// the inverse, K^T); after the inverse no barrier is needed until the next
+// chunk.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
 // of lane l is row l%16 with 8 k-values, the B operand column l%16 with the
 // same 8 k-values, and the accumulator holds column l%16, rows 4(l/16) .. +3.
-// A wave's own [rows x 16] accumulators therefore serve directly as B
-// operands when the k-values of lane group g are taken as rows
-// {4g .. 4g+3} of one 16-row tile and {16+4g .. 16+4g+3} of the next; the A
-// operand then reads the same two 4-element runs of its row from LDS.
+// A wave's own [rows x 16] accumulators serve directly as B operands when
+// the k-values of lane group g are taken as rows {4g .. 4g+3} of one 16-row
+// tile and {16+4g .. 16+4g+3} of the next; the A operand then reads the same
+// two 4-element runs of its row from LDS.  The masked products are computed
+// transposed (keys as rows), so each lane holds 4 consecutive keys of one
+// query and writes them as one packed store.
 // FP32 operands enter as a hi + lo pair of bf16 (hi = bf16(x),
 // lo = bf16(x - hi)), about 16 mantissa bits:
 //   K K^T, Q K^T        bf16 x bf16 (exact products)            1 pass
 //   K S_0, Q S_0        bf16 x (S_0 hi, lo)                     2 passes
 //   K^T (d U)           bf16 x (decayed U hi, lo)               2 passes
 //   T RHS, P U          (hi, lo) x (hi, lo) without lo x lo     3 passes
-// The decay e^{min(gamma_S - gamma_r, 0)} of the state update is applied to
-// the rows of U, so K^T enters exact.  The 64-row inverse (8x8 Neumann
-// blocks, then 2x2 block levels) runs in FP32 on the vector units.  The next
-// chunk's K, Q, V, beta and g are loaded into registers while the current
-// chunk computes.
+// Decay factors: on the diagonal 16x16 tiles e^{gamma_i - gamma_j} is formed
+// per element; below them it is the product e^{gamma_i - gamma_c}
+// e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
+// The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) runs in
+// FP32 on the FP32 matrix cores.  The next chunk's K, Q, V, beta and g are loaded
+// into registers while the current chunk computes.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 #include "tri_inverse.h"
@@ -48,7 +52,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int L64 = 64 + 8;  // row stride (bf16) of 64-column operands
 
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
@@ -74,9 +77,12 @@ __device__ __forceinline__ void acc_frag(const floatx4& t0, const floatx4& t1, b
         lo[4 + r] = static_cast<__bf16>(t1[r] - static_cast<float>(h1));
     }
 }
-__device__ __forceinline__ void split(float x, __bf16& hi, __bf16& lo) {
-    hi = static_cast<__bf16>(x);
-    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+__device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        hi[r] = static_cast<__bf16>(x[r]);
+        lo[r] = static_cast<__bf16>(x[r] - static_cast<float>(hi[r]));
+    }
 }
 
 template <int DK, int DVT>
@@ -85,7 +91,7 @@ struct MfmaSmem {
     static constexpr int LDV = DVT + 8;
     __bf16 K[64 * LDK];
     __bf16 Q[64 * LDK];
-    __bf16 KT[DK * L64];   // K^T, exact
+    __bf16 KT[DK * L64];    // K^T, exact
     __bf16 V[64 * LDV];
     __bf16 P_hi[64 * L64];  // masked decayed Q K^T
     __bf16 P_lo[64 * L64];
@@ -94,31 +100,32 @@ struct MfmaSmem {
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
     float gam[64];
+    float Gam[64];          // e^gamma
     float beta[64];
     float decS[64];         // e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
 };
 
-template <int DK, int DVT>
-struct Prefetch {
-    static constexpr int NK = 64 * DK / 8 / kThreads;    // 16-byte pieces of K (and of Q) per thread
-    static constexpr int NV = (64 * DVT / 8 + kThreads - 1) / kThreads;
-    uint4 k[NK], q[NK], v[NV];
-    float g, beta;
-};
+// Lower-triangular 16x16 tile pairs (query tile, key tile) of the 64x64 masks.
+__constant__ int kPairs[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 template <int DK, int DVT>
-__global__ __launch_bounds__(kThreads) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v,
-                                                           const float* __restrict__ beta,
-                                                           const float* __restrict__ g, float* __restrict__ o,
-                                                           const float* S_in, float* S_out, Batch bt, int Hk, int Hv,
-                                                           int dv) {
+__global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const float* __restrict__ beta,
+                                                          const float* __restrict__ g, float* __restrict__ o,
+                                                          const float* S_in, float* S_out, Batch bt, int Hk, int Hv,
+                                                          int dv) {
     using Sm = MfmaSmem<DK, DVT>;
-    using Pf = Prefetch<DK, DVT>;
+    constexpr int NW = DVT / 16;           // waves: one per 16 state columns
+    constexpr int NT = NW * 64;
     constexpr int LDK = Sm::LDK, LDV = Sm::LDV;
-    constexpr int KS = DK / 32;   // k-steps over dk
-    constexpr int RT = DK / 16;   // state row tiles
+    constexpr int KS = DK / 32;            // k-steps over dk
+    constexpr int RT = DK / 16;            // state row tiles
+    constexpr int PK = 64 * DK / 8;        // 16-byte pieces of a K (or Q) chunk
+    constexpr int PV = 64 * DVT / 8;
+    constexpr int NK = (PK + NT - 1) / NT;
+    constexpr int NV = (PV + NT - 1) / NT;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
@@ -128,47 +135,49 @@ __global__ __launch_bounds__(kThreads) void gdn_mfma_kernel(const uint16_t* __re
     const int lg = lane >> 4;        // lane group
     const int lk = lg * 8;           // contiguous fragment k offset
     const int lq = lg * 4;           // accumulator row offset
-    const bool owner = 16 * w < DVT; // this wave owns state columns 16w .. 16w+15 of the slice
     const int ntile = dv / DVT;
     const int h = blockIdx.x / ntile;
-    const int vt = blockIdx.x % ntile;
+    const int c0v = (blockIdx.x % ntile) * DVT;  // first column of the slice
     const int kh = h / (Hv / Hk);
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
-    const long sbase = ((long)p * Hv + h) * DK * dv + vt * DVT + 16 * w;
+    const long sbase = ((long)p * Hv + h) * DK * dv + c0v + 16 * w;
 
     floatx4 sacc[RT];
 #pragma unroll
     for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[tr][r] = owner ? S_in[sbase + (long)(16 * tr + lq + r) * dv + lr] : 0.f;
+        for (int r = 0; r < 4; ++r) sacc[tr][r] = S_in[sbase + (long)(16 * tr + lq + r) * dv + lr];
+    // The masks' tiles above the diagonal stay zero for the whole prompt.
+    for (int e = tid; e < 64 * kTriLd; e += NT) sm.M[e] = 0.f;
+    for (int e = tid; e < 64 * L64; e += NT) sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
 
-    Pf pf;
+    uint4 pk[NK], pq[NK], pv[NV];
+    float pg = 0.f, pb = 0.f;
     auto fetch = [&](int c0) {
         const int S = min(64, L - c0);
 #pragma unroll
-        for (int x = 0; x < Pf::NK; ++x) {
-            const int e = tid + x * kThreads, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            pf.k[x] = pf.q[x] = make_uint4(0, 0, 0, 0);
-            if (r < S) {
+        for (int x = 0; x < NK; ++x) {
+            const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+            pk[x] = pq[x] = make_uint4(0, 0, 0, 0);
+            if (e < PK && r < S) {
                 const long off = ((row0 + c0 + r) * Hk + kh) * DK + c8;
-                pf.k[x] = *reinterpret_cast<const uint4*>(k + off);
-                pf.q[x] = *reinterpret_cast<const uint4*>(q + off);
+                pk[x] = *reinterpret_cast<const uint4*>(k + off);
+                pq[x] = *reinterpret_cast<const uint4*>(q + off);
             }
         }
 #pragma unroll
-        for (int x = 0; x < Pf::NV; ++x) {
-            const int e = tid + x * kThreads, r = e / (DVT / 8), c8 = (e % (DVT / 8)) * 8;
-            pf.v[x] = make_uint4(0, 0, 0, 0);
-            if (e < 64 * DVT / 8 && r < S)
-                pf.v[x] = *reinterpret_cast<const uint4*>(v + ((row0 + c0 + r) * Hv + h) * (long)dv + vt * DVT + c8);
+        for (int x = 0; x < NV; ++x) {
+            const int e = tid + x * NT, r = e / (DVT / 8), c8 = (e % (DVT / 8)) * 8;
+            pv[x] = make_uint4(0, 0, 0, 0);
+            if (e < PV && r < S)
+                pv[x] = *reinterpret_cast<const uint4*>(v + ((row0 + c0 + r) * Hv + h) * (long)dv + c0v + c8);
         }
-        pf.g = 0.f;
-        pf.beta = 0.f;
+        pg = pb = 0.f;
         if (tid < S) {
-            pf.g = g[(row0 + c0 + tid) * Hv + h];
-            pf.beta = beta[(row0 + c0 + tid) * Hv + h];
+            pg = g[(row0 + c0 + tid) * Hv + h];
+            pb = beta[(row0 + c0 + tid) * Hv + h];
         }
     };
 
@@ -176,103 +185,137 @@ __global__ __launch_bounds__(kThreads) void gdn_mfma_kernel(const uint16_t* __re
     for (int c0 = 0; c0 < L; c0 += 64) {
         const int S = min(64, L - c0);
         __syncthreads();  // previous chunk done with every LDS buffer
-        // ---- stage the prefetched chunk: K, K^T, Q, V, beta, gamma
+        // ---- stage the prefetched chunk: K, Q, V, beta, gamma, Gamma, decay of the state update
 #pragma unroll
-        for (int x = 0; x < Pf::NK; ++x) {
-            const int e = tid + x * kThreads, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sm.K[r * LDK + c8]) = pf.k[x];
-            *reinterpret_cast<uint4*>(&sm.Q[r * LDK + c8]) = pf.q[x];
-            const uint32_t wd[4] = {pf.k[x].x, pf.k[x].y, pf.k[x].z, pf.k[x].w};
-            uint16_t* kt = reinterpret_cast<uint16_t*>(sm.KT);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kt[(c8 + 2 * i) * L64 + r] = uint16_t(wd[i] & 0xffffu);
-                kt[(c8 + 2 * i + 1) * L64 + r] = uint16_t(wd[i] >> 16);
+        for (int x = 0; x < NK; ++x) {
+            const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+            if (e < PK) {
+                *reinterpret_cast<uint4*>(&sm.K[r * LDK + c8]) = pk[x];
+                *reinterpret_cast<uint4*>(&sm.Q[r * LDK + c8]) = pq[x];
             }
         }
 #pragma unroll
-        for (int x = 0; x < Pf::NV; ++x) {
-            const int e = tid + x * kThreads, r = e / (DVT / 8), c8 = (e % (DVT / 8)) * 8;
-            if (e < 64 * DVT / 8) *reinterpret_cast<uint4*>(&sm.V[r * LDV + c8]) = pf.v[x];
+        for (int x = 0; x < NV; ++x) {
+            const int e = tid + x * NT, r = e / (DVT / 8), c8 = (e % (DVT / 8)) * 8;
+            if (e < PV) *reinterpret_cast<uint4*>(&sm.V[r * LDV + c8]) = pv[x];
         }
         if (tid < 64) {
-            sm.beta[tid] = pf.beta;
-            float x = pf.g;  // inclusive prefix sum over the wave
+            sm.beta[tid] = pb;
+            float x = pg;  // inclusive prefix sum over the wave
 #pragma unroll
             for (int s = 1; s < 64; s <<= 1) {
                 const float y = __shfl_up(x, s, 64);
                 if (tid >= s) x += y;
             }
             sm.gam[tid] = x;
+            sm.Gam[tid] = fast_exp(x);
             const float gS = __shfl(x, S - 1, 64);
             sm.decS[tid] = tid < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
         }
         if (c0 + 64 < L) fetch(c0 + 64);
         __syncthreads();
 
+        // ---- shared: K^T by 4-row x 8-column blocks (the inverse's barriers order it before use)
+        for (int b = tid; b < 2 * DK; b += NT) {
+            const int n = b & 15, m = b >> 4;  // rows 4n .. 4n+3, columns 8m .. 8m+7
+            uint4 rw[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) rw[a] = *reinterpret_cast<const uint4*>(&sm.K[(4 * n + a) * LDK + 8 * m]);
+            const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
+            const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
+            const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
+            const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
+                uint2 out;
+                out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
+                out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
+                *reinterpret_cast<uint2*>(&sm.KT[(8 * m + e) * L64 + 4 * n]) = out;
+            }
+        }
+
         // ---- private: K S_0 and Q S_0 for this wave's columns (B from the state accumulators)
         floatx4 ks0[4], qs0[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) ks0[t] = qs0[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (owner) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 bh, bl;
+            acc_frag(sacc[2 * s], sacc[2 * s + 1], bh, bl);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8 ak = frag_perm(&sm.K[(16 * t + lr) * LDK + 32 * s], lg);
+                const bf16x8 aq = frag_perm(&sm.Q[(16 * t + lr) * LDK + 32 * s], lg);
+                ks0[t] = mfma(ak, bh, ks0[t]);
+                ks0[t] = mfma(ak, bl, ks0[t]);
+                qs0[t] = mfma(aq, bh, qs0[t]);
+                qs0[t] = mfma(aq, bl, qs0[t]);
+            }
+        }
+        // ---- shared: masked products, transposed (keys as rows) -> A (FP32) and P (hi/lo)
+        for (int pr = w; pr < 10; pr += NW) {
+            const int ti = kPairs[pr][0], tj = kPairs[pr][1];  // query tile, key tile
+            floatx4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                bf16x8 bh, bl;
-                acc_frag(sacc[2 * s], sacc[2 * s + 1], bh, bl);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const bf16x8 ak = frag_perm(&sm.K[(16 * t + lr) * LDK + 32 * s], lg);
-                    const bf16x8 aq = frag_perm(&sm.Q[(16 * t + lr) * LDK + 32 * s], lg);
-                    ks0[t] = mfma(ak, bh, ks0[t]);
-                    ks0[t] = mfma(ak, bl, ks0[t]);
-                    qs0[t] = mfma(aq, bh, qs0[t]);
-                    qs0[t] = mfma(aq, bl, qs0[t]);
-                }
+                const bf16x8 ak = frag(&sm.K[(16 * tj + lr) * LDK + 32 * s + lk]);
+                kk = mfma(ak, frag(&sm.K[(16 * ti + lr) * LDK + 32 * s + lk]), kk);
+                qk = mfma(ak, frag(&sm.Q[(16 * ti + lr) * LDK + 32 * s + lk]), qk);
             }
-        }
-        // ---- shared: K K^T and Q K^T for row tile w -> A (FP32, strictly lower) and P (hi/lo)
+            const int i = 16 * ti + lr;  // query row of this lane
+            const float gi = sm.gam[i];
+            floatx4 dec;
+            if (ti > tj) {
+                const float gc = sm.gam[16 * ti];
+                const float rowf = fast_exp(gi - gc);
 #pragma unroll
-        for (int tc = 0; tc < 4; ++tc) {
-            floatx4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
-            if (tc <= w) {
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const bf16x8 bk = frag(&sm.K[(16 * tc + lr) * LDK + 32 * s + lk]);
-                    kk = mfma(frag(&sm.K[(16 * w + lr) * LDK + 32 * s + lk]), bk, kk);
-                    qk = mfma(frag(&sm.Q[(16 * w + lr) * LDK + 32 * s + lk]), bk, qk);
-                }
-            }
-            const int j = 16 * tc + lr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + lq + r;
-                const float dec = i >= j ? fast_exp(sm.gam[i] - sm.gam[j]) : 0.f;
-                sm.M[i * kTriLd + j] = i > j ? sm.beta[i] * dec * kk[r] : 0.f;
-                split(i >= j ? dec * qk[r] : 0.f, sm.P_hi[i * L64 + j], sm.P_lo[i * L64 + j]);
-            }
-        }
-        // ---- RHS = diag(beta) V - diag(beta Gamma) K S_0 (private, in registers)
-        if (owner) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
+                for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - sm.gam[16 * tj + lq + r]);
+            } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * t + lq + r;
-                    const float bi = sm.beta[i];
-                    ks0[t][r] = bi * static_cast<float>(sm.V[i * LDV + 16 * w + lr]) -
-                                bi * fast_exp(sm.gam[i]) * ks0[t][r];
+                    const int j = 16 * tj + lq + r;
+                    dec[r] = i >= j ? fast_exp(gi - sm.gam[j]) : 0.f;
                 }
+            }
+            const float bi = sm.beta[i];
+            floatx4 av, pv4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * tj + lq + r;
+                av[r] = i > j ? bi * dec[r] * kk[r] : 0.f;
+                pv4[r] = dec[r] * qk[r];
+            }
+            *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
+            bf16x4 ph, pl;
+            split4(pv4, ph, pl);
+            *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj + lq]) = ph;
+            *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj + lq]) = pl;
         }
-        // ---- T = (I + A)^-1 in FP32 (barriers inside), then T as hi/lo bf16
-        tri_inverse64(sm.M, sm.scratch);
-        for (int e = tid; e < 64 * 64; e += kThreads) {
-            const int r = e >> 6, c = e & 63;
-            split(sm.M[r * kTriLd + c], sm.T_hi[r * L64 + c], sm.T_lo[r * L64 + c]);
+        // ---- private: RHS = diag(beta) V - diag(beta Gamma) K S_0, in registers
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * t + lq + r;
+                const float bi = sm.beta[i];
+                ks0[t][r] = bi * (static_cast<float>(sm.V[i * LDV + 16 * w + lr]) - sm.Gam[i] * ks0[t][r]);
+            }
+        // ---- shared: T = (I + A)^-1 in FP32 (barriers inside), then T as hi/lo bf16
+        tri_inverse64<NW>(sm.M, sm.scratch);
+        for (int x = tid; x < 512; x += NT) {
+            const int r = x >> 3, c = (x & 7) * 8;
+            const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c]);
+            const floatx4 b = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c + 4]);
+            bf16x4 ah, al, bh, bl;
+            split4(a, ah, al);
+            split4(b, bh, bl);
+            *reinterpret_cast<bf16x8*>(&sm.T_hi[r * L64 + c]) = bf16x8{ah[0], ah[1], ah[2], ah[3], bh[0], bh[1], bh[2], bh[3]};
+            *reinterpret_cast<bf16x8*>(&sm.T_lo[r * L64 + c]) = bf16x8{al[0], al[1], al[2], al[3], bl[0], bl[1], bl[2], bl[3]};
         }
         __syncthreads();
-        if (!owner) continue;
 
-        // ---- U = T RHS (T lower triangular: k-steps up to the row tile's diagonal)
+        // ---- private: U = T RHS (T lower triangular: k-steps up to the row tile's diagonal)
         floatx4 u[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) u[t] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -289,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void gdn_mfma_kernel(const uint16_t* __re
                 u[t] = mfma(al, bh, u[t]);
             }
         }
-        // ---- O = diag(Gamma) Q S_0 + P U for this wave's columns
+        // ---- private: O = diag(Gamma) Q S_0 + P U for this wave's columns
         {
             floatx4 pu[4];
 #pragma unroll
@@ -313,13 +356,13 @@ __global__ __launch_bounds__(kThreads) void gdn_mfma_kernel(const uint16_t* __re
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * t + lq + r;
                     if (i < S)
-                        o[((row0 + c0 + i) * Hv + h) * (long)dv + vt * DVT + 16 * w + lr] =
-                            fmaf(fast_exp(sm.gam[i]), qs0[t][r], pu[t][r]);
+                        o[((row0 + c0 + i) * Hv + h) * (long)dv + c0v + 16 * w + lr] =
+                            fmaf(sm.Gam[i], qs0[t][r], pu[t][r]);
                 }
         }
-        // ---- S_S = e^{gamma_S} S_0 + K^T (decS * U), in the state accumulators
+        // ---- private: S_S = e^{gamma_S} S_0 + K^T (decS * U), in the state accumulators
         {
-            const float GS = fast_exp(sm.gam[S - 1]);
+            const float GS = sm.Gam[S - 1];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -339,12 +382,10 @@ __global__ __launch_bounds__(kThreads) void gdn_mfma_kernel(const uint16_t* __re
             }
         }
     }
-    if (owner) {
 #pragma unroll
-        for (int tr = 0; tr < RT; ++tr)
+    for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S_out[sbase + (long)(16 * tr + lq + r) * dv + lr] = sacc[tr][r];
-    }
+        for (int r = 0; r < 4; ++r) S_out[sbase + (long)(16 * tr + lq + r) * dv + lr] = sacc[tr][r];
 }
 
 template <int DK, int DVT>
@@ -360,10 +401,22 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const float*
         configured = true;
     }
     const dim3 grid((unsigned)(Hv * (dv / DVT)), (unsigned)bt.P);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, static_cast<const uint16_t*>(q),
+    hipLaunchKernelGGL(kern, grid, dim3(DVT * 4), smem, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, g, o, S_in, S_out, bt,
                        Hk, Hv, dv);
     return hipGetLastError();
+}
+
+template <int DVT>
+hipError_t launch_dk(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
+                     const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
+                     hipStream_t st) {
+    switch (dk) {
+        case 32: return launch_mfma<32, DVT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 64: return launch_mfma<64, DVT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 128: return launch_mfma<128, DVT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -371,20 +424,8 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const float*
 hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, const float* beta, const float* g,
                                 float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
                                 int dv, hipStream_t st) {
-    if (dv >= 64) {
-        switch (dk) {
-            case 32: return launch_mfma<32, 64>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-            case 64: return launch_mfma<64, 64>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-            case 128: return launch_mfma<128, 64>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-        }
-    } else {
-        switch (dk) {
-            case 32: return launch_mfma<32, 32>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-            case 64: return launch_mfma<64, 32>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-            case 128: return launch_mfma<128, 32>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-        }
-    }
-    return hipErrorInvalidValue;
+    if (dv == 32) return launch_dk<32>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    return launch_dk<64>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
 }
 
 }  // namespace lrc

@@ -1,5 +1,6 @@
-// Unit lower-triangular inverse on a 64-row padding, for one workgroup of
-// 256 threads, in LDS, FP32.
+// Unit lower-triangular inverse on a 64-row padding, FP32, in LDS, on the
+// FP32 matrix cores of CDNA4 (v_mfma_f32_16x16x4f32), for one workgroup of NW
+// waves.
 //
 // Source: "perf(qwen3_5): prefill text prompts in multi-token chunks",
 // Implementation -- I + A is inverted on a fixed 64-row padding (padded rows
@@ -12,126 +13,139 @@
 //        [[T11, 0], [L21, T22]]  ->  T21 = -T22 (L21 T11),
 //    where T11, T22 are the inverted s x s blocks of the previous level and
 //    L21 is the untouched block of A below T11.
-// All loops have compile-time trip counts and read 16-byte row segments, so
-// the loads of a level issue together instead of one dependent load at a
-// time.
+//
+// Mapping.  Everything is a product of 16x16 tiles.  A wave inverts one
+// diagonal 16x16 tile alone: N holds the strictly lower parts of its two 8x8
+// diagonal blocks, D = (I - N)(I + N^2)(I + N^4) inverts both at once, and the
+// level-8 step is T = D - D (L D) with L the tile's lower-left 8x8 block of A.
+// The level-16 and level-32 steps follow with workgroup barriers between
+// them (five barriers in all).  Products run in FP32 with FP32 accumulation.
+//
+// Tile product Z = X Y: lane l holds, for X, the row segment
+// X[l%16][4g .. 4g+3] (g = l/16) and, for Y, the accumulator-layout column
+// slice Y[4g .. 4g+3][l%16]; the four 16x16x4 steps pair k = 4g + kk on both
+// sides, so Y can be a previous product's accumulator as it is.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace lrc {
 
-constexpr int kTriLd = 68;  // row stride of the 64x64 matrix in LDS (floats), 16-byte aligned rows
+constexpr int kTriLd = 68;            // row stride of the 64x64 matrix in LDS (floats), 16-byte aligned rows
+constexpr int kTriScratch = 4 * 16 * 20;  // floats: four 16x20 tiles, later the 32x36 level-32 product
 
-// Scratch: 3 x 8 x 64 floats for the Neumann stage, up to 32 x 32 for the levels.
-constexpr int kTriScratch = 3 * 8 * 64;
+typedef float tri_f4 __attribute__((ext_vector_type(4)));
 
-template <int s>
-__device__ __forceinline__ void tri_level(float* M, float* Y) {
-    constexpr int quads = 8 * s;            // (64 / 2s) blocks x s*s/4 output quads
-    constexpr int per = s * s / 4;          // quads per block
-    const int tid = threadIdx.x;
-    int b = 0, r = 0, c = 0, base = 0;
-    if (tid < quads) {
-        b = tid / per;
-        r = (tid % per) / (s / 4);
-        c = (tid % (s / 4)) * 4;
-        base = b * 2 * s;
-        // Y_b = L21_b T11_b (entries of T11 above its diagonal are zero)
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float* l21 = M + (base + s + r) * kTriLd + base;
-#pragma unroll
-        for (int m = 0; m < s; ++m) {
-            const float l = l21[m];
-            const float4 t = *reinterpret_cast<const float4*>(M + (base + m) * kTriLd + base + c);
-            acc.x = fmaf(l, t.x, acc.x);
-            acc.y = fmaf(l, t.y, acc.y);
-            acc.z = fmaf(l, t.z, acc.z);
-            acc.w = fmaf(l, t.w, acc.w);
-        }
-        *reinterpret_cast<float4*>(Y + b * s * s + r * s + c) = acc;
-    }
-    __syncthreads();
-    if (tid < quads) {
-        // T21_b = -T22_b Y_b, written over L21_b (entries of T22 above its diagonal are zero)
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        const float* t22 = M + (base + s + r) * kTriLd + base + s;
-#pragma unroll
-        for (int m = 0; m < s; ++m) {
-            const float t = t22[m];
-            const float4 y = *reinterpret_cast<const float4*>(Y + b * s * s + m * s + c);
-            acc.x = fmaf(t, y.x, acc.x);
-            acc.y = fmaf(t, y.y, acc.y);
-            acc.z = fmaf(t, y.z, acc.z);
-            acc.w = fmaf(t, y.w, acc.w);
-        }
-        *reinterpret_cast<float4*>(M + (base + s + r) * kTriLd + base + c) =
-            make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
-    }
-    __syncthreads();
+namespace tri {
+
+__device__ __forceinline__ tri_f4 mm(tri_f4 z, tri_f4 xrow, tri_f4 yc) {
+    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[0], yc[0], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[1], yc[1], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[2], yc[2], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[3], yc[3], z, 0, 0, 0);
+    return z;
 }
+// Row segment X[lr][4g .. 4g+3] of a row-major tile.
+__device__ __forceinline__ tri_f4 ld_row(const float* t, int ld, int lr, int g) {
+    return *reinterpret_cast<const tri_f4*>(t + lr * ld + 4 * g);
+}
+// Accumulator-layout slice Y[4g .. 4g+3][lr] of a row-major tile.
+__device__ __forceinline__ tri_f4 ld_acc(const float* t, int ld, int lr, int g) {
+    return tri_f4{t[(4 * g) * ld + lr], t[(4 * g + 1) * ld + lr], t[(4 * g + 2) * ld + lr], t[(4 * g + 3) * ld + lr]};
+}
+__device__ __forceinline__ void st_acc(float* t, int ld, int lr, int g, tri_f4 v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[(4 * g + r) * ld + lr] = v[r];
+}
+// Order this wave's LDS writes before its later LDS reads of other lanes' data.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+}  // namespace tri
 
 // In:  M[i * kTriLd + j] holds A_ij for j < i; entries above the diagonal
 //      must be zero; diagonal entries are ignored.
 // Out: M holds T = (I + A)^-1 (ones on the diagonal, zeros above).
-// All 256 threads of the block must call it; it begins and ends with a
-// barrier.
+// All NW waves of the block must call it; it begins and ends with a barrier.
+template <int NW>
 __device__ inline void tri_inverse64(float* M, float* scratch) {
-    const int tid = threadIdx.x;
+    using tri::ld_acc;
+    using tri::ld_row;
+    using tri::mm;
+    using tri::st_acc;
+    constexpr int ld = kTriLd;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lr = lane & 15, g = lane >> 4;
+    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     __syncthreads();
-    // ---- Neumann stage: 8 blocks x 64 entries, 2 entries per thread.
-    float* N2 = scratch;
-    float* N4 = scratch + 512;
-    float* X = scratch + 1024;
-    auto Nb = [&](int blk, int r, int c) -> float {  // strictly lower part of a diagonal block
-        return c < r ? M[(blk * 8 + r) * kTriLd + blk * 8 + c] : 0.f;
-    };
+
+    // ---- diagonal 16x16 tiles: Neumann on the 8x8 blocks, then the level-8 step
+    for (int t = w; t < 4; t += NW) {
+        float* Mt = M + 16 * t * ld + 16 * t;
+        float* S = scratch + t * 16 * 20;
+        tri_f4 nrow = ld_row(Mt, ld, lr, g), nacc = ld_acc(Mt, ld, lr, g);
+        tri_f4 lorow = nrow;
 #pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-        const int e = tid * 2 + e2, blk = e >> 6, r = (e >> 3) & 7, c = e & 7;
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) s = fmaf(Nb(blk, r, m), Nb(blk, m, c), s);
-        N2[e] = s;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-        const int e = tid * 2 + e2, blk = e >> 6, r = (e >> 3) & 7, c = e & 7;
-        const float* n2 = N2 + blk * 64;
-        float s4 = 0.f, sx = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            s4 = fmaf(n2[r * 8 + m], n2[m * 8 + c], s4);
-            sx = fmaf(Nb(blk, r, m), n2[m * 8 + c], sx);  // N N^2
+        for (int k = 0; k < 4; ++k) {
+            const int jr = 4 * g + k;  // column of the row segment
+            const int ia = 4 * g + k;  // row of the accumulator slice
+            const bool in_row = jr < lr && (jr >> 3) == (lr >> 3);
+            const bool in_acc = lr < ia && (lr >> 3) == (ia >> 3);
+            lorow[k] = (lr >= 8 && jr < 8) ? nrow[k] : 0.f;
+            nrow[k] = in_row ? nrow[k] : 0.f;
+            nacc[k] = in_acc ? nacc[k] : 0.f;
         }
-        N4[e] = s4;
-        // X = (I - N)(I + N^2) = I - N + N^2 - N N^2
-        X[e] = (r == c ? 1.f : 0.f) - Nb(blk, r, c) + n2[r * 8 + c] - sx;
+        const tri_f4 n2 = mm(zero, nrow, nacc);   // N^2
+        const tri_f4 nn2 = mm(zero, nrow, n2);    // N N^2
+        st_acc(S, 20, lr, g, n2);
+        tri::wave_sync();
+        const tri_f4 n4 = mm(zero, ld_row(S, 20, lr, g), n2);  // N^4
+        tri_f4 x;                                               // (I - N)(I + N^2)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = (4 * g + k == lr ? 1.f : 0.f) - nacc[k] + n2[k] - nn2[k];
+        tri::wave_sync();
+        st_acc(S, 20, lr, g, x);
+        tri::wave_sync();
+        const tri_f4 d = x + mm(zero, ld_row(S, 20, lr, g), n4);  // D = X (I + N^4)
+        const tri_f4 y = mm(zero, lorow, d);                       // L D
+        tri::wave_sync();
+        st_acc(S, 20, lr, g, d);
+        tri::wave_sync();
+        const tri_f4 z = mm(zero, ld_row(S, 20, lr, g), y);       // D L D
+        st_acc(Mt, ld, lr, g, d - z);
     }
     __syncthreads();
-    float tnew[2];
-#pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-        const int e = tid * 2 + e2, blk = e >> 6, r = (e >> 3) & 7, c = e & 7;
-        const float* x = X + blk * 64;
-        const float* n4 = N4 + blk * 64;
-        float s = x[r * 8 + c];  // X (I + N^4) = X + X N^4
-#pragma unroll
-        for (int m = 0; m < 8; ++m) s = fmaf(x[r * 8 + m], n4[m * 8 + c], s);
-        tnew[e2] = s;
-    }
-    __syncthreads();  // every read of the diagonal blocks of A is done
-#pragma unroll
-    for (int e2 = 0; e2 < 2; ++e2) {
-        const int e = tid * 2 + e2, blk = e >> 6, r = (e >> 3) & 7, c = e & 7;
-        M[(blk * 8 + r) * kTriLd + blk * 8 + c] = tnew[e2];
+    // ---- level 16: blocks b = 0, 1 (rows 32b+16 .., columns 32b ..)
+    for (int b = w; b < 2; b += NW) {
+        float* L21 = M + (32 * b + 16) * ld + 32 * b;
+        const tri_f4 y = mm(zero, ld_row(L21, ld, lr, g), ld_acc(M + 32 * b * ld + 32 * b, ld, lr, g));
+        const tri_f4 z = mm(zero, ld_row(M + (32 * b + 16) * ld + 32 * b + 16, ld, lr, g), y);
+        st_acc(L21, ld, lr, g, -z);
     }
     __syncthreads();
-    // ---- Levels s = 8, 16, 32 (two barriers each, the last one closes the routine).
-    tri_level<8>(M, scratch);
-    tri_level<16>(M, scratch);
-    tri_level<32>(M, scratch);
+    // ---- level 32: Y = L21 T11, then T21 = -T22 Y, by 16x16 output tiles (ta, tb)
+    float* Y = scratch;  // 32 x 36
+    for (int q = w; q < 4; q += NW) {
+        const int ta = q >> 1, tb = q & 1;
+        tri_f4 acc = zero;
+        for (int c = tb; c < 2; ++c)  // T11 is block lower triangular
+            acc = mm(acc, ld_row(M + (32 + 16 * ta) * ld + 16 * c, ld, lr, g),
+                     ld_acc(M + 16 * c * ld + 16 * tb, ld, lr, g));
+        st_acc(Y + 16 * ta * 36 + 16 * tb, 36, lr, g, acc);
+    }
+    __syncthreads();
+    for (int q = w; q < 4; q += NW) {
+        const int ta = q >> 1, tb = q & 1;
+        tri_f4 acc = zero;
+        for (int c = 0; c <= ta; ++c)  // T22 is block lower triangular
+            acc = mm(acc, ld_row(M + (32 + 16 * ta) * ld + 32 + 16 * c, ld, lr, g),
+                     ld_acc(Y + 16 * c * 36 + 16 * tb, 36, lr, g));
+        st_acc(M + (32 + 16 * ta) * ld + 16 * tb, ld, lr, g, -acc);
+    }
+    __syncthreads();
 }
 
 }  // namespace lrc
