@@ -7,11 +7,11 @@
 // followed by h_t = a_t h_0 + b_t for the incoming state.  Every factor is a
 // decay in (0, 1], so the products stay finite.
 //
-// Mapping on CDNA4.  A workgroup (4 waves) owns 64 consecutive state
-// elements of one prompt and walks that prompt's 64-row chunks, keeping the
-// carried state of its elements in registers:
-//  1. The chunk's a and b tiles [64 rows x 64 elements] are read with
-//     row-contiguous 16-byte loads (256 bytes per row, 2 full cache lines)
+// Mapping on CDNA4.  A workgroup (one wave per 16 elements) owns COLS
+// consecutive state elements of one prompt and walks that prompt's 64-row
+// chunks, keeping the carried state of its elements in registers:
+//  1. The chunk's a and b tiles [64 rows x COLS elements] are read with
+//     row-contiguous 16-byte loads (4*COLS bytes per row, whole cache lines)
 //     and written to LDS; the next chunk's loads are issued before this
 //     chunk is scanned, so their latency hides behind the arithmetic.
 //  2. Each wave reads 16 element columns out of LDS with lane t = row t and
@@ -32,10 +32,13 @@
 namespace lrc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTileCols = 64;        // state elements per workgroup
+// State elements per workgroup.  Wider tiles read longer runs of every row
+// (1 KiB at 256 columns), which keeps more DRAM-page locality between the 64
+// rows a chunk touches; 256 measured fastest of 64 / 128 / 256 on the mixed
+// prefill shape.  LDS: 2 x 64 x 257 floats per workgroup.
+constexpr int kScanCols = 256;
+
 constexpr int kColsPerWave = 16;
-constexpr int kLd = kTileCols + 1;   // LDS row stride (floats): column reads hit distinct banks
 
 #define LRC_SCAN_ROUND(CTRL)                                   \
     "v_fmac_f32_dpp %0, %0, %4 " CTRL "\n"                    \
@@ -63,10 +66,14 @@ __device__ __forceinline__ void wave_scan4(float (&a)[4], float (&b)[4]) {
 }
 #undef LRC_SCAN_ROUND
 
-template <bool VEC4>
-__global__ __launch_bounds__(kThreads) void scan_rows_kernel(const float* __restrict__ a, const float* __restrict__ b,
+// COLS state elements per workgroup, one wave per 16 of them.
+template <int COLS, bool VEC4>
+__global__ __launch_bounds__(COLS * 4) void scan_rows_kernel(const float* __restrict__ a, const float* __restrict__ b,
                                                             float* __restrict__ h, const float* h0, float* hS,
                                                             Batch bt, long E) {
+    constexpr int kTileCols = COLS;
+    constexpr int kLd = COLS + 1;  // LDS row stride (floats): column reads hit distinct banks
+    constexpr int kLoadThreadsPerRow = COLS / 4;
     __shared__ float As[kWave * kLd];
     __shared__ float Bs[kWave * kLd];
 
@@ -79,8 +86,8 @@ __global__ __launch_bounds__(kThreads) void scan_rows_kernel(const float* __rest
     const int L = batch_len(bt, p);
 
     // Load-phase mapping: thread -> (row lr + 16 r, 4 columns at lc).
-    const int lr = tid >> 4;
-    const int lc = (tid & 15) * 4;
+    const int lr = tid / kLoadThreadsPerRow;
+    const int lc = (tid % kLoadThreadsPerRow) * 4;
     const bool lcol_ok = tile0 + lc < E;
 
     // Column-phase mapping: this wave's 16 columns start at cw.
@@ -179,14 +186,20 @@ __global__ __launch_bounds__(kThreads) void scan_rows_kernel(const float* __rest
 
 }  // namespace
 
+template <int COLS>
+hipError_t launch_cols(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt, long E,
+                       hipStream_t st) {
+    const dim3 grid((unsigned)((E + COLS - 1) / COLS), (unsigned)bt.P);
+    if (E % 4 == 0)
+        hipLaunchKernelGGL((scan_rows_kernel<COLS, true>), grid, dim3(COLS * 4), 0, st, a, b, h, h0, hS, bt, E);
+    else
+        hipLaunchKernelGGL((scan_rows_kernel<COLS, false>), grid, dim3(COLS * 4), 0, st, a, b, h, h0, hS, bt, E);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt, long E,
                        hipStream_t st) {
-    const dim3 grid((unsigned)((E + kTileCols - 1) / kTileCols), (unsigned)bt.P);
-    if (E % 4 == 0)
-        hipLaunchKernelGGL(scan_rows_kernel<true>, grid, dim3(kThreads), 0, st, a, b, h, h0, hS, bt, E);
-    else
-        hipLaunchKernelGGL(scan_rows_kernel<false>, grid, dim3(kThreads), 0, st, a, b, h, h0, hS, bt, E);
-    return hipGetLastError();
+    return launch_cols<kScanCols>(a, b, h, h0, hS, bt, E, st);
 }
 
 }  // namespace lrc
