@@ -87,8 +87,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mixed_prefill.md")
 
 
 def source_sha(kernel: str) -> str:
+    """Hash of the kernel's HIP source with comments and whitespace removed, so
+    that only a change to the code itself invalidates a stored measurement."""
     path = os.path.join(ROOT, "linear_recurrence_chunked_amd", "csrc", KERNEL_SOURCE[kernel])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def stored_traffic(kernel: str):

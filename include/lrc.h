@@ -44,9 +44,10 @@
 extern "C" {
 #endif
 
-/* Largest chunk: the pages bound a chunk at 64 rows (the static padding of
-   the triangular solve [qwen]; the doubling scan [mamba]; the [S+1, S]
-   exponent tensor [rwkv]).  A chunk call with more rows is rejected. */
+/* Largest chunk.  All three pages cap a chunk at 64 rows: the triangular
+   solve is padded to that size [qwen], the doubling scan stays cheap at it
+   [mamba], and the [S+1, S] exponent tensor grows with its square [rwkv].
+   A chunk call with more rows is rejected. */
 #define LRC_MAX_ROWS 64
 /* Largest number of prompts in one prefill-driver call (prompt offsets
    travel to the device by value, inside the kernel arguments). */
@@ -151,10 +152,10 @@ lrc_status lrc_wkv4_prefill(const float* k, const float* v, const float* w, cons
  *   (I + A) U = diag(beta) V - diag(beta Gamma) K S_0
  *   O   = diag(Gamma) Q S_0 + (e^{gamma_t - gamma_i} q_t.k_i)_{i <= t} U
  *   S_S = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
- * gamma_S is the last cumulative sum.  I + A is inverted on a 64-row
- * padding (padded rows identity): 8x8 diagonal blocks by the Neumann
- * product (I+N)^-1 = (I-N)(I+N^2)(I+N^4), then 2x2 block inversion level by
- * level (16, 32, 64 rows).  Decay factors are formed element by element from
+ * gamma_S is the last cumulative sum.  The inverse of I + A pads the chunk
+ * to 64 rows with identity rows, inverts the eight 8x8 diagonal blocks as
+ * (I+N)^-1 = (I-N)(I+N^2)(I+N^4), and then merges blocks pairwise at
+ * 16, 32 and 64 rows with T21 = -T22 L21 T11.  Decay factors are formed element by element from
  * gamma differences, never as ratios of Gamma.  No scale is applied to q.
  *
  *  q, k        [B, S, Hk, dk]  dtype

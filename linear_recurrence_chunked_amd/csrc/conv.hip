@@ -2,8 +2,9 @@
 //
 // Source: "perf(mamba): prefill text prompts in multi-token chunks" and
 // "perf(qwen3_5): prefill text prompts in multi-token chunks",
-// Implementation -- the conv runs over the previous K-1 conv-state columns
-// plus the chunk's columns, and the new conv state is the last K-1 columns.
+// Implementation -- each output row is a depthwise window over the K-1 rows
+// kept as conv state followed by the chunk's rows; after the chunk, the state
+// keeps the final K-1 rows of that window sequence.
 //
 // Row t's output depends only on rows t-K+1 .. t of the prompt (or of the
 // incoming state before the prompt's first row), so splitting a prompt into

@@ -1,11 +1,12 @@
 // K1: selective scan h_t = a_t h_{t-1} + b_t over rows, FP32, on gfx950.
 //
 // Source: "perf(mamba): prefill text prompts in multi-token chunks",
-// Implementation -- the scan over a chunk of at most 64 rows is a doubling
-// (Hillis-Steele) scan of the pairs (a, b)_t under
-//     (a, b)_t <- (a_t a_{t-k}, a_t b_{t-k} + b_t),  k = 1, 2, 4, ...
-// followed by h_t = a_t h_0 + b_t for the incoming state.  Every factor is a
-// decay in (0, 1], so the products stay finite.
+// Implementation -- within a chunk of at most 64 rows the recurrence is
+// evaluated as a doubling (Hillis-Steele) scan: in round k = 1, 2, 4, ... each
+// row t combines its pair with the pair k rows earlier,
+//     (a, b)_t <- (a_t a_{t-k}, a_t b_{t-k} + b_t),
+// and the carried state enters last, h_t = A_t h_0 + B_t.  The a_t are decay
+// factors no larger than one, so the running products cannot overflow.
 //
 // Mapping on CDNA4.  A workgroup (one wave per 16 elements) owns COLS
 // consecutive state elements of one prompt and walks that prompt's 64-row

@@ -3,9 +3,10 @@
 // waves.
 //
 // Source: "perf(qwen3_5): prefill text prompts in multi-token chunks",
-// Implementation -- I + A is inverted on a fixed 64-row padding (padded rows
-// are identity): 8x8 diagonal blocks by a Neumann product, then 2x2 block
-// inversion level by level, batched over the blocks of each level.
+// Implementation -- the chunk is padded to 64 rows with identity rows; the
+// eight 8x8 diagonal blocks are inverted by a truncated Neumann series, and
+// the result is assembled by merging neighbouring blocks two at a time, all
+// blocks of one size together.
 //
 //  * Diagonal 8x8 blocks: with N the block's strictly lower part, N^8 = 0, so
 //        (I + N)^-1 = (I - N)(I + N^2)(I + N^4).

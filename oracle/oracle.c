@@ -14,10 +14,10 @@
  *
  * Sources (page title, section):
  *  - "perf(mamba): prefill text prompts in multi-token chunks", Implementation:
- *    the depthwise causal short conv over the previous conv-state columns
- *    plus the chunk, and the selective scan h_t = a_t h_{t-1} + b_t.
+ *    the depthwise causal short conv whose window reaches back into a stored
+ *    conv state, and the selective scan h_t = a_t h_{t-1} + b_t.
  *  - "perf(rwkv): prefill text prompts in multi-token chunks", Implementation:
- *    the RWKV-4 one-token WKV step that keeps A and B as (num, den, max).
+ *    the RWKV-4 one-token WKV step, with A and B stored as (num, den, max).
  *  - "perf(qwen3_5): prefill text prompts in multi-token chunks",
  *    Implementation: the chunked Gated DeltaNet delta rule; its one-row case
  *    is the token step below.
@@ -49,9 +49,9 @@ void oracle_set_num_threads(int n) {
 
 /*
  * Depthwise causal convolution over rows ("perf(mamba): ..." and
- * "perf(qwen3_5): ...", Implementation: the conv runs over the previous
- * kernel-1 conv-state columns plus the S chunk columns, and the new conv
- * state is the last kernel-1 columns).
+ * "perf(qwen3_5): ...", Implementation): the window of each row reaches back
+ * into K-1 stored state rows before the chunk, and the state kept for the
+ * next chunk is the final K-1 rows of state-then-chunk.
  *
  * Reading where the page is silent: the window is a causal cross-correlation,
  * tap K-1 multiplies the current row and tap 0 the oldest one; no activation;
@@ -113,8 +113,8 @@ void oracle_scan(const double* a, const double* b, const double* h0, int S, long
  * RWKV-4 WKV, one token at a time ("perf(rwkv): ...", Implementation).
  * The decoder keeps A_t = e^w A_{t-1} + e^{k_t} v_t and
  * B_t = e^w B_{t-1} + e^{k_t} as A = num * e^max, B = den * e^max, and emits
- * wkv_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t}).  Before every
- * exp it subtracts the largest exponent of the terms being combined:
+ * wkv_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t}).  Every exponential
+ * is taken after a shift by the largest exponent among the terms it joins:
  *   output:  p = max(max, u+k_t)
  *   update:  q = max(max + w, k_t),  new max = q.
  * The empty state is (0, 0, -1e38): a finite stand-in for log 0.
@@ -199,7 +199,7 @@ void oracle_gdn(const double* q, const double* k, const double* v, const double*
 
 /*
  * Inverse of a unit lower-triangular matrix I + L ("perf(qwen3_5): ...",
- * Implementation: I + A is unit lower triangular and is inverted).  The
+ * Implementation, where the chunk form needs (I + A)^-1 for strictly lower A).  The
  * oracle uses textbook forward substitution, column by column:
  *   T[i][j] = [i == j] - sum_{j <= m < i} L[i][m] T[m][j].
  * Only the strictly lower part of L is read.

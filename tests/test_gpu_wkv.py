@@ -4,9 +4,9 @@ Workload: 169M-like, 768 x 12 independent channels, 128 rows as 2 x 64, fp32,
 decays w = -exp(U(-6, 2)), bonuses U(-2, 2), keys N(0, 3) with 1% set to
 +-30, incoming (num, den, max) from 32 warm-up steps run by the oracle.
 
-The state triple is defined only up to a common scale ("the same A and B at
-another scale"), so it is compared scale-free: num / den, and num, den
-rescaled to the oracle's max, e^{max - max_oracle}.
+The state triple fixes A and B only up to a common scale factor, so it is
+compared scale-free: num / den, and num, den rescaled to the oracle's max,
+e^{max - max_oracle}.
 """
 import numpy as np
 import pytest

@@ -1,8 +1,8 @@
 """Pins for the oracle's depthwise causal short conv.
 
 Source: "perf(mamba): prefill text prompts in multi-token chunks",
-Implementation (the conv over the previous kernel-1 conv-state columns plus
-the chunk; the new state is the last kernel-1 columns).  The pins: numpy's
+Implementation (a causal depthwise window that reaches back into K-1 stored
+state rows; the next state keeps the final K-1 rows).  The pins: numpy's
 library correlation on the concatenated window, one-hot taps that expose the
 tap order, the state rule for chunks shorter than the window, and chunk-split
 invariance.

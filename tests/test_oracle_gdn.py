@@ -13,7 +13,7 @@ walks one token at a time (the form's one-row case); these tests pin it
   * to the beta = 0 and single-row special cases;
   * to the value-head -> key-head map (consecutive value heads share a key head);
 and pin the forward-substitution inverse to numpy's dense inverse on nearly
-parallel keys with beta near one (the page's own check of its solve).
+parallel keys and beta close to 1, the case the page itself checks its solve on.
 """
 import numpy as np
 import pytest
