@@ -8,113 +8,217 @@
 // exponent before exp; row S, without the bonus, is the outgoing
 // (num, den, max).
 //
-// Mapping on CDNA4: one lane owns one channel of one prompt and walks the
-// prompt's 64-row chunks row by row, so every row's loads and stores are
-// contiguous across the wave (channels innermost).  Because w does not depend
-// on the row, the largest exponent among the state and the rows before row t
-// is always of the form  m + n w : m is the incoming max_0 or the key k_i that
-// last took the lead, and n the number of rows since (t for the state, t-1-i
-// for row i).  The kernel carries (m, n) and forms every exponent directly as
+// Exponent bookkeeping.  Because w does not depend on the row, the largest
+// exponent among the state and the rows before row t is always of the form
+// m + n w: m is the incoming max_0 or the key k_i that last took the lead,
+// and n the number of rows since (t for the state, t-1-i for row i).  A
+// running state carries (m, n) and forms every exponent directly as
 // fma(n, w, m), exactly the page's max_0 + t w and k_i + (t-1-i) w, so no
-// rounding accumulates in the running maximum.  The sums over earlier rows
-// are carried as (num, den) scaled by e^{-(m + n w)}.  Row t's largest
-// exponent is max(m + n w, u + k_t) and exactly one of its two exp factors
-// is 1, so a row costs one exp for the output and one for the state update
-// (against t + 2 for the materialised [S+1, S] form).
+// rounding accumulates in the running maximum; the sums over earlier rows are
+// carried as (num, den) scaled by e^{-(m + n w)}.  Of the two exp factors
+// that line up two such sums, exactly one is 1, so each step costs one exp.
 //
-// Rows are fetched kGroup at a time, one group ahead of the arithmetic, so
-// the HBM latency of the next rows overlaps the current rows' exps.
+// Mapping on CDNA4.  The recurrence is linear in (num, den) with the constant
+// factor e^w per row, so a block of rows reduces, from a zero state, to one
+// state of the same form, and "decay a state by n rows, then add a block" is
+// again one exp.  A workgroup owns 64 channels (one per lane, so every row's
+// loads and stores are one contiguous 256-byte run) of one prompt and walks
+// the prompt's 64-row chunks; its NW waves split each chunk into NW blocks of
+// 64/NW rows.  Per chunk:
+//   1. each wave reduces its block from a zero state: the block's exponents
+//      k_i + (n-1-i) w are independent of each other, so their maximum and
+//      the sums relative to it are plain reductions over the rows held in
+//      registers, not a chain;
+//   2. the block states meet in LDS; wave j folds the carried state and
+//      blocks 0 .. j-1, in row order, into its own start state, and the last
+//      wave folds all of them into the state after the chunk, which it hands
+//      to the next chunk through LDS;
+//   3. each wave replays its rows from its start state and writes the rows'
+//      outputs (the larger of the running maximum and the bonus u + k_t, one
+//      exp and one reciprocal per row).
+// A chunk's sequential work per wave is thus 64/NW rows plus at most NW folds
+// instead of 64 rows, and a prompt keeps NW waves per 64 channels busy.  The
+// next chunk's rows are loaded while the current chunk computes; the row
+// updates are branch-free selects.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
 namespace lrc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kGroup = 16;
+#ifndef LRC_WKV_WAVES
+#define LRC_WKV_WAVES 8
+#endif
+constexpr int kWkvWaves = LRC_WKV_WAVES;
 
 struct WkvState {
     float aa, bb;  // num, den scaled by e^{-(m + n w)}
     float m, n;    // current largest exponent is m + n w
 };
 
-__device__ __forceinline__ void wkv_row(WkvState& s, float wc, float uc, float kt, float vt, float* out) {
-    const float pp = fmaf(s.n, wc, s.m);
-    // output: largest exponent of (state, earlier rows) against the bonus
-    const float eb = uc + kt;
-    const float d = pp - eb;
+// One more row: decay the state by e^w, then add row (k_t, v_t).
+__device__ __forceinline__ void push_row(WkvState& s, float wc, float kt, float vt) {
+    const float n1 = s.n + 1.f;
+    const float d = fmaf(n1, wc, s.m) - kt;
+    const float e = fast_exp(-fabsf(d));
+    const bool lead = d >= 0.f;  // the decayed maximum stays in the lead
+    s.aa = fmaf(e, lead ? vt : s.aa, lead ? s.aa : vt);
+    s.bb = fmaf(e, lead ? 1.f : s.bb, lead ? s.bb : 1.f);
+    s.n = lead ? n1 : 0.f;
+    s.m = lead ? s.m : kt;
+}
+
+// Output of row t from the state before it and the bonus exponent u + k_t.
+__device__ __forceinline__ float out_row(const WkvState& s, float wc, float uc, float kt, float vt) {
+    const float d = fmaf(s.n, wc, s.m) - (uc + kt);
     const float e = fast_exp(-fabsf(d));
     const float fs = d >= 0.f ? 1.f : e;
     const float fb = d >= 0.f ? e : 1.f;
-    const float nt = fmaf(fs, s.aa, fb * vt);
-    const float dt = fmaf(fs, s.bb, fb);
-    *out = nt * __builtin_amdgcn_rcpf(dt);
-    // state: one more decay, then row t with its own exponent
-    const float ed = fmaf(s.n + 1.f, wc, s.m);
-    const float d2 = ed - kt;
-    const float e2 = fast_exp(-fabsf(d2));
-    if (d2 >= 0.f) {  // the decayed maximum stays in the lead
-        s.aa = fmaf(e2, vt, s.aa);
-        s.bb = s.bb + e2;
-        s.n = s.n + 1.f;
-    } else {          // row t's key takes the lead
-        s.aa = fmaf(e2, s.aa, vt);
-        s.bb = fmaf(e2, s.bb, 1.f);
-        s.m = kt;
-        s.n = 0.f;
-    }
+    return fmaf(fs, s.aa, fb * vt) * __builtin_amdgcn_rcpf(fmaf(fs, s.bb, fb));
 }
 
-__global__ __launch_bounds__(kThreads) void wkv4_kernel(const float* __restrict__ k, const float* __restrict__ v,
-                                                       const float* __restrict__ w, const float* __restrict__ u,
-                                                       float* __restrict__ wkv, float* num, float* den, float* mx,
-                                                       Batch bt, int C) {
-    const int c = blockIdx.x * kThreads + threadIdx.x;
-    if (c >= C) return;
+// s <- (s decayed by len rows) + z, where z is a block reduced from a zero state.
+__device__ __forceinline__ void absorb(WkvState& s, const float4& z, float len, float wc) {
+    const float nl = s.n + len;
+    const float d = fmaf(nl, wc, s.m) - fmaf(z.w, wc, z.z);
+    const float e = fast_exp(-fabsf(d));
+    const bool lead = d >= 0.f;
+    s.aa = fmaf(e, lead ? z.x : s.aa, lead ? s.aa : z.x);
+    s.bb = fmaf(e, lead ? z.y : s.bb, lead ? s.bb : z.y);
+    s.n = lead ? nl : z.w;
+    s.m = lead ? s.m : z.z;
+}
+
+// Rows 0 .. nb-1 of a block reduced from a zero state, as (aa, bb, m, n).
+template <int R>
+__device__ __forceinline__ float4 reduce_block(const float (&kb)[R], const float (&vb)[R], int nb, float wc) {
+    float ex[R];
+    float best = fmaf((float)(nb - 1), wc, kb[0]), zm = kb[0], zn = (float)(nb - 1);
+#pragma unroll
+    for (int i = 1; i < R; ++i) {
+        ex[i] = fmaf((float)(nb - 1 - i), wc, kb[i]);
+        const bool gt = i < nb && ex[i] > best;
+        best = gt ? ex[i] : best;
+        zm = gt ? kb[i] : zm;
+        zn = gt ? (float)(nb - 1 - i) : zn;
+    }
+    ex[0] = fmaf((float)(nb - 1), wc, kb[0]);
+    float aa = 0.f, bb = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        if (i < nb) {
+            const float e = fast_exp(ex[i] - best);
+            aa = fmaf(e, vb[i], aa);
+            bb = bb + e;
+        }
+    return make_float4(aa, bb, zm, zn);
+}
+
+template <int NW, bool FULL>
+__global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__ k, const float* __restrict__ v,
+                                                      const float* __restrict__ w, const float* __restrict__ u,
+                                                      float* __restrict__ wkv, float* num, float* den, float* mx,
+                                                      Batch bt, int C) {
+    constexpr int R = 64 / NW;  // rows per wave and chunk
+    __shared__ float4 zs[2][NW][64];  // block states of a chunk
+    __shared__ float4 cs[2][64];      // state after a chunk, from the last wave
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = blockIdx.x * 64 + lane;
+    const bool valid = FULL || c < C;
+    const int cl = valid ? c : C - 1;  // lanes past C compute a copy of the last channel and store nothing
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
-    const long sidx = (long)p * C + c;
-    WkvState s{num[sidx], den[sidx], mx[sidx], 0.f};
-    const float wc = w[c], uc = u[c];
-    const float* kp = k + row0 * C + c;
-    const float* vp = v + row0 * C + c;
-    float* op = wkv + row0 * C + c;
+    const long sidx = (long)p * C + cl;
+    const float wc = w[cl], uc = u[cl];
+    WkvState carry{num[sidx], den[sidx], mx[sidx], 0.f};
+    const float* kp = k + row0 * C + cl;
+    const float* vp = v + row0 * C + cl;
 
-    float k0[kGroup], v0[kGroup], k1[kGroup], v1[kGroup];
-    auto fetch = [&](int t0, float (&kb)[kGroup], float (&vb)[kGroup]) {
+    float k0[R], v0[R], k1[R], v1[R];
+    // Loads are issued unconditionally (rows past the prompt re-read its last
+    // row) so that the compiler can count them and wait only for the chunk
+    // about to be used, not for the one being prefetched.
+    auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R]) {
+        const int r0 = c0 + R * wv;
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
-            if (t0 + i < L) {
-                kb[i] = kp[(long)(t0 + i) * C];
-                vb[i] = vp[(long)(t0 + i) * C];
-            }
+        for (int i = 0; i < R; ++i) {
+            const long r = min(r0 + i, L - 1);
+            kb[i] = kp[r * C];
+            vb[i] = vp[r * C];
+        }
     };
-    auto consume = [&](int t0, const float (&kb)[kGroup], const float (&vb)[kGroup]) {
+    int buf = 0;
+    auto chunk = [&](int c0, const float (&kb)[R], const float (&vb)[R]) {
+        const int S = min(64, L - c0);
+        const int nb = min(R, max(0, S - R * wv));  // rows of this wave's block
+        if (nb > 0) zs[buf][wv][lane] = reduce_block<R>(kb, vb, nb, wc);
+        __syncthreads();
+        if (c0 > 0) {
+            const float4 cc = cs[buf ^ 1][lane];
+            carry = WkvState{cc.x, cc.y, cc.z, cc.w};
+        }
+        // all block states at once (slots of empty blocks hold stale values
+        // that are never folded); opaque registers, so that the folds' selects
+        // stay selects instead of conditional LDS loads
+        float4 zz[NW];
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i)
-            if (t0 + i < L) wkv_row(s, wc, uc, kb[i], vb[i], op + (long)(t0 + i) * C);
+        for (int j = 0; j < NW; ++j) {
+            zz[j] = zs[buf][j][lane];
+            asm volatile("" : "+v"(zz[j].x), "+v"(zz[j].y), "+v"(zz[j].z), "+v"(zz[j].w));
+        }
+        WkvState s = carry;
+        const int jn = min(wv, (S + R - 1) / R);  // non-empty blocks before this wave's
+#pragma unroll
+        for (int j = 0; j < NW - 1; ++j)
+            if (j < jn) absorb(s, zz[j], (float)min(R, S - R * j), wc);
+        if (wv == NW - 1) {
+            WkvState e = s;
+            if (nb > 0) absorb(e, zz[NW - 1], (float)nb, wc);
+            cs[buf][lane] = make_float4(e.aa, e.bb, e.m, e.n);
+            carry = e;
+        }
+        buf ^= 1;
+        if (nb > 0) {
+            float* op = wkv + (row0 + c0 + R * wv) * C + cl;
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                if (i < nb) {
+                    const float o = out_row(s, wc, uc, kb[i], vb[i]);
+                    if (valid) op[(long)i * C] = o;
+                    if (i + 1 < nb) push_row(s, wc, kb[i], vb[i]);
+                }
+        }
     };
 
     if (L > 0) fetch(0, k0, v0);
-    for (int t0 = 0; t0 < L; t0 += 2 * kGroup) {
-        if (t0 + kGroup < L) fetch(t0 + kGroup, k1, v1);
-        consume(t0, k0, v0);
-        if (t0 + kGroup >= L) break;
-        if (t0 + 2 * kGroup < L) fetch(t0 + 2 * kGroup, k0, v0);
-        consume(t0 + kGroup, k1, v1);
+    for (int c0 = 0; c0 < L; c0 += 128) {
+        fetch(c0 + 64, k1, v1);
+        chunk(c0, k0, v0);
+        if (c0 + 64 >= L) break;
+        fetch(c0 + 128, k0, v0);
+        chunk(c0 + 64, k1, v1);
     }
-    num[sidx] = s.aa;
-    den[sidx] = s.bb;
-    mx[sidx] = fmaf(s.n, wc, s.m);
+    // the last wave holds the state after the prompt (or the incoming one)
+    if (wv == NW - 1 && valid) {
+        num[sidx] = carry.aa;
+        den[sidx] = carry.bb;
+        mx[sidx] = fmaf(carry.n, wc, carry.m);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st) {
-    const dim3 grid((unsigned)((C + kThreads - 1) / kThreads), (unsigned)bt.P);
-    hipLaunchKernelGGL(wkv4_kernel, grid, dim3(kThreads), 0, st, k, v, w, u, wkv, num, den, mx, bt, C);
+    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)bt.P);
+    if (C % 64 == 0)
+        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, true>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
+                           den, mx, bt, C);
+    else
+        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, false>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
+                           den, mx, bt, C);
     return hipGetLastError();
 }
 
