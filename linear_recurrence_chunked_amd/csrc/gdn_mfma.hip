@@ -85,18 +85,23 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
     }
 }
 
+// LDS of one workgroup, kept under 80 KiB so that two workgroups share a CU.
+// One buffer holds, in turn, Q (staging .. masked products), T as hi/lo
+// (after the inverse .. U) and K^T (after U .. state update).
 template <int DK, int DVT>
 struct MfmaSmem {
     static constexpr int LDK = DK + 8;
-    static constexpr int LDV = DVT + 8;
     __bf16 K[64 * LDK];
-    __bf16 Q[64 * LDK];
-    __bf16 KT[DK * L64];    // K^T, exact
-    __bf16 V[64 * LDV];
+    union {
+        __bf16 Q[64 * LDK];
+        struct {
+            __bf16 hi[64 * L64];  // (I + A)^-1
+            __bf16 lo[64 * L64];
+        } T;
+        __bf16 KT[DK * L64];     // K^T, exact
+    } u;
     __bf16 P_hi[64 * L64];  // masked decayed Q K^T
     __bf16 P_lo[64 * L64];
-    __bf16 T_hi[64 * L64];  // (I + A)^-1
-    __bf16 T_lo[64 * L64];
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
     float gam[64];
@@ -109,7 +114,7 @@ struct MfmaSmem {
 __constant__ int kPairs[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 template <int DK, int DVT>
-__global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           const float* __restrict__ beta,
@@ -119,13 +124,11 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
     using Sm = MfmaSmem<DK, DVT>;
     constexpr int NW = DVT / 16;           // waves: one per 16 state columns
     constexpr int NT = NW * 64;
-    constexpr int LDK = Sm::LDK, LDV = Sm::LDV;
+    constexpr int LDK = Sm::LDK;
     constexpr int KS = DK / 32;            // k-steps over dk
     constexpr int RT = DK / 16;            // state row tiles
     constexpr int PK = 64 * DK / 8;        // 16-byte pieces of a K (or Q) chunk
-    constexpr int PV = 64 * DVT / 8;
     constexpr int NK = (PK + NT - 1) / NT;
-    constexpr int NV = (PV + NT - 1) / NT;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
@@ -144,16 +147,22 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
     const int L = batch_len(bt, p);
     const long sbase = ((long)p * Hv + h) * DK * dv + c0v + 16 * w;
 
+    // Per-lane address offsets pass through an empty asm wherever they are
+    // used, so that the compiler recomputes addresses (a few adds) instead of
+    // keeping dozens of 64-bit addresses alive across the chunk loop.
+    int s_lane = lq * dv + lr;
+    asm volatile("" : "+v"(s_lane));
     floatx4 sacc[RT];
 #pragma unroll
     for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[tr][r] = S_in[sbase + (long)(16 * tr + lq + r) * dv + lr];
+        for (int r = 0; r < 4; ++r) sacc[tr][r] = S_in[sbase + s_lane + (long)(16 * tr + r) * dv];
     // The masks' tiles above the diagonal stay zero for the whole prompt.
     for (int e = tid; e < 64 * kTriLd; e += NT) sm.M[e] = 0.f;
     for (int e = tid; e < 64 * L64; e += NT) sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
 
-    uint4 pk[NK], pq[NK], pv[NV];
+    uint4 pk[NK], pq[NK];
+    uint32_t pv[8];  // V in accumulator layout, two bf16 a word: rows 16t + 4(l/16) + r, column l%16 of this wave's slice
     float pg = 0.f, pb = 0.f;
     auto fetch = [&](int c0) {
         const int S = min(64, L - c0);
@@ -167,13 +176,21 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
                 pq[x] = *reinterpret_cast<const uint4*>(q + off);
             }
         }
+        const uint16_t* vc = v + (row0 + c0) * Hv * (long)dv + (long)h * dv + c0v + 16 * w;
+        int v_lane = lr;
+        asm volatile("" : "+v"(v_lane));
 #pragma unroll
-        for (int x = 0; x < NV; ++x) {
-            const int e = tid + x * NT, r = e / (DVT / 8), c8 = (e % (DVT / 8)) * 8;
-            pv[x] = make_uint4(0, 0, 0, 0);
-            if (e < PV && r < S)
-                pv[x] = *reinterpret_cast<const uint4*>(v + ((row0 + c0 + r) * Hv + h) * (long)dv + c0v + c8);
-        }
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * t + lq + r;
+                const uint16_t x = vc[(long)min(i, S - 1) * Hv * dv + v_lane];  // rows past the chunk re-read its last row
+                const uint32_t xv = i < S ? uint32_t(x) : 0u;
+                if (r & 1)
+                    pv[2 * t + r / 2] |= xv << 16;
+                else
+                    pv[2 * t + r / 2] = xv;
+            }
         pg = pb = 0.f;
         if (tid < S) {
             pg = g[(row0 + c0 + tid) * Hv + h];
@@ -191,49 +208,18 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
             const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
             if (e < PK) {
                 *reinterpret_cast<uint4*>(&sm.K[r * LDK + c8]) = pk[x];
-                *reinterpret_cast<uint4*>(&sm.Q[r * LDK + c8]) = pq[x];
+                *reinterpret_cast<uint4*>(&sm.u.Q[r * LDK + c8]) = pq[x];
             }
-        }
-#pragma unroll
-        for (int x = 0; x < NV; ++x) {
-            const int e = tid + x * NT, r = e / (DVT / 8), c8 = (e % (DVT / 8)) * 8;
-            if (e < PV) *reinterpret_cast<uint4*>(&sm.V[r * LDV + c8]) = pv[x];
         }
         if (tid < 64) {
             sm.beta[tid] = pb;
-            float x = pg;  // inclusive prefix sum over the wave
-#pragma unroll
-            for (int s = 1; s < 64; s <<= 1) {
-                const float y = __shfl_up(x, s, 64);
-                if (tid >= s) x += y;
-            }
+            const float x = wave_prefix_sum(pg);  // gamma, inclusive over the chunk rows
             sm.gam[tid] = x;
             sm.Gam[tid] = fast_exp(x);
-            const float gS = __shfl(x, S - 1, 64);
+            const float gS = readlane_f(x, S - 1);  // the last cumulative sum
             sm.decS[tid] = tid < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
         }
-        if (c0 + 64 < L) fetch(c0 + 64);
         __syncthreads();
-
-        // ---- shared: K^T by 4-row x 8-column blocks (the inverse's barriers order it before use)
-        for (int b = tid; b < 2 * DK; b += NT) {
-            const int n = b & 15, m = b >> 4;  // rows 4n .. 4n+3, columns 8m .. 8m+7
-            uint4 rw[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) rw[a] = *reinterpret_cast<const uint4*>(&sm.K[(4 * n + a) * LDK + 8 * m]);
-            const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
-            const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
-            const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
-            const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
-                uint2 out;
-                out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
-                out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
-                *reinterpret_cast<uint2*>(&sm.KT[(8 * m + e) * L64 + 4 * n]) = out;
-            }
-        }
 
         // ---- private: K S_0 and Q S_0 for this wave's columns (B from the state accumulators)
         floatx4 ks0[4], qs0[4];
@@ -246,12 +232,13 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const bf16x8 ak = frag_perm(&sm.K[(16 * t + lr) * LDK + 32 * s], lg);
-                const bf16x8 aq = frag_perm(&sm.Q[(16 * t + lr) * LDK + 32 * s], lg);
+                const bf16x8 aq = frag_perm(&sm.u.Q[(16 * t + lr) * LDK + 32 * s], lg);
                 ks0[t] = mfma(ak, bh, ks0[t]);
                 ks0[t] = mfma(ak, bl, ks0[t]);
                 qs0[t] = mfma(aq, bh, qs0[t]);
                 qs0[t] = mfma(aq, bl, qs0[t]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // ---- shared: masked products, transposed (keys as rows) -> A (FP32) and P (hi/lo)
         for (int pr = w; pr < 10; pr += NW) {
@@ -261,21 +248,22 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
             for (int s = 0; s < KS; ++s) {
                 const bf16x8 ak = frag(&sm.K[(16 * tj + lr) * LDK + 32 * s + lk]);
                 kk = mfma(ak, frag(&sm.K[(16 * ti + lr) * LDK + 32 * s + lk]), kk);
-                qk = mfma(ak, frag(&sm.Q[(16 * ti + lr) * LDK + 32 * s + lk]), qk);
+                qk = mfma(ak, frag(&sm.u.Q[(16 * ti + lr) * LDK + 32 * s + lk]), qk);
             }
             const int i = 16 * ti + lr;  // query row of this lane
             const float gi = sm.gam[i];
+            const floatx4 gj = *reinterpret_cast<const floatx4*>(&sm.gam[16 * tj + lq]);
             floatx4 dec;
             if (ti > tj) {
                 const float gc = sm.gam[16 * ti];
                 const float rowf = fast_exp(gi - gc);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - sm.gam[16 * tj + lq + r]);
+                for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - gj[r]);
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 16 * tj + lq + r;
-                    dec[r] = i >= j ? fast_exp(gi - sm.gam[j]) : 0.f;
+                    dec[r] = i >= j ? fast_exp(gi - gj[r]) : 0.f;
                 }
             }
             const float bi = sm.beta[i];
@@ -294,15 +282,19 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
         }
         // ---- private: RHS = diag(beta) V - diag(beta Gamma) K S_0, in registers
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+            const floatx4 b4 = *reinterpret_cast<const floatx4*>(&sm.beta[16 * t + lq]);
+            const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[16 * t + lq]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * t + lq + r;
-                const float bi = sm.beta[i];
-                ks0[t][r] = bi * (static_cast<float>(sm.V[i * LDV + 16 * w + lr]) - sm.Gam[i] * ks0[t][r]);
+                const uint32_t wd = pv[2 * t + r / 2];
+                const float vv = __uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                ks0[t][r] = b4[r] * (vv - G4[r] * ks0[t][r]);
             }
+        }
         // ---- shared: T = (I + A)^-1 in FP32 (barriers inside), then T as hi/lo bf16
         tri_inverse64<NW>(sm.M, sm.scratch);
+        if (c0 + 64 < L) fetch(c0 + 64);  // next chunk's rows, in flight during U, O and the state update
         for (int x = tid; x < 512; x += NT) {
             const int r = x >> 3, c = (x & 7) * 8;
             const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c]);
@@ -310,8 +302,8 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
             bf16x4 ah, al, bh, bl;
             split4(a, ah, al);
             split4(b, bh, bl);
-            *reinterpret_cast<bf16x8*>(&sm.T_hi[r * L64 + c]) = bf16x8{ah[0], ah[1], ah[2], ah[3], bh[0], bh[1], bh[2], bh[3]};
-            *reinterpret_cast<bf16x8*>(&sm.T_lo[r * L64 + c]) = bf16x8{al[0], al[1], al[2], al[3], bl[0], bl[1], bl[2], bl[3]};
+            *reinterpret_cast<bf16x8*>(&sm.u.T.hi[r * L64 + c]) = bf16x8{ah[0], ah[1], ah[2], ah[3], bh[0], bh[1], bh[2], bh[3]};
+            *reinterpret_cast<bf16x8*>(&sm.u.T.lo[r * L64 + c]) = bf16x8{al[0], al[1], al[2], al[3], bl[0], bl[1], bl[2], bl[3]};
         }
         __syncthreads();
 
@@ -325,11 +317,31 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
             acc_frag(ks0[2 * s], ks0[2 * s + 1], bh, bl);
 #pragma unroll
             for (int t = 2 * s; t < 4; ++t) {
-                const bf16x8 ah = frag_perm(&sm.T_hi[(16 * t + lr) * L64 + 32 * s], lg);
-                const bf16x8 al = frag_perm(&sm.T_lo[(16 * t + lr) * L64 + 32 * s], lg);
+                const bf16x8 ah = frag_perm(&sm.u.T.hi[(16 * t + lr) * L64 + 32 * s], lg);
+                const bf16x8 al = frag_perm(&sm.u.T.lo[(16 * t + lr) * L64 + 32 * s], lg);
                 u[t] = mfma(ah, bh, u[t]);
                 u[t] = mfma(ah, bl, u[t]);
                 u[t] = mfma(al, bh, u[t]);
+            }
+        }
+        __syncthreads();  // every wave is done reading T
+        // ---- shared: K^T by 4-row x 8-column blocks, into the buffer T occupied
+        for (int b = tid; b < 2 * DK; b += NT) {
+            const int n = b & 15, m = b >> 4;  // rows 4n .. 4n+3, columns 8m .. 8m+7
+            uint4 rw[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) rw[a] = *reinterpret_cast<const uint4*>(&sm.K[(4 * n + a) * LDK + 8 * m]);
+            const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
+            const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
+            const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
+            const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
+                uint2 out;
+                out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
+                out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
+                *reinterpret_cast<uint2*>(&sm.u.KT[(8 * m + e) * L64 + 4 * n]) = out;
             }
         }
         // ---- private: O = diag(Gamma) Q S_0 + P U for this wave's columns
@@ -350,23 +362,23 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
                     pu[t] = mfma(al, bh, pu[t]);
                 }
             }
+            float* oc = o + (row0 + c0) * Hv * (long)dv + (long)h * dv + c0v + 16 * w;
+            int o_lane = lq * Hv * dv + lr;
+            asm volatile("" : "+v"(o_lane));
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t) {
+                const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[16 * t + lq]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * t + lq + r;
-                    if (i < S)
-                        o[((row0 + c0 + i) * Hv + h) * (long)dv + c0v + 16 * w + lr] =
-                            fmaf(sm.Gam[i], qs0[t][r], pu[t][r]);
-                }
+                for (int r = 0; r < 4; ++r)
+                    if (16 * t + lq + r < S) oc[o_lane + (long)(16 * t + r) * Hv * dv] = fmaf(G4[r], qs0[t][r], pu[t][r]);
+            }
         }
+        __syncthreads();  // K^T complete
         // ---- private: S_S = e^{gamma_S} S_0 + K^T (decS * U), in the state accumulators
         {
             const float GS = sm.Gam[S - 1];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) u[t][r] *= sm.decS[16 * t + lq + r];
+            for (int t = 0; t < 4; ++t) u[t] *= *reinterpret_cast<const floatx4*>(&sm.decS[16 * t + lq]);
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) sacc[tr] = sacc[tr] * GS;
 #pragma unroll
@@ -375,17 +387,19 @@ __global__ __launch_bounds__(DVT * 4) void gdn_mfma_kernel(const uint16_t* __res
                 acc_frag(u[2 * s], u[2 * s + 1], bh, bl);
 #pragma unroll
                 for (int tr = 0; tr < RT; ++tr) {
-                    const bf16x8 a = frag_perm(&sm.KT[(16 * tr + lr) * L64 + 32 * s], lg);
+                    const bf16x8 a = frag_perm(&sm.u.KT[(16 * tr + lr) * L64 + 32 * s], lg);
                     sacc[tr] = mfma(a, bh, sacc[tr]);
                     sacc[tr] = mfma(a, bl, sacc[tr]);
+                    if (tr % 4 == 3) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
     }
+    asm volatile("" : "+v"(s_lane));
 #pragma unroll
     for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S_out[sbase + (long)(16 * tr + lq + r) * dv + lr] = sacc[tr][r];
+        for (int r = 0; r < 4; ++r) S_out[sbase + s_lane + (long)(16 * tr + r) * dv] = sacc[tr][r];
 }
 
 template <int DK, int DVT>

@@ -23,6 +23,18 @@ constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0
 constexpr int kRowBcast15 = 0x142;  // lane 15 of row r feeds every lane of row r + 1
 constexpr int kRowBcast31 = 0x143;  // lane 31 feeds every lane of rows 2 and 3
 
+// Inclusive prefix sum over the 64 lanes of a wave: sums within each 16-lane
+// row by DPP shifts, then carries row totals forward by row broadcasts.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_move<kRowShr1, 0xf>(0.f, x);
+    x += dpp_move<kRowShr2, 0xf>(0.f, x);
+    x += dpp_move<kRowShr4, 0xf>(0.f, x);
+    x += dpp_move<kRowShr8, 0xf>(0.f, x);
+    x += dpp_move<kRowBcast15, 0xa>(0.f, x);
+    x += dpp_move<kRowBcast31, 0xc>(0.f, x);
+    return x;
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
