@@ -51,6 +51,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int L64 = 64 + 8;  // row stride (bf16) of 64-column operands
 
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15;        // fragment row / column within a tile
     const int lg = lane >> 4;        // lane group
     const int lk = lg * 8;           // contiguous fragment k offset
@@ -162,7 +163,8 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
     for (int e = tid; e < 64 * L64; e += NT) sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
 
     uint4 pk[NK], pq[NK];
-    uint32_t pv[8];  // V in accumulator layout, two bf16 a word: rows 16t + 4(l/16) + r, column l%16 of this wave's slice
+    uint16_t pv[16];  // next chunk's V in accumulator layout: rows 16t + 4(l/16) + r, column l%16 of this wave's slice
+    u16x2 vc2[8];     // this chunk's V, two rows a word
     float pg = 0.f, pb = 0.f;
     auto fetch = [&](int c0) {
         const int S = min(64, L - c0);
@@ -179,18 +181,12 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
         const uint16_t* vc = v + (row0 + c0) * Hv * (long)dv + (long)h * dv + c0v + 16 * w;
         int v_lane = lr;
         asm volatile("" : "+v"(v_lane));
+        // Rows past the chunk re-read its last row and are zeroed where V is
+        // used; the values are packed only at staging, so nothing waits here.
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * t + lq + r;
-                const uint16_t x = vc[(long)min(i, S - 1) * Hv * dv + v_lane];  // rows past the chunk re-read its last row
-                const uint32_t xv = i < S ? uint32_t(x) : 0u;
-                if (r & 1)
-                    pv[2 * t + r / 2] |= xv << 16;
-                else
-                    pv[2 * t + r / 2] = xv;
-            }
+            for (int r = 0; r < 4; ++r) pv[4 * t + r] = vc[(long)min(16 * t + lq + r, S - 1) * Hv * dv + v_lane];
         pg = pb = 0.f;
         if (tid < S) {
             pg = g[(row0 + c0 + tid) * Hv + h];
@@ -201,6 +197,12 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
     if (L > 0) fetch(0);
     for (int c0 = 0; c0 < L; c0 += 64) {
         const int S = min(64, L - c0);
+        // The lane indices pass through an empty asm once per chunk, so that
+        // the LDS addresses derived from them are recomputed here instead of
+        // being held in registers across the whole prompt.
+        int tid_c = tid;
+        asm volatile("" : "+v"(tid_c));
+        const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
         __syncthreads();  // previous chunk done with every LDS buffer
         // ---- stage the prefetched chunk: K, Q, V, beta, gamma, Gamma, decay of the state update
 #pragma unroll
@@ -211,6 +213,8 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
                 *reinterpret_cast<uint4*>(&sm.u.Q[r * LDK + c8]) = pq[x];
             }
         }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) vc2[x] = u16x2{pv[2 * x], pv[2 * x + 1]};
         if (tid < 64) {
             sm.beta[tid] = pb;
             const float x = wave_prefix_sum(pg);  // gamma, inclusive over the chunk rows
@@ -238,47 +242,60 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
                 qs0[t] = mfma(aq, bh, qs0[t]);
                 qs0[t] = mfma(aq, bl, qs0[t]);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         // ---- shared: masked products, transposed (keys as rows) -> A (FP32) and P (hi/lo)
-        for (int pr = w; pr < 10; pr += NW) {
-            const int ti = kPairs[pr][0], tj = kPairs[pr][1];  // query tile, key tile
-            floatx4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
+        {
+            constexpr int PPW = (10 + NW - 1) / NW;  // tile pairs per wave
+            floatx4 kk[PPW], qk[PPW];
+            int ti[PPW], tj[PPW];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 ak = frag(&sm.K[(16 * tj + lr) * LDK + 32 * s + lk]);
-                kk = mfma(ak, frag(&sm.K[(16 * ti + lr) * LDK + 32 * s + lk]), kk);
-                qk = mfma(ak, frag(&sm.u.Q[(16 * ti + lr) * LDK + 32 * s + lk]), qk);
+            for (int q = 0; q < PPW; ++q) {
+                const int pr = min(w + q * NW, 9);
+                ti[q] = kPairs[pr][0];
+                tj[q] = kPairs[pr][1];
+                kk[q] = qk[q] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
-            const int i = 16 * ti + lr;  // query row of this lane
-            const float gi = sm.gam[i];
-            const floatx4 gj = *reinterpret_cast<const floatx4*>(&sm.gam[16 * tj + lq]);
-            floatx4 dec;
-            if (ti > tj) {
-                const float gc = sm.gam[16 * ti];
-                const float rowf = fast_exp(gi - gc);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - gj[r]);
-            } else {
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int q = 0; q < PPW; ++q) {
+                    const bf16x8 ak = frag(&sm.K[(16 * tj[q] + lr) * LDK + 32 * s + lk]);
+                    kk[q] = mfma(ak, frag(&sm.K[(16 * ti[q] + lr) * LDK + 32 * s + lk]), kk[q]);
+                    qk[q] = mfma(ak, frag(&sm.u.Q[(16 * ti[q] + lr) * LDK + 32 * s + lk]), qk[q]);
+                }
+#pragma unroll
+            for (int q = 0; q < PPW; ++q) {
+                if (w + q * NW >= 10) break;
+                const int i = 16 * ti[q] + lr;
+                const float gi = sm.gam[i];
+                const floatx4 gj = *reinterpret_cast<const floatx4*>(&sm.gam[16 * tj[q] + lq]);
+                floatx4 dec;
+                if (ti[q] > tj[q]) {
+                    const float gc = sm.gam[16 * ti[q]];
+                    const float rowf = fast_exp(gi - gc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - gj[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * tj[q] + lq + r;
+                        dec[r] = i >= j ? fast_exp(gi - gj[r]) : 0.f;
+                    }
+                }
+                const float bi = sm.beta[i];
+                floatx4 av, pv4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * tj + lq + r;
-                    dec[r] = i >= j ? fast_exp(gi - gj[r]) : 0.f;
+                    const int j = 16 * tj[q] + lq + r;
+                    av[r] = i > j ? bi * dec[r] * kk[q][r] : 0.f;
+                    pv4[r] = dec[r] * qk[q][r];
                 }
+                *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj[q] + lq]) = av;
+                bf16x4 ph, pl;
+                split4(pv4, ph, pl);
+                *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj[q] + lq]) = ph;
+                *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj[q] + lq]) = pl;
             }
-            const float bi = sm.beta[i];
-            floatx4 av, pv4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * tj + lq + r;
-                av[r] = i > j ? bi * dec[r] * kk[r] : 0.f;
-                pv4[r] = dec[r] * qk[r];
-            }
-            *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
-            bf16x4 ph, pl;
-            split4(pv4, ph, pl);
-            *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj + lq]) = ph;
-            *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj + lq]) = pl;
         }
         // ---- private: RHS = diag(beta) V - diag(beta Gamma) K S_0, in registers
 #pragma unroll
@@ -287,15 +304,17 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
             const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[16 * t + lq]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint32_t wd = pv[2 * t + r / 2];
-                const float vv = __uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                const uint16_t raw = (r & 1) ? vc2[2 * t + r / 2].y : vc2[2 * t + r / 2].x;
+                const float vv = 16 * t + lq + r < S ? bf16_to_f32(raw) : 0.f;
                 ks0[t][r] = b4[r] * (vv - G4[r] * ks0[t][r]);
             }
         }
         // ---- shared: T = (I + A)^-1 in FP32 (barriers inside), then T as hi/lo bf16
         tri_inverse64<NW>(sm.M, sm.scratch);
         if (c0 + 64 < L) fetch(c0 + 64);  // next chunk's rows, in flight during U, O and the state update
-        for (int x = tid; x < 512; x += NT) {
+#pragma unroll
+        for (int xi = 0; xi < 512 / NT; ++xi) {
+            const int x = tid + xi * NT;
             const int r = x >> 3, c = (x & 7) * 8;
             const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c]);
             const floatx4 b = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c + 4]);
@@ -390,7 +409,6 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
                     const bf16x8 a = frag_perm(&sm.u.KT[(16 * tr + lr) * L64 + 32 * s], lg);
                     sacc[tr] = mfma(a, bh, sacc[tr]);
                     sacc[tr] = mfma(a, bl, sacc[tr]);
-                    if (tr % 4 == 3) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }

@@ -78,7 +78,11 @@ __device__ inline void tri_inverse64(float* M, float* scratch) {
     using tri::mm;
     using tri::st_acc;
     constexpr int ld = kTriLd;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // lane index through an empty asm: addresses are formed per call, not
+    // kept in registers by a caller that calls this in a loop
+    int tl = threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const int lane = tl & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, g = lane >> 4;
     const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     __syncthreads();
