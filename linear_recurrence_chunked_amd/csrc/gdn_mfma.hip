@@ -166,19 +166,24 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
     uint16_t pv[16];  // next chunk's V in accumulator layout: rows 16t + 4(l/16) + r, column l%16 of this wave's slice
     u16x2 vc2[8];     // this chunk's V, two rows a word
     float pg = 0.f, pb = 0.f;
+    // Addresses: a 64-bit base per chunk (scalar) plus 32-bit lane offsets
+    // formed with 24-bit multiplies (heads x head size stays below 2^24).
+    const uint32_t rowK = Hk * DK, rowV = Hv * dv;
     auto fetch = [&](int c0) {
         const int S = min(64, L - c0);
+        const uint16_t* kc = k + ((row0 + c0) * Hk + kh) * (long)DK;
+        const uint16_t* qc = q + ((row0 + c0) * Hk + kh) * (long)DK;
 #pragma unroll
         for (int x = 0; x < NK; ++x) {
             const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
             pk[x] = pq[x] = make_uint4(0, 0, 0, 0);
             if (e < PK && r < S) {
-                const long off = ((row0 + c0 + r) * Hk + kh) * DK + c8;
-                pk[x] = *reinterpret_cast<const uint4*>(k + off);
-                pq[x] = *reinterpret_cast<const uint4*>(q + off);
+                const uint32_t off = __umul24(r, rowK) + c8;
+                pk[x] = *reinterpret_cast<const uint4*>(kc + off);
+                pq[x] = *reinterpret_cast<const uint4*>(qc + off);
             }
         }
-        const uint16_t* vc = v + (row0 + c0) * Hv * (long)dv + (long)h * dv + c0v + 16 * w;
+        const uint16_t* vc = v + (row0 + c0) * (long)rowV + (long)h * dv + c0v + 16 * w;
         int v_lane = lr;
         asm volatile("" : "+v"(v_lane));
         // Rows past the chunk re-read its last row and are zeroed where V is
@@ -186,11 +191,12 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pv[4 * t + r] = vc[(long)min(16 * t + lq + r, S - 1) * Hv * dv + v_lane];
+            for (int r = 0; r < 4; ++r) pv[4 * t + r] = vc[__umul24(min(16 * t + lq + r, S - 1), rowV) + v_lane];
         pg = pb = 0.f;
         if (tid < S) {
-            pg = g[(row0 + c0 + tid) * Hv + h];
-            pb = beta[(row0 + c0 + tid) * Hv + h];
+            const long gi = (row0 + c0) * Hv + h + __umul24(tid, Hv);
+            pg = g[gi];
+            pb = beta[gi];
         }
     };
 
@@ -381,15 +387,15 @@ __global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(co
                     pu[t] = mfma(al, bh, pu[t]);
                 }
             }
-            float* oc = o + (row0 + c0) * Hv * (long)dv + (long)h * dv + c0v + 16 * w;
-            int o_lane = lq * Hv * dv + lr;
+            float* oc = o + (row0 + c0) * (long)rowV + (long)h * dv + c0v + 16 * w;
+            uint32_t o_lane = __umul24(lq, rowV) + lr;
             asm volatile("" : "+v"(o_lane));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[16 * t + lq]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (16 * t + lq + r < S) oc[o_lane + (long)(16 * t + r) * Hv * dv] = fmaf(G4[r], qs0[t][r], pu[t][r]);
+                    if (16 * t + lq + r < S) oc[o_lane + (16 * t + r) * rowV] = fmaf(G4[r], qs0[t][r], pu[t][r]);
             }
         }
         __syncthreads();  // K^T complete
