@@ -49,7 +49,11 @@ namespace {
 #ifndef LRC_WKV_WAVES
 #define LRC_WKV_WAVES 8
 #endif
+#ifndef LRC_WKV_DEPTH
+#define LRC_WKV_DEPTH 2
+#endif
 constexpr int kWkvWaves = LRC_WKV_WAVES;
+constexpr int kWkvDepth = LRC_WKV_DEPTH;  // chunks whose rows are in flight ahead of the one computing
 
 struct WkvState {
     float aa, bb;  // num, den scaled by e^{-(m + n w)}
@@ -62,8 +66,9 @@ __device__ __forceinline__ void push_row(WkvState& s, float wc, float kt, float 
     const float d = fmaf(n1, wc, s.m) - kt;
     const float e = fast_exp(-fabsf(d));
     const bool lead = d >= 0.f;  // the decayed maximum stays in the lead
-    s.aa = fmaf(e, lead ? vt : s.aa, lead ? s.aa : vt);
-    s.bb = fmaf(e, lead ? 1.f : s.bb, lead ? s.bb : 1.f);
+    const float fs = lead ? 1.f : e, fb = lead ? e : 1.f;
+    s.aa = fmaf(fs, s.aa, fb * vt);
+    s.bb = fmaf(fs, s.bb, fb);
     s.n = lead ? n1 : 0.f;
     s.m = lead ? s.m : kt;
 }
@@ -114,7 +119,7 @@ __device__ __forceinline__ float4 reduce_block(const float (&kb)[R], const float
     return make_float4(aa, bb, zm, zn);
 }
 
-template <int NW, bool FULL>
+template <int NW, int DEPTH, bool FULL>
 __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__ k, const float* __restrict__ v,
                                                       const float* __restrict__ w, const float* __restrict__ u,
                                                       float* __restrict__ wkv, float* num, float* den, float* mx,
@@ -127,6 +132,12 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
     const int c = blockIdx.x * 64 + lane;
     const bool valid = FULL || c < C;
     const int cl = valid ? c : C - 1;  // lanes past C compute a copy of the last channel and store nothing
+    {   // the longest prompts come first in the grid; their waves get issue priority
+        const int q4 = (4 * blockIdx.y) / gridDim.y;
+        if (q4 == 0) __builtin_amdgcn_s_setprio(3);
+        else if (q4 == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q4 == 2) __builtin_amdgcn_s_setprio(1);
+    }
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
@@ -136,24 +147,31 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
     const float* kp = k + row0 * C + cl;
     const float* vp = v + row0 * C + cl;
 
-    float k0[R], v0[R], k1[R], v1[R];
+    float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R];  // ring of row buffers
     // Loads are issued unconditionally (rows past the prompt re-read its last
     // row) so that the compiler can count them and wait only for the chunk
     // about to be used, not for the one being prefetched.
+    // Row offsets within a chunk are 32-bit (64 rows x C); the base moves per chunk.
     auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R]) {
-        const int r0 = c0 + R * wv;
+        const int r0 = min(c0 + R * wv, L - 1);
+        const float* kc = kp + (long)r0 * C;
+        const float* vc = vp + (long)r0 * C;
+        const int last = L - 1 - r0;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const long r = min(r0 + i, L - 1);
-            kb[i] = kp[r * C];
-            vb[i] = vp[r * C];
+            const int off = min(i, last) * C;
+            kb[i] = kc[off];
+            vb[i] = vc[off];
         }
     };
     int buf = 0;
     auto chunk = [&](int c0, const float (&kb)[R], const float (&vb)[R]) {
         const int S = min(64, L - c0);
         const int nb = min(R, max(0, S - R * wv));  // rows of this wave's block
-        if (nb > 0) zs[buf][wv][lane] = reduce_block<R>(kb, vb, nb, wc);
+        if (nb == R)
+            zs[buf][wv][lane] = reduce_block<R>(kb, vb, R, wc);  // constant row count: no per-row checks
+        else if (nb > 0)
+            zs[buf][wv][lane] = reduce_block<R>(kb, vb, nb, wc);
         __syncthreads();
         if (c0 > 0) {
             const float4 cc = cs[buf ^ 1][lane];
@@ -180,25 +198,37 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
             carry = e;
         }
         buf ^= 1;
-        if (nb > 0) {
-            float* op = wkv + (row0 + c0 + R * wv) * C + cl;
+        float* op = wkv + (row0 + c0 + R * wv) * C + cl;
+        if (nb == R) {  // full block: straight-line code
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float o = out_row(s, wc, uc, kb[i], vb[i]);
+                if (valid) op[i * C] = o;
+                if (i + 1 < R) push_row(s, wc, kb[i], vb[i]);
+            }
+        } else if (nb > 0) {
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 if (i < nb) {
                     const float o = out_row(s, wc, uc, kb[i], vb[i]);
-                    if (valid) op[(long)i * C] = o;
+                    if (valid) op[i * C] = o;
                     if (i + 1 < nb) push_row(s, wc, kb[i], vb[i]);
                 }
         }
     };
 
-    if (L > 0) fetch(0, k0, v0);
-    for (int c0 = 0; c0 < L; c0 += 128) {
-        fetch(c0 + 64, k1, v1);
-        chunk(c0, k0, v0);
-        if (c0 + 64 >= L) break;
-        fetch(c0 + 128, k0, v0);
-        chunk(c0 + 64, k1, v1);
+    if (L > 0) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) fetch(64 * s, kb_[s], vb_[s]);
+    }
+    for (int c0 = 0; c0 < L; c0 += 64 * (DEPTH + 1)) {
+#pragma unroll
+        for (int s = 0; s <= DEPTH; ++s) {
+            const int cc = c0 + 64 * s;
+            if (cc >= L) break;
+            fetch(cc + 64 * DEPTH, kb_[(s + DEPTH) % (DEPTH + 1)], vb_[(s + DEPTH) % (DEPTH + 1)]);
+            chunk(cc, kb_[s], vb_[s]);
+        }
     }
     // the last wave holds the state after the prompt (or the incoming one)
     if (wv == NW - 1 && valid) {
@@ -214,10 +244,10 @@ hipError_t launch_wkv4(const float* k, const float* v, const float* w, const flo
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st) {
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)bt.P);
     if (C % 64 == 0)
-        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, true>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
+        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, kWkvDepth, true>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
                            den, mx, bt, C);
     else
-        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, false>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
+        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, kWkvDepth, false>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
                            den, mx, bt, C);
     return hipGetLastError();
 }
