@@ -80,6 +80,9 @@ def make_workload(dev):
 
 
 KERNELS = ["conv_mamba", "scan", "wkv4", "conv_gdn", "gdn"]
+# Oracle sample for the CPU baseline: every prompt and row; every n-th channel or
+# state element per kernel (every DeltaNet head), about 10 s of float64 work.
+SAMPLE_STRIDE = {"conv_mamba": 2, "scan": 16, "wkv4": 1, "conv_gdn": 2}
 # HIP source of each kernel (its hash ties a stored counter measurement to the code measured)
 KERNEL_SOURCE = {"conv_mamba": "conv.hip", "scan": "scan.hip", "wkv4": "wkv4.hip", "conv_gdn": "conv.hip",
                  "gdn": "gdn_mfma.hip"}
@@ -206,11 +209,11 @@ def cpu_baseline(W, lrc_outputs_fresh, budget_s):
     E = sh["mamba_d_inner"] * sh["mamba_d_state"]
     Hk, Hv = sh["gdn_hk"], sh["gdn_hv"]
     sel = {
-        "conv_mamba": np.arange(0, Cm, 16),
-        "scan": np.arange(0, E, 64),
-        "wkv4": np.arange(0, Cr, 8),
-        "conv_gdn": np.arange(0, Cg, 32),
-        "gdn_keyheads": np.array([0, Hk - 1]),  # key heads 0 and 15 -> value heads 0, 1, 30, 31
+        "conv_mamba": np.arange(0, Cm, SAMPLE_STRIDE["conv_mamba"]),
+        "scan": np.arange(0, E, SAMPLE_STRIDE["scan"]),
+        "wkv4": np.arange(0, Cr, SAMPLE_STRIDE["wkv4"]),
+        "conv_gdn": np.arange(0, Cg, SAMPLE_STRIDE["conv_gdn"]),
+        "gdn_keyheads": np.arange(Hk),  # every key head and its value heads
     }
     f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
     t_kernel, err = {}, {}
@@ -254,7 +257,9 @@ def cpu_baseline(W, lrc_outputs_fresh, budget_s):
     t_kernel["conv_gdn"] = (time.perf_counter() - t0) * Cg / len(c); err["conv_gdn"] = e
     # gated deltanet: two key heads and their value heads
     kh = torch.as_tensor(sel["gdn_keyheads"], device=W["q"].device)
-    vh = torch.as_tensor(np.concatenate([[2 * i, 2 * i + 1] for i in sel["gdn_keyheads"]]), device=W["q"].device)
+    grp = Hv // Hk
+    vh = torch.as_tensor(np.concatenate([np.arange(grp * i, grp * (i + 1)) for i in sel["gdn_keyheads"]]),
+                         device=W["q"].device)
     q = f64(W["q"][:, kh]); kk = f64(W["gk"][:, kh]); vv = f64(W["gv"][:, vh])
     be = f64(W["beta"][:, vh]); gg = f64(W["g"][:, vh]); o = fresh["o"]
     dk, dv = q.shape[2], vv.shape[2]
@@ -270,10 +275,10 @@ def cpu_baseline(W, lrc_outputs_fresh, budget_s):
         ("wkv4", len(sel["wkv4"]) / Cr), ("conv_gdn", len(sel["conv_gdn"]) / Cg), ("gdn", len(vh) / Hv)])
     return {
         "value": R / total, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
-        "sample": (f"all {len(lens)} prompts ({R} rows); every 16th Mamba conv channel, every 64th scan state "
-                   f"element, every 8th RWKV channel, every 32nd DeltaNet conv channel, value heads 0,1,30,31 "
-                   f"of the DeltaNet chunk; {sample_s:.1f} s of oracle time scaled by the sampled fraction "
-                   f"of each kernel"),
+        "sample": (f"all {len(lens)} prompts ({R} rows); every {SAMPLE_STRIDE['conv_mamba']}nd Mamba conv "
+                   f"channel, every {SAMPLE_STRIDE['scan']}th scan state element, every RWKV channel, every "
+                   f"{SAMPLE_STRIDE['conv_gdn']}nd DeltaNet conv channel, every DeltaNet head; {sample_s:.1f} s "
+                   f"of oracle time, each kernel's time scaled by its sampled fraction"),
         "seconds_per_step_estimated": total,
         "per_kernel_s": {n: round(t, 3) for n, t in t_kernel.items()},
     }, err
@@ -291,15 +296,14 @@ def fresh_outputs_sample(lrc, W):
     for k in KERNELS:
         run_kernel(lrc, W, k)
     torch.cuda.synchronize()
-    Hk = sh["gdn_hk"]
-    vh = np.concatenate([[2 * i, 2 * i + 1] for i in (0, Hk - 1)])
     f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    st = SAMPLE_STRIDE
     return {
-        "ym": f64(W["ym"][:, ::16]),
-        "h": f64(W["h"].view(W["R"], E)[:, ::64]),
-        "wkv": f64(W["wkv"][:, ::8]),
-        "yg": f64(W["yg"][:, ::32]),
-        "o": f64(W["o"][:, torch.as_tensor(vh, device=W["o"].device)]),
+        "ym": f64(W["ym"][:, ::st["conv_mamba"]]),
+        "h": f64(W["h"].view(W["R"], E)[:, ::st["scan"]]),
+        "wkv": f64(W["wkv"][:, ::st["wkv4"]]),
+        "yg": f64(W["yg"][:, ::st["conv_gdn"]]),
+        "o": f64(W["o"]),
     }
 
 
@@ -324,7 +328,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernels shard over prompts/channels/heads with no communication; see DESIGN.md).",
+              "(the kernels would shard over prompts, channels and heads with no communication).",
               file=sys.stderr)
         sys.exit(2)
     import torch
