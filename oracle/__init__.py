@@ -54,6 +54,8 @@ def _load():
         lib.oracle_wkv4.argtypes = [P, P, P, P, I, I, P, P, P, P]
         lib.oracle_gdn.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P]
         lib.oracle_unit_lower_inverse.argtypes = [P, I, I, P]
+        lib.oracle_time_shift.argtypes = [P, P, P, I, I, I, P, P]
+        lib.oracle_mamba_mixer.argtypes = [P, P, P, P, P, P, P, I, I, I, P, P]
         lib.oracle_num_threads.restype = I
         lib.oracle_set_num_threads.argtypes = [I]
         _lib = lib
@@ -145,3 +147,34 @@ def unit_lower_inverse(L):
     T = np.empty(L.shape)
     _load().oracle_unit_lower_inverse(_p(L), batch, n, _p(T))
     return T
+
+
+def time_shift(x, state_in, mix):
+    """RWKV-4 time shift.  x [S, C], state_in [C], mix [M, C].
+
+    Returns (out [M, S, C], state_out [C]).
+    """
+    x, state_in, mix = _f64(x), _f64(state_in), _f64(mix)
+    S, C = x.shape
+    M = mix.shape[0]
+    assert state_in.shape == (C,) and mix.shape == (M, C)
+    out = np.empty((M, S, C))
+    st = np.empty(C)
+    _load().oracle_time_shift(_p(x), _p(state_in), _p(mix), S, C, M, _p(out), _p(st))
+    return out, st
+
+
+def mamba_mixer(x, dt, A, B, C, D, h0):
+    """Mamba mixer rows: a = exp(dt A), b = dt B x, h_t = a h_{t-1} + b, y = C.h + D x.
+
+    x, dt [S, Dm]; A [Dm, N]; B, C [S, N]; D [Dm]; h0 [Dm, N].  Returns (y [S, Dm], hS [Dm, N]).
+    """
+    x, dt, A, B, C, D, h0 = map(_f64, (x, dt, A, B, C, D, h0))
+    S, Dm = x.shape
+    N = A.shape[1]
+    assert dt.shape == (S, Dm) and A.shape == (Dm, N) and B.shape == (S, N) and C.shape == (S, N)
+    assert D.shape == (Dm,) and h0.shape == (Dm, N) and N <= 256
+    y = np.empty((S, Dm))
+    hS = np.empty((Dm, N))
+    _load().oracle_mamba_mixer(_p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(h0), S, Dm, N, _p(y), _p(hS))
+    return y, hS

@@ -224,3 +224,77 @@ void oracle_unit_lower_inverse(const double* L, int batch, int n, double* T) {
         }
     }
 }
+
+/*
+ * RWKV-4 time shift ("perf(rwkv): prefill text prompts in multi-token
+ * chunks", Implementation): each mixed input blends row t with row t-1, and
+ * row 0 with the incoming shift state; the shift state kept for the next
+ * chunk is the chunk's last row.
+ *
+ * Reading where the page is silent: the blend is RWKV-4's per-channel mix
+ * mu x_t + (1 - mu) x_{t-1}, with M mixing vectors (one per mixed input:
+ * key, value, receptance, ...) applied to the same rows.
+ *
+ *   xp(t) = state_in[c]  (t = 0),   x[t-1][c]  (t > 0)
+ *   out[j][t][c] = mix[j][c] * x[t][c] + (1 - mix[j][c]) * xp(t)
+ *   state_out[c] = x[S-1][c]  (S > 0),   state_in[c]  (S = 0)
+ *
+ * x: [S][C]; state_in, state_out: [C]; mix: [M][C]; out: [M][S][C].
+ */
+void oracle_time_shift(const double* x, const double* state_in, const double* mix, int S, int C, int M,
+                       double* out, double* state_out) {
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < C; ++c) {
+        double prev = state_in[c];
+        for (int t = 0; t < S; ++t) {
+            const double cur = x[(size_t)t * C + c];
+            for (int j = 0; j < M; ++j) {
+                const double mu = mix[(size_t)j * C + c];
+                out[((size_t)j * S + t) * C + c] = mu * cur + (1.0 - mu) * prev;
+            }
+            prev = cur;
+        }
+        state_out[c] = prev;
+    }
+}
+
+/*
+ * Mamba selective-scan mixer rows with the discretisation and the readout
+ * around the scan ("perf(mamba): prefill text prompts in multi-token
+ * chunks", Implementation: the mixer rows run the scan h_t = a_t h_{t-1} + b_t
+ * between the steps that form a, b and read h out).
+ *
+ * Reading where the page is silent: the selective state-space step of
+ * Mamba -- a zero-order hold on A and an Euler step on B -- with the skip
+ * term D and no output gate:
+ *
+ *   a_t[d][n] = exp(dt[t][d] * A[d][n])
+ *   b_t[d][n] = dt[t][d] * Bm[t][n] * x[t][d]
+ *   h_t[d][n] = a_t[d][n] h_{t-1}[d][n] + b_t[d][n]
+ *   y[t][d]   = sum_n Cm[t][n] h_t[d][n] + Dp[d] x[t][d]
+ *
+ * x, dt: [S][Dm]; A: [Dm][N]; Bm, Cm: [S][N]; Dp: [Dm]; h0, hS: [Dm][N];
+ * y: [S][Dm].  N <= 256.
+ */
+void oracle_mamba_mixer(const double* x, const double* dt, const double* A, const double* Bm,
+                        const double* Cm, const double* Dp, const double* h0, int S, int Dm, int N,
+                        double* y, double* hS) {
+#pragma omp parallel for schedule(static)
+    for (int d = 0; d < Dm; ++d) {
+        double h[256];
+        for (int n = 0; n < N; ++n) h[n] = h0[(size_t)d * N + n];
+        for (int t = 0; t < S; ++t) {
+            const double dtv = dt[(size_t)t * Dm + d];
+            const double xv = x[(size_t)t * Dm + d];
+            double acc = 0.0;
+            for (int n = 0; n < N; ++n) {
+                const double a = exp(dtv * A[(size_t)d * N + n]);
+                const double b = dtv * Bm[(size_t)t * N + n] * xv;
+                h[n] = a * h[n] + b;
+                acc += Cm[(size_t)t * N + n] * h[n];
+            }
+            y[(size_t)t * Dm + d] = acc + Dp[d] * xv;
+        }
+        for (int n = 0; n < N; ++n) hS[(size_t)d * N + n] = h[n];
+    }
+}

@@ -15,6 +15,7 @@ import pytest
 
 import test_oracle_conv as T_conv
 import test_oracle_gdn as T_gdn
+import test_oracle_next as T_next
 import test_oracle_scan as T_scan
 import test_oracle_wkv as T_wkv
 
@@ -50,6 +51,19 @@ MUTATIONS = [
       (T_gdn.test_gdn_exact_recall_with_orthonormal_keys, {})]),
     ("inverse drops a term", "for (int m = j; m < i; ++m)", "for (int m = j + 1; m < i; ++m)",
      [(T_gdn.test_unit_lower_inverse_matches_numpy, dict(n=64, par=(0, 64)))]),
+    ("time shift never advances", "            prev = cur;\n", "",
+     [(T_next.test_time_shift_one_hot_mixes_are_rows_and_shifted_rows, {})]),
+    ("time shift mixes the wrong row", "mu * cur + (1.0 - mu) * prev;", "mu * prev + (1.0 - mu) * cur;",
+     [(T_next.test_time_shift_one_hot_mixes_are_rows_and_shifted_rows, {})]),
+    ("mixer reads h before the update", "                h[n] = a * h[n] + b;\n                acc += Cm[(size_t)t * N + n] * h[n];",
+     "                acc += Cm[(size_t)t * N + n] * h[n];\n                h[n] = a * h[n] + b;",
+     [(T_next.test_mixer_brute_force_product_form, {}), (T_next.test_mixer_agrees_with_the_pinned_scan, {})]),
+    ("mixer decay misses dt", "const double a = exp(dtv * A[(size_t)d * N + n]);", "const double a = exp(A[(size_t)d * N + n]);",
+     [(T_next.test_mixer_constant_decay_geometric_closed_form, {})]),
+    ("mixer drops the skip term", "y[(size_t)t * Dm + d] = acc + Dp[d] * xv;", "y[(size_t)t * Dm + d] = acc;",
+     [(T_next.test_mixer_zero_input_weight_leaves_skip_and_decayed_state, {})]),
+    ("mixer transposed A", "exp(dtv * A[(size_t)d * N + n])", "exp(dtv * A[(size_t)(n % Dm) * N + (d % N)])",
+     [(T_next.test_mixer_brute_force_product_form, {}), (T_next.test_mixer_constant_decay_geometric_closed_form, {})]),
 ]
 
 
