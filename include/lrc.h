@@ -54,6 +54,8 @@ extern "C" {
 #define LRC_MAX_PROMPTS 256
 /* Largest depthwise conv width. */
 #define LRC_MAX_CONV_K 8
+/* Largest number of mixed inputs one time-shift call produces. */
+#define LRC_MAX_MIX 8
 
 typedef enum {
     LRC_OK = 0,
@@ -183,6 +185,51 @@ lrc_status lrc_gdn_prefill(const void* q, const void* k, const void* v, const fl
    padded to 64 rows with identity.  A, T [batch, n, n] float; T must not
    overlap A.  [qwen] */
 lrc_status lrc_unit_lower_inverse(const float* A, float* T, int batch, int n, void* stream);
+
+/* ------------------------------------------------------------------------
+ * RWKV-4 time shift ([rwkv]: each mixed input blends row t with row t-1,
+ * row 0 with the incoming shift state; the next shift state is the chunk's
+ * last row).  For each of M mixing vectors mu_j:
+ *   out[j][t][c] = mu_j[c] x[t][c] + (1 - mu_j[c]) x[t-1][c],  x[-1] = state_in
+ *   state_out    = x[S-1]  (state_in if S = 0)
+ * One pass over x writes all M mixed inputs.
+ *  x          [B, S, C]     float
+ *  out        [M, B, S, C]  float (mixed input j is plane j)
+ *  state_in   [B, C]        float
+ *  state_out  [B, C]        float; may alias state_in
+ *  mix        [M, C]        float
+ *  1 <= M <= LRC_MAX_MIX.  Errors: as for the other chunk calls.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_time_shift_rows(const float* x, float* out, const float* state_in, float* state_out,
+                               const float* mix, int B, int S, int C, int M, void* stream);
+
+/* Time-shift driver: x [R, C] packed rows, out [M, R, C], state [P, C] in place. */
+lrc_status lrc_time_shift_prefill(const float* x, float* out, float* state, const float* mix,
+                                  const int* lens_host, int P, int C, int M, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Mamba mixer rows with the scan's inputs formed and its output read out in
+ * the same kernel ([mamba]: the mixer rows run h_t = a_t h_{t-1} + b_t
+ * between forming a, b and reading h; here those are the selective
+ * state-space step).  a, b and h stay on chip:
+ *   a_t[d][n] = exp(dt[t][d] A[d][n]),   b_t[d][n] = dt[t][d] B[t][n] x[t][d]
+ *   h_t = a_t h_{t-1} + b_t,             y[t][d] = sum_n C[t][n] h_t[d][n] + Dp[d] x[t][d]
+ *  x, dt, y   [B, S, D]  float (dt as given, e.g. after softplus)
+ *  Bm, Cm     [B, S, N]  float
+ *  A          [D, N]     float
+ *  Dp         [D]        float
+ *  h_in       [B, D, N]  float
+ *  h_out      [B, D, N]  float; may alias h_in
+ *  N in {2, 4, 8, 16, 32, 64}.  Errors: as for the other chunk calls.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_mamba_mixer_rows(const float* x, const float* dt, const float* A, const float* Bm,
+                                const float* Cm, const float* Dp, float* y, const float* h_in,
+                                float* h_out, int B, int S, int D, int N, void* stream);
+
+/* Mixer driver: x, dt, y [R, D], Bm, Cm [R, N] packed rows; state [P, D, N] in place. */
+lrc_status lrc_mamba_mixer_prefill(const float* x, const float* dt, const float* A, const float* Bm,
+                                   const float* Cm, const float* Dp, float* y, float* state,
+                                   const int* lens_host, int P, int D, int N, void* stream);
 
 /* ------------------------------------------------------------------------ */
 const char* lrc_status_string(lrc_status s);

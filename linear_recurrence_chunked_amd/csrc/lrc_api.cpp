@@ -180,7 +180,50 @@ lrc_status gdn_common(const void* q, const void* k, const void* v, const float* 
     return LRC_OK;
 }
 
+// ---------------------------------------------------------------- time shift
+lrc_status shift_common(const float* x, float* out, const float* s_in, float* s_out, const float* mix, long rows,
+                        int P, int C, int M) {
+    REQUIRE_PTR_IF(x, rows > 0); REQUIRE_PTR_IF(out, rows > 0); REQUIRE_PTR(mix);
+    REQUIRE_PTR_IF(s_in, P > 0); REQUIRE_PTR_IF(s_out, P > 0);
+    REQUIRE(C >= 1, LRC_ERR_SHAPE, "channels %d < 1", C);
+    REQUIRE(M >= 1 && M <= LRC_MAX_MIX, LRC_ERR_SHAPE, "mixed inputs %d outside [1, %d]", M, LRC_MAX_MIX);
+    REQUIRE((uint64_t)rows * C * M < kMaxElems, LRC_ERR_SHAPE, "tensor too large");
+    REQUIRE_ALIGN(x); REQUIRE_ALIGN(out); REQUIRE_ALIGN(s_in); REQUIRE_ALIGN(s_out); REQUIRE_ALIGN(mix);
+    const uint64_t xb = (uint64_t)rows * C * 4, ob = xb * M, sb = (uint64_t)P * C * 4, mb = (uint64_t)M * C * 4;
+    REQUIRE(!overlap(out, ob, x, xb) && !overlap(out, ob, mix, mb), LRC_ERR_ALIAS, "out overlaps x or mix");
+    REQUIRE(!overlap(out, ob, s_in, sb) && !overlap(out, ob, s_out, sb), LRC_ERR_ALIAS, "out overlaps the state");
+    REQUIRE(!overlap(s_out, sb, x, xb) && !overlap(s_out, sb, mix, mb), LRC_ERR_ALIAS, "state_out overlaps x or mix");
+    REQUIRE(s_in == s_out || !overlap(s_out, sb, s_in, sb), LRC_ERR_ALIAS, "state_out partially overlaps state_in");
+    return LRC_OK;
+}
+
+// ---------------------------------------------------------------- mamba mixer
+lrc_status mixer_common(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                        const float* Dp, float* y, const float* h_in, float* h_out, long rows, int P, int D, int N) {
+    REQUIRE_PTR_IF(x, rows > 0); REQUIRE_PTR_IF(dt, rows > 0); REQUIRE_PTR_IF(Bm, rows > 0);
+    REQUIRE_PTR_IF(Cm, rows > 0); REQUIRE_PTR_IF(y, rows > 0);
+    REQUIRE_PTR(A); REQUIRE_PTR(Dp); REQUIRE_PTR_IF(h_in, P > 0); REQUIRE_PTR_IF(h_out, P > 0);
+    REQUIRE(D >= 1, LRC_ERR_SHAPE, "d_inner %d < 1", D);
+    REQUIRE(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, LRC_ERR_SHAPE,
+            "d_state %d is not 2, 4, 8, 16, 32 or 64", N);
+    REQUIRE((uint64_t)rows * D < kMaxElems && (uint64_t)P * D * N < kMaxElems, LRC_ERR_SHAPE, "tensor too large");
+    REQUIRE_ALIGN(x); REQUIRE_ALIGN(dt); REQUIRE_ALIGN(A); REQUIRE_ALIGN(Bm); REQUIRE_ALIGN(Cm); REQUIRE_ALIGN(Dp);
+    REQUIRE_ALIGN(y); REQUIRE_ALIGN(h_in); REQUIRE_ALIGN(h_out);
+    const uint64_t xb = (uint64_t)rows * D * 4, bb = (uint64_t)rows * N * 4, sb = (uint64_t)P * D * N * 4;
+    const uint64_t ab = (uint64_t)D * N * 4, db = (uint64_t)D * 4;
+    const void* ins[] = {x, dt, Bm, Cm, A, Dp};
+    const uint64_t inb[] = {xb, xb, bb, bb, ab, db};
+    for (int i = 0; i < 6; ++i) {
+        REQUIRE(!overlap(y, xb, ins[i], inb[i]), LRC_ERR_ALIAS, "y overlaps an input");
+        REQUIRE(!overlap(h_out, sb, ins[i], inb[i]), LRC_ERR_ALIAS, "h_out overlaps an input");
+    }
+    REQUIRE(!overlap(y, xb, h_in, sb) && !overlap(y, xb, h_out, sb), LRC_ERR_ALIAS, "y overlaps the state");
+    REQUIRE(h_in == h_out || !overlap(h_out, sb, h_in, sb), LRC_ERR_ALIAS, "h_out partially overlaps h_in");
+    return LRC_OK;
+}
+
 }  // namespace
+
 
 extern "C" {
 
@@ -285,6 +328,56 @@ lrc_status lrc_unit_lower_inverse(const float* A, float* T, int batch, int n, vo
     if (batch == 0 || n == 0) return ok();
     auto st = static_cast<hipStream_t>(stream);
     return check_launch(lrc::launch_unit_lower_inverse(A, T, batch, n, st), st, "unit_lower_inverse");
+}
+
+lrc_status lrc_time_shift_rows(const float* x, float* out, const float* state_in, float* state_out,
+                               const float* mix, int B, int S, int C, int M, void* stream) {
+    lrc::Batch bt;
+    lrc_status s = uniform_batch(B, S, bt);
+    if (s != LRC_OK) return s;
+    if ((s = shift_common(x, out, state_in, state_out, mix, (long)B * S, B, C, M)) != LRC_OK) return s;
+    if (B == 0) return ok();
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_time_shift(x, out, state_in, state_out, mix, bt, C, M, (long)B * S * C, st),
+                        st, "time shift");
+}
+
+lrc_status lrc_time_shift_prefill(const float* x, float* out, float* state, const float* mix, const int* lens_host,
+                                  int P, int C, int M, void* stream) {
+    thread_local lrc::Batch bt;
+    long rows = 0;
+    lrc_status s = packed_batch(lens_host, P, bt, rows);
+    if (s != LRC_OK) return s;
+    if ((s = shift_common(x, out, state, state, mix, rows, P, C, M)) != LRC_OK) return s;
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_time_shift(x, out, state, state, mix, bt, C, M, rows * C, st), st,
+                        "time shift prefill");
+}
+
+lrc_status lrc_mamba_mixer_rows(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                                const float* Dp, float* y, const float* h_in, float* h_out, int B, int S, int D,
+                                int N, void* stream) {
+    lrc::Batch bt;
+    lrc_status s = uniform_batch(B, S, bt);
+    if (s != LRC_OK) return s;
+    if ((s = mixer_common(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, (long)B * S, B, D, N)) != LRC_OK) return s;
+    if (B == 0) return ok();
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_mamba_mixer(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, D, N, st), st,
+                        "mamba mixer");
+}
+
+lrc_status lrc_mamba_mixer_prefill(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                                   const float* Dp, float* y, float* state, const int* lens_host, int P, int D, int N,
+                                   void* stream) {
+    thread_local lrc::Batch bt;
+    long rows = 0;
+    lrc_status s = packed_batch(lens_host, P, bt, rows);
+    if (s != LRC_OK) return s;
+    if ((s = mixer_common(x, dt, A, Bm, Cm, Dp, y, state, state, rows, P, D, N)) != LRC_OK) return s;
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_mamba_mixer(x, dt, A, Bm, Cm, Dp, y, state, state, bt, D, N, st), st,
+                        "mamba mixer prefill");
 }
 
 const char* lrc_status_string(lrc_status s) {

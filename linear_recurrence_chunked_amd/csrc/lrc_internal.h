@@ -46,5 +46,11 @@ hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, con
                                 float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
                                 int dv, hipStream_t st);
 hipError_t launch_unit_lower_inverse(const float* A, float* T, int batch, int n, hipStream_t st);
+// `plane` is the element stride between mixed inputs in `out` (rows x C).
+hipError_t launch_time_shift(const float* x, float* out, const float* state_in, float* state_out, const float* mix,
+                             const Batch& bt, int C, int M, long plane, hipStream_t st);
+hipError_t launch_mamba_mixer(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                              const float* Dp, float* y, const float* h_in, float* h_out, const Batch& bt, int Dm,
+                              int N, hipStream_t st);
 
 }  // namespace lrc

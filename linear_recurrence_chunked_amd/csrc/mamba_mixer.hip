@@ -1,0 +1,196 @@
+// Mamba mixer rows with the discretisation and the readout fused around the
+// selective scan, FP32, on gfx950.
+//
+// Source: "perf(mamba): prefill text prompts in multi-token chunks",
+// Implementation -- the mixer rows run the scan h_t = a_t h_{t-1} + b_t
+// between forming a, b and reading h out.  Here those steps are the
+// selective state-space step of Mamba:
+//   a_t[d][n] = exp(dt[t][d] A[d][n]),  b_t[d][n] = dt[t][d] B[t][n] x[t][d],
+//   h_t = a_t h_{t-1} + b_t,            y[t][d] = sum_n C[t][n] h_t[d][n] + D[d] x[t][d].
+// a, b and h never reach HBM: per row the kernel reads x, dt (per channel)
+// and B, C (per row, shared by all channels) and writes y, instead of
+// reading a, b and writing h for every (d, n).
+//
+// Mapping on CDNA4.  Two lanes own one channel d: lane (d, half) keeps the
+// N/2 states h[d][half*N/2 ..] in registers for the whole prompt and walks
+// the prompt's rows; the two halves of C.h are added across the lane pair
+// with one DPP move.  Each lane's N/2 recurrences are independent, so one
+// row's exps and FMAs overlap.  a = exp(dt A) is the hardware base-2
+// exponential of dt (A log2 e), with A log2 e formed once per lane.
+//   * B and C of a 64-row chunk are staged in LDS by the workgroup (the next
+//     chunk's rows load into registers while the current chunk computes);
+//     every lane of a half reads the same LDS address (a broadcast).
+//   * x and dt move through a register ring of two 16-row groups, loaded one
+//     group ahead; loads past the prompt re-read its last row and those rows
+//     are never computed, so the state stops at the prompt's last row.
+#include "lrc_device.h"
+#include "lrc_internal.h"
+
+namespace lrc {
+namespace {
+
+constexpr int kThreads = 256;          // 128 channels per workgroup
+constexpr int kChunk = 64;             // rows of B and C staged per chunk
+constexpr int kGroup = 16;             // rows of x and dt per register group
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Value of the partner lane (lane ^ 1) within the quad.
+__device__ __forceinline__ float pair_swap(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
+}
+
+template <int NP>
+__global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __restrict__ x,
+                                                              const float* __restrict__ dt,
+                                                              const float* __restrict__ A,
+                                                              const float* __restrict__ Bm,
+                                                              const float* __restrict__ Cm,
+                                                              const float* __restrict__ Dp, float* __restrict__ y,
+                                                              const float* h_in, float* h_out, Batch bt, int Dm) {
+    constexpr int N = 2 * NP;
+    constexpr int PER_ROW = 2 * N;                   // floats of B and C per row
+    constexpr int STAGE = kChunk * PER_ROW;          // floats staged per chunk
+    constexpr int LOADS = (STAGE + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float bc[2][kChunk][PER_ROW];  // [buffer][row][B | C]
+
+    const int tid = threadIdx.x;
+    const int half = tid & 1;
+    const int d = blockIdx.x * (kThreads / 2) + (tid >> 1);
+    const bool valid = d < Dm;
+    const int dl = valid ? d : Dm - 1;  // lanes past Dm compute a copy of the last channel and store nothing
+    const int p = batch_prompt(bt, blockIdx.y);
+    const long row0 = batch_row0(bt, p);
+    const int L = batch_len(bt, p);
+
+    float a2[NP], h[NP];
+    const long sbase = ((long)p * Dm + dl) * N + half * NP;
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+        a2[n] = A[(long)dl * N + half * NP + n] * kLog2e;
+        h[n] = h_in[sbase + n];
+    }
+    const float dd = Dp[dl];
+
+    // B and C rows of a chunk, cooperatively: element e of the stage is row e / PER_ROW,
+    // entry e % PER_ROW (B for the first N, C for the rest).
+    float pre[LOADS];
+    auto fetch_bc = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int e = tid + i * kThreads;
+            const int r = e / PER_ROW, k = e % PER_ROW;
+            const long row = row0 + min(c0 + r, L - 1);
+            pre[i] = e < STAGE ? (k < N ? Bm[row * N + k] : Cm[row * N + k - N]) : 0.f;
+        }
+    };
+    auto stage_bc = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < STAGE) (&bc[buf][0][0])[e] = pre[i];
+        }
+    };
+    float xg[2][kGroup], tg[2][kGroup];
+    auto fetch_x = [&](int g0, float (&xs)[kGroup], float (&ts)[kGroup]) {
+        const float* xp = x + (row0 + min(g0, L - 1)) * Dm + dl;
+        const float* tp = dt + (row0 + min(g0, L - 1)) * Dm + dl;
+        const int last = L - 1 - min(g0, L - 1);
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            const int off = min(i, last) * Dm;
+            xs[i] = xp[off];
+            ts[i] = tp[off];
+        }
+    };
+    // Rows g0 .. g0+n-1 of the prompt; their B, C sit at rows rb .. of LDS buffer buf.
+    auto rows = [&](int g0, int n, int buf, int rb, const float (&xs)[kGroup], const float (&ts)[kGroup]) {
+        float* yp = y + (row0 + g0) * Dm + d;
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+            if (i >= n) break;
+            const float* bcr = &bc[buf][rb + i][0];
+            float bv[NP], cv[NP];
+#pragma unroll
+            for (int n4 = 0; n4 < NP; n4 += (NP >= 4 ? 4 : NP)) {
+                if (NP >= 4) {
+                    const float4 b4 = *reinterpret_cast<const float4*>(bcr + half * NP + n4);
+                    const float4 c4 = *reinterpret_cast<const float4*>(bcr + N + half * NP + n4);
+                    bv[n4] = b4.x; bv[n4 + 1] = b4.y; bv[n4 + 2] = b4.z; bv[n4 + 3] = b4.w;
+                    cv[n4] = c4.x; cv[n4 + 1] = c4.y; cv[n4 + 2] = c4.z; cv[n4 + 3] = c4.w;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < NP; ++q) {
+                        bv[q] = bcr[half * NP + q];
+                        cv[q] = bcr[N + half * NP + q];
+                    }
+                }
+            }
+            const float dtv = ts[i], xv = xs[i];
+            const float dtx = dtv * xv;
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                const float a = __builtin_amdgcn_exp2f(dtv * a2[q]);
+                h[q] = fmaf(a, h[q], dtx * bv[q]);
+                acc = fmaf(cv[q], h[q], acc);
+            }
+            acc += pair_swap(acc);
+            if (half == 0 && valid) yp[(long)i * Dm] = fmaf(dd, xv, acc);
+        }
+    };
+
+    if (L > 0) {
+        fetch_bc(0);
+        fetch_x(0, xg[0], tg[0]);
+    }
+    int buf = 0;
+    for (int c0 = 0; c0 < L; c0 += kChunk) {
+        __syncthreads();  // every wave is done with the buffer about to be written
+        stage_bc(buf);
+        fetch_bc(c0 + kChunk);
+        __syncthreads();
+        const int S = min(kChunk, L - c0);
+#pragma unroll
+        for (int gi = 0; gi < kChunk / kGroup; gi += 2) {
+            const int g0 = c0 + gi * kGroup;
+            if (gi * kGroup >= S) break;
+            fetch_x(g0 + kGroup, xg[1], tg[1]);
+            rows(g0, min(kGroup, S - gi * kGroup), buf, gi * kGroup, xg[0], tg[0]);
+            if ((gi + 1) * kGroup >= S) break;  // only in a prompt's last chunk
+            fetch_x(g0 + 2 * kGroup, xg[0], tg[0]);
+            rows(g0 + kGroup, min(kGroup, S - (gi + 1) * kGroup), buf, (gi + 1) * kGroup, xg[1], tg[1]);
+        }
+        buf ^= 1;
+    }
+#pragma unroll
+    for (int n = 0; n < NP; ++n)
+        if (valid) h_out[sbase + n] = h[n];
+}
+
+template <int NP>
+hipError_t launch_np(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                     const float* Dp, float* y, const float* h_in, float* h_out, const Batch& bt, int Dm,
+                     hipStream_t st) {
+    const dim3 grid((unsigned)((Dm + kThreads / 2 - 1) / (kThreads / 2)), (unsigned)bt.P);
+    hipLaunchKernelGGL(mamba_mixer_kernel<NP>, grid, dim3(kThreads), 0, st, x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt,
+                       Dm);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mamba_mixer(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                              const float* Dp, float* y, const float* h_in, float* h_out, const Batch& bt, int Dm,
+                              int N, hipStream_t st) {
+    switch (N) {
+        case 2: return launch_np<1>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 4: return launch_np<2>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 8: return launch_np<4>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 16: return launch_np<8>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 32: return launch_np<16>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 64: return launch_np<32>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lrc

@@ -76,6 +76,30 @@ def mamba_tiny(seed: int | None = None, rows: int = 75, d_inner: int = 64, d_sta
     }
 
 
+def mamba_mixer_tiny(seed: int | None = None, rows: int = 75, d_inner: int = 64, d_state: int = 16) -> dict:
+    """Inputs of the fused mixer rows, in the Mamba-tiny recipe: dt ~ U(1e-3, 0.1) per (t, d),
+    A = -U(1, 16) per (d, n), B, C ~ N(0,1) per (t, n), x ~ N(0,1) per (t, d), D ~ N(0,1) per d,
+    h0 ~ N(0,1)."""
+    rng = np.random.default_rng(seed_for(6) if seed is None else seed)
+    return {
+        "x": _t(rng.standard_normal((rows, d_inner))),
+        "dt": _t(rng.uniform(1e-3, 0.1, size=(rows, d_inner))),
+        "A": _t(-rng.uniform(1.0, 16.0, size=(d_inner, d_state))),
+        "B": _t(rng.standard_normal((rows, d_state))),
+        "C": _t(rng.standard_normal((rows, d_state))),
+        "D": _t(rng.standard_normal(d_inner)),
+        "h0": _t(rng.standard_normal((d_inner, d_state))),
+    }
+
+
+def rwkv_shift(seed: int | None = None, rows: int = 128, channels: int = 768 * 12, mixes: int = 3) -> dict:
+    """Time-shift inputs at the 169M-like width: x ~ N(0,1) rows, incoming shift state ~ N(0,1),
+    mixing vectors ~ U(0,1) (key, value, receptance)."""
+    rng = np.random.default_rng(seed_for(7) if seed is None else seed)
+    return {"x": _t(rng.standard_normal((rows, channels))), "state": _t(rng.standard_normal(channels)),
+            "mix": _t(rng.uniform(0.0, 1.0, size=(mixes, channels)))}
+
+
 # --------------------------------------------------------------------------
 # RWKV-4 169M-like: hidden 768 x 12 layers as independent channels, 128 rows.
 # --------------------------------------------------------------------------
@@ -250,3 +274,31 @@ def mixed_gdn(lens, device, seed: int | None = None, hk=16, hv=32, dk=128, dv=12
         out["conv_state"] = torch.zeros((P, conv_k - 1, cc), device=device, dtype=dtype)
         out["conv_w"] = torch.randn((cc, conv_k), **f) * 0.5
     return out
+
+
+def mixed_mamba_mixer(lens, device, seed: int | None = None, d_inner=5120, d_state=16) -> dict:
+    """Packed inputs of the fused mixer rows at model width (same recipe as mamba_mixer_tiny,
+    fresh state)."""
+    gen = _gen(device, (seed_for(5) if seed is None else seed) * 8 + 4)
+    R = int(sum(lens))
+    P = len(lens)
+    f = dict(device=device, dtype=torch.float32, generator=gen)
+    return {
+        "x": torch.randn((R, d_inner), **f),
+        "dt": torch.rand((R, d_inner), **f) * (0.1 - 1e-3) + 1e-3,
+        "A": -(torch.rand((d_inner, d_state), **f) * 15.0 + 1.0),
+        "B": torch.randn((R, d_state), **f),
+        "C": torch.randn((R, d_state), **f),
+        "D": torch.randn((d_inner,), **f),
+        "h0": torch.zeros((P, d_inner, d_state), device=device, dtype=torch.float32),
+    }
+
+
+def mixed_time_shift(lens, device, seed: int | None = None, channels=2560, mixes=3) -> dict:
+    """Packed time-shift inputs at the RWKV-4 width of the mixed workload (fresh state)."""
+    gen = _gen(device, (seed_for(5) if seed is None else seed) * 8 + 5)
+    R = int(sum(lens))
+    P = len(lens)
+    f = dict(device=device, dtype=torch.float32, generator=gen)
+    return {"x": torch.randn((R, channels), **f), "mix": torch.rand((mixes, channels), **f),
+            "state": torch.zeros((P, channels), device=device, dtype=torch.float32)}

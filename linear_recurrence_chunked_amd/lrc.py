@@ -27,6 +27,7 @@ lib = ctypes.CDLL(LIB_PATH)
 MAX_ROWS = 64
 MAX_PROMPTS = 256
 MAX_CONV_K = 8
+MAX_MIX = 8
 F32, BF16 = 0, 1
 
 STATUS = {0: "LRC_OK", 1: "LRC_ERR_NULL", 2: "LRC_ERR_ROWS", 3: "LRC_ERR_SHAPE", 4: "LRC_ERR_DTYPE",
@@ -45,6 +46,10 @@ _SIGS = {
     "lrc_gdn_chunk": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P],
     "lrc_gdn_prefill": [_P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _I, _I, _P],
     "lrc_unit_lower_inverse": [_P, _P, _I, _I, _P],
+    "lrc_time_shift_rows": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "lrc_time_shift_prefill": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
+    "lrc_mamba_mixer_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "lrc_mamba_mixer_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _I, _P],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -253,3 +258,72 @@ def unit_lower_inverse(A, T):
     _need(A, torch.float32, (batch, n, n), "A")
     _need(T, torch.float32, (batch, n, n), "T")
     _check(lib.lrc_unit_lower_inverse(_ptr(A), _ptr(T), batch, n, _stream(A)))
+
+
+# ------------------------------------------------------------------ RWKV-4 time shift
+def time_shift_rows(x, out, state_in, state_out, mix):
+    """x [B, S, C] f32; out [M, B, S, C] f32; state_in, state_out [B, C] (may be the same tensor);
+    mix [M, C] f32."""
+    _dev(x, out, state_in, state_out, mix)
+    B, S, C = x.shape
+    M = mix.shape[0]
+    _need(x, torch.float32, x.shape, "x")
+    _need(out, torch.float32, (M, B, S, C), "out")
+    _need(mix, torch.float32, (M, C), "mix")
+    _need(state_in, torch.float32, (B, C), "state_in")
+    _need(state_out, torch.float32, (B, C), "state_out")
+    _check(lib.lrc_time_shift_rows(_ptr(x), _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(mix), B, S, C, M,
+                                   _stream(x)))
+
+
+def time_shift_prefill(x, out, state, mix, lens):
+    """x [R, C] packed rows; out [M, R, C]; state [P, C] updated in place; mix [M, C]."""
+    _dev(x, out, state, mix)
+    R, C = x.shape
+    M = mix.shape[0]
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but x has {R} rows")
+    _need(x, torch.float32, (R, C), "x")
+    _need(out, torch.float32, (M, R, C), "out")
+    _need(mix, torch.float32, (M, C), "mix")
+    _need(state, torch.float32, (P, C), "state")
+    _check(lib.lrc_time_shift_prefill(_ptr(x), _ptr(out), _ptr(state), _ptr(mix), arr, P, C, M, _stream(x)))
+
+
+# ------------------------------------------------------------------ fused Mamba mixer rows
+def mamba_mixer_rows(x, dt, A, Bm, Cm, Dp, y, h_in, h_out):
+    """x, dt, y [B, S, D]; Bm, Cm [B, S, N]; A [D, N]; Dp [D]; h_in, h_out [B, D, N] (may be the
+    same tensor); all f32."""
+    _dev(x, dt, A, Bm, Cm, Dp, y, h_in, h_out)
+    B, S, D = x.shape
+    N = A.shape[1]
+    for t, n in ((x, "x"), (dt, "dt"), (y, "y")):
+        _need(t, torch.float32, (B, S, D), n)
+    for t, n in ((Bm, "Bm"), (Cm, "Cm")):
+        _need(t, torch.float32, (B, S, N), n)
+    _need(A, torch.float32, (D, N), "A")
+    _need(Dp, torch.float32, (D,), "Dp")
+    _need(h_in, torch.float32, (B, D, N), "h_in")
+    _need(h_out, torch.float32, (B, D, N), "h_out")
+    _check(lib.lrc_mamba_mixer_rows(_ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dp), _ptr(y), _ptr(h_in),
+                                    _ptr(h_out), B, S, D, N, _stream(x)))
+
+
+def mamba_mixer_prefill(x, dt, A, Bm, Cm, Dp, y, state, lens):
+    """x, dt, y [R, D]; Bm, Cm [R, N] packed rows; A [D, N]; Dp [D]; state [P, D, N] updated in place."""
+    _dev(x, dt, A, Bm, Cm, Dp, y, state)
+    R, D = x.shape
+    N = A.shape[1]
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but x has {R} rows")
+    for t, n in ((x, "x"), (dt, "dt"), (y, "y")):
+        _need(t, torch.float32, (R, D), n)
+    for t, n in ((Bm, "Bm"), (Cm, "Cm")):
+        _need(t, torch.float32, (R, N), n)
+    _need(A, torch.float32, (D, N), "A")
+    _need(Dp, torch.float32, (D,), "Dp")
+    _need(state, torch.float32, (P, D, N), "state")
+    _check(lib.lrc_mamba_mixer_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dp), _ptr(y),
+                                       _ptr(state), arr, P, D, N, _stream(x)))

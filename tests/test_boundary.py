@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["lrc_conv_rows", "lrc_conv_prefill", "lrc_scan_rows", "lrc_scan_prefill", "lrc_wkv4_rows",
               "lrc_wkv4_prefill", "lrc_gdn_chunk", "lrc_gdn_prefill", "lrc_unit_lower_inverse",
+              "lrc_time_shift_rows", "lrc_time_shift_prefill", "lrc_mamba_mixer_rows", "lrc_mamba_mixer_prefill",
               "lrc_status_string", "lrc_last_error", "lrc_version"]:
         assert n in names
 
@@ -124,6 +125,41 @@ def test_inverse_rejects(L):
     assert _st(L, f(A0, A0, 4, 8, None)) == "LRC_ERR_ALIAS"
     assert _st(L, f(None, A1, 4, 8, None)) == "LRC_ERR_NULL"
     assert _st(L, f(A0, A1, -1, 8, None)) == "LRC_ERR_SHAPE"
+
+
+def test_time_shift_rejects(L):
+    f = L.lib.lrc_time_shift_rows
+    assert _st(L, f(A0, A1, A2, A3, A4, 1, 65, 16, 3, None)) == "LRC_ERR_ROWS"
+    assert _st(L, f(A0, A1, A2, A3, A4, 1, 8, 16, 0, None)) == "LRC_ERR_SHAPE"   # no mixed input
+    assert _st(L, f(A0, A1, A2, A3, A4, 1, 8, 16, 9, None)) == "LRC_ERR_SHAPE"   # more than LRC_MAX_MIX
+    assert _st(L, f(A0, A1, A2, A3, A4, 1, 8, 0, 3, None)) == "LRC_ERR_SHAPE"
+    assert _st(L, f(A0, A0, A2, A3, A4, 1, 8, 16, 3, None)) == "LRC_ERR_ALIAS"   # out over x
+    assert _st(L, f(A0, A1, A2, A2 + 16, A4, 1, 8, 16, 3, None)) == "LRC_ERR_ALIAS"
+    assert _st(L, f(A0, A1, None, A3, A4, 1, 8, 16, 3, None)) == "LRC_ERR_NULL"
+    assert _st(L, f(A0, MIS, A2, A3, A4, 1, 8, 16, 3, None)) == "LRC_ERR_ALIGN"
+    lens = (ctypes.c_int * 2)(70, -1)
+    assert _st(L, L.lib.lrc_time_shift_prefill(A0, A1, A2, A3, lens, 2, 16, 3, None)) == "LRC_ERR_ROWS"
+
+
+def test_mamba_mixer_rejects(L):
+    f = L.lib.lrc_mamba_mixer_rows
+    ok_args = [A0, A1, A2, A3, A4, A5, A6, A7, A7 + 0x4000000]
+    assert _st(L, f(*ok_args, 1, 65, 64, 16, None)) == "LRC_ERR_ROWS"
+    assert _st(L, f(*ok_args, 1, 8, 64, 12, None)) == "LRC_ERR_SHAPE"   # d_state not a supported size
+    assert _st(L, f(*ok_args, 1, 8, 64, 128, None)) == "LRC_ERR_SHAPE"
+    assert _st(L, f(*ok_args, 1, 8, 0, 16, None)) == "LRC_ERR_SHAPE"
+    bad = list(ok_args)
+    bad[6] = A0  # y over x
+    assert _st(L, f(*bad, 1, 8, 64, 16, None)) == "LRC_ERR_ALIAS"
+    bad = list(ok_args)
+    bad[8] = bad[7] + 16  # h_out partly over h_in
+    assert _st(L, f(*bad, 1, 8, 64, 16, None)) == "LRC_ERR_ALIAS"
+    bad = list(ok_args)
+    bad[2] = None  # A
+    assert _st(L, f(*bad, 1, 8, 64, 16, None)) == "LRC_ERR_NULL"
+    lens = (ctypes.c_int * 1)(5)
+    assert _st(L, L.lib.lrc_mamba_mixer_prefill(A0, A1, A2, A3, A4, A5, A6, A7, lens, 0, 64, 16, None)) \
+        == "LRC_ERR_SHAPE"
 
 
 def test_binding_refuses_cpu_tensors(L):
