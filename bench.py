@@ -284,6 +284,62 @@ def cpu_baseline(W, lrc_outputs_fresh, budget_s):
     }, err
 
 
+# ALU peak for the fused mixer rows: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz issue 39.3 T lane-slots/s;
+# one (t, d, n) step costs 4 full-rate VALU slots (dt*A', dt x * B, the state FMA, the readout FMA) plus one
+# exp at a quarter of that rate (4 slots), so 8 slots per step.
+ALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9
+MIXER_SLOTS_PER_STEP = 8
+
+
+def measure_next_rows(lrc, dev, lens, reps=10):
+    """Time the rows beyond the step's hot path -- the RWKV-4 time shift (three mixed inputs at
+    the RWKV width) and the fused Mamba mixer rows (Mamba width) -- on the same prompt lengths,
+    from fresh states, with HIP events on the launch stream."""
+    import torch
+
+    from linear_recurrence_chunked_amd import inputs
+
+    sh = inputs.MIXED_SHAPES
+    R, P = int(sum(lens)), len(lens)
+    m = inputs.mixed_mamba_mixer(lens, dev)
+    t = inputs.mixed_time_shift(lens, dev)
+    Dm, N = sh["mamba_d_inner"], sh["mamba_d_state"]
+    C, M = t["x"].shape[1], t["mix"].shape[0]
+    y = torch.empty_like(m["x"])
+    out = torch.empty((M, R, C), device=dev)
+    runs = {
+        "time_shift": (lambda: lrc.time_shift_prefill(t["x"], out, t["state"], t["mix"], lens),
+                       R * C * 4 * (1 + M) + P * C * 8 + M * C * 4, None),
+        "mamba_mixer": (lambda: lrc.mamba_mixer_prefill(m["x"], m["dt"], m["A"], m["B"], m["C"], m["D"], y,
+                                                        m["h0"], lens),
+                        R * Dm * 12 + R * N * 8 + P * Dm * N * 8 + Dm * N * 4 + Dm * 4, R * Dm * N),
+    }
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, (fn, nbytes, steps) in runs.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        d = {"ms": round(ms, 4), "rows_per_s": R / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
+             "algorithmic_bytes": nbytes}
+        d["hbm_frac"] = d["GBps"] / HBM_PEAK_GBS
+        if steps:
+            rate = steps / (ms * 1e-3)
+            peak = ALU_LANE_SLOTS / MIXER_SLOTS_PER_STEP
+            d.update({"bound": "alu", "state_steps_per_s": rate, "alu_peak_steps_per_s": peak, "alu_frac": rate / peak})
+        else:
+            d["bound"] = "hbm"
+        res[name] = d
+    del m, t, y, out
+    return res
+
+
 def fresh_outputs_sample(lrc, W):
     """Run one step from fresh states and keep host copies of the sampled outputs."""
     import numpy as np
@@ -380,6 +436,9 @@ def main():
             d["TFLOPs"] = work[k]["flops"] / (ms * 1e-3) / 1e12
             d["mfma_bf16_frac"] = d["TFLOPs"] / MFMA_BF16_PEAK_TFS
         kern[k] = d
+    nxt = measure_next_rows(lrc, dev, W["lens"]) if not args.only else None
+    if nxt and "scan" in per_k:
+        nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
     dom = max(kernels, key=lambda k: per_k[k])
     copy_gbps = measure_copy_gbps(dev)
     if dom == "gdn":
@@ -404,6 +463,8 @@ def main():
                    "prompts": len(W["lens"]), "rows": R, "lens": W["lens"], "kernels": kernels},
         "roofline": roof,
         "kernels": kern,
+        # rows beyond the step (not in `value`): the RWKV-4 time shift and the fused Mamba mixer rows
+        "next_rows": nxt,
     }
     if not args.no_cpu_baseline and set(kernels) == set(KERNELS):
         cb, err = cpu_baseline(W, fresh, args.cpu_budget)

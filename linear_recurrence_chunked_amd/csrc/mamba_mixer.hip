@@ -11,15 +11,17 @@
 // and B, C (per row, shared by all channels) and writes y, instead of
 // reading a, b and writing h for every (d, n).
 //
-// Mapping on CDNA4.  Two lanes own one channel d: lane (d, half) keeps the
-// N/2 states h[d][half*N/2 ..] in registers for the whole prompt and walks
-// the prompt's rows; the two halves of C.h are added across the lane pair
-// with one DPP move.  Each lane's N/2 recurrences are independent, so one
+// Mapping on CDNA4.  LPD consecutive lanes (4 for d_state >= 16, else 2) own
+// one channel d: lane (d, part) keeps the N/LPD states h[d][part*N/LPD ..] in
+// registers for the whole prompt and walks the prompt's rows; the parts of
+// C.h are added across the lanes by DPP quad permutes.  More lanes per channel
+// shorten the per-row chain of the longest prompts, whose waves also get
+// issue priority.  Each lane's N/2 recurrences are independent, so one
 // row's exps and FMAs overlap.  a = exp(dt A) is the hardware base-2
 // exponential of dt (A log2 e), with A log2 e formed once per lane.
 //   * B and C of a 64-row chunk are staged in LDS by the workgroup (the next
 //     chunk's rows load into registers while the current chunk computes);
-//     every lane of a half reads the same LDS address (a broadcast).
+//     every lane of a part reads the same LDS address (a broadcast).
 //   * x and dt move through a register ring of two 16-row groups, loaded one
 //     group ahead; loads past the prompt re-read its last row and those rows
 //     are never computed, so the state stops at the prompt's last row.
@@ -29,17 +31,24 @@
 namespace lrc {
 namespace {
 
-constexpr int kThreads = 256;          // 128 channels per workgroup
+#ifndef LRC_MIXER_LANES
+#define LRC_MIXER_LANES 4
+#endif
+constexpr int kThreads = 256;
+constexpr int kLanes = LRC_MIXER_LANES;  // lanes per channel when d_state allows (2 or 4)
 constexpr int kChunk = 64;             // rows of B and C staged per chunk
 constexpr int kGroup = 16;             // rows of x and dt per register group
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Value of the partner lane (lane ^ 1) within the quad.
-__device__ __forceinline__ float pair_swap(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
+// Sum over the LPD lanes (1, 2 or 4 consecutive lanes of a quad) that share a channel.
+template <int LPD>
+__device__ __forceinline__ float lanes_sum(float v) {
+    if (LPD >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
+    if (LPD >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));
+    return v;
 }
 
-template <int NP>
+template <int NP, int LPD>
 __global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __restrict__ x,
                                                               const float* __restrict__ dt,
                                                               const float* __restrict__ A,
@@ -47,26 +56,32 @@ __global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __re
                                                               const float* __restrict__ Cm,
                                                               const float* __restrict__ Dp, float* __restrict__ y,
                                                               const float* h_in, float* h_out, Batch bt, int Dm) {
-    constexpr int N = 2 * NP;
+    constexpr int N = LPD * NP;
     constexpr int PER_ROW = 2 * N;                   // floats of B and C per row
     constexpr int STAGE = kChunk * PER_ROW;          // floats staged per chunk
     constexpr int LOADS = (STAGE + kThreads - 1) / kThreads;
     __shared__ __align__(16) float bc[2][kChunk][PER_ROW];  // [buffer][row][B | C]
 
     const int tid = threadIdx.x;
-    const int half = tid & 1;
-    const int d = blockIdx.x * (kThreads / 2) + (tid >> 1);
+    const int part = tid % LPD;  // which part of the channel's states this lane owns
+    const int d = blockIdx.x * (kThreads / LPD) + tid / LPD;
     const bool valid = d < Dm;
     const int dl = valid ? d : Dm - 1;  // lanes past Dm compute a copy of the last channel and store nothing
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
+    {   // the longest prompts come first in the grid; their waves get issue priority
+        const int q4 = (4 * blockIdx.y) / gridDim.y;
+        if (q4 == 0) __builtin_amdgcn_s_setprio(3);
+        else if (q4 == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q4 == 2) __builtin_amdgcn_s_setprio(1);
+    }
 
     float a2[NP], h[NP];
-    const long sbase = ((long)p * Dm + dl) * N + half * NP;
+    const long sbase = ((long)p * Dm + dl) * N + part * NP;
 #pragma unroll
     for (int n = 0; n < NP; ++n) {
-        a2[n] = A[(long)dl * N + half * NP + n] * kLog2e;
+        a2[n] = A[(long)dl * N + part * NP + n] * kLog2e;
         h[n] = h_in[sbase + n];
     }
     const float dd = Dp[dl];
@@ -113,15 +128,15 @@ __global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __re
 #pragma unroll
             for (int n4 = 0; n4 < NP; n4 += (NP >= 4 ? 4 : NP)) {
                 if (NP >= 4) {
-                    const float4 b4 = *reinterpret_cast<const float4*>(bcr + half * NP + n4);
-                    const float4 c4 = *reinterpret_cast<const float4*>(bcr + N + half * NP + n4);
+                    const float4 b4 = *reinterpret_cast<const float4*>(bcr + part * NP + n4);
+                    const float4 c4 = *reinterpret_cast<const float4*>(bcr + N + part * NP + n4);
                     bv[n4] = b4.x; bv[n4 + 1] = b4.y; bv[n4 + 2] = b4.z; bv[n4 + 3] = b4.w;
                     cv[n4] = c4.x; cv[n4 + 1] = c4.y; cv[n4 + 2] = c4.z; cv[n4 + 3] = c4.w;
                 } else {
 #pragma unroll
                     for (int q = 0; q < NP; ++q) {
-                        bv[q] = bcr[half * NP + q];
-                        cv[q] = bcr[N + half * NP + q];
+                        bv[q] = bcr[part * NP + q];
+                        cv[q] = bcr[N + part * NP + q];
                     }
                 }
             }
@@ -134,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __re
                 h[q] = fmaf(a, h[q], dtx * bv[q]);
                 acc = fmaf(cv[q], h[q], acc);
             }
-            acc += pair_swap(acc);
-            if (half == 0 && valid) yp[(long)i * Dm] = fmaf(dd, xv, acc);
+            acc = lanes_sum<LPD>(acc);
+            if (part == 0 && valid) yp[(long)i * Dm] = fmaf(dd, xv, acc);
         }
     };
 
@@ -167,13 +182,15 @@ __global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __re
         if (valid) h_out[sbase + n] = h[n];
 }
 
-template <int NP>
+template <int N>
 hipError_t launch_np(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
                      const float* Dp, float* y, const float* h_in, float* h_out, const Batch& bt, int Dm,
                      hipStream_t st) {
-    const dim3 grid((unsigned)((Dm + kThreads / 2 - 1) / (kThreads / 2)), (unsigned)bt.P);
-    hipLaunchKernelGGL(mamba_mixer_kernel<NP>, grid, dim3(kThreads), 0, st, x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt,
-                       Dm);
+    constexpr int LPD = N >= 16 ? kLanes : 2;
+    const int per = kThreads / LPD;
+    const dim3 grid((unsigned)((Dm + per - 1) / per), (unsigned)bt.P);
+    hipLaunchKernelGGL((mamba_mixer_kernel<N / LPD, LPD>), grid, dim3(kThreads), 0, st, x, dt, A, Bm, Cm, Dp, y,
+                       h_in, h_out, bt, Dm);
     return hipGetLastError();
 }
 
@@ -183,12 +200,12 @@ hipError_t launch_mamba_mixer(const float* x, const float* dt, const float* A, c
                               const float* Dp, float* y, const float* h_in, float* h_out, const Batch& bt, int Dm,
                               int N, hipStream_t st) {
     switch (N) {
-        case 2: return launch_np<1>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
-        case 4: return launch_np<2>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
-        case 8: return launch_np<4>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
-        case 16: return launch_np<8>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
-        case 32: return launch_np<16>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
-        case 64: return launch_np<32>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 2: return launch_np<2>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 4: return launch_np<4>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 8: return launch_np<8>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 16: return launch_np<16>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 32: return launch_np<32>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
+        case 64: return launch_np<64>(x, dt, A, Bm, Cm, Dp, y, h_in, h_out, bt, Dm, st);
     }
     return hipErrorInvalidValue;
 }

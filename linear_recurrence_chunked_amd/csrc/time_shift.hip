@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;
+constexpr int kUnroll = 8;
 
 template <int VEC>
 __device__ __forceinline__ void ld(const float* p, int nc, float* v) {
@@ -79,10 +80,7 @@ __global__ __launch_bounds__(kThreads) void time_shift_kernel(const float* __res
         else
             ld<VEC>(x + (row0 + t0 - 1) * C + c0, nc, prev);
         const int n = min(kTile, L - t0);
-        for (int i = 0; i < n; ++i) {
-            const long r = row0 + t0 + i;
-            float cur[VEC];
-            ld<VEC>(x + r * C + c0, nc, cur);
+        auto emit = [&](long r, const float* cur) {
 #pragma unroll
             for (int j = 0; j < LRC_MAX_MIX; ++j) {
                 if (j >= M) break;
@@ -93,6 +91,20 @@ __global__ __launch_bounds__(kThreads) void time_shift_kernel(const float* __res
             }
 #pragma unroll
             for (int e = 0; e < VEC; ++e) prev[e] = cur[e];
+        };
+        int i = 0;
+        // groups of kUnroll rows: all loads first, so they are in flight together
+        for (; i + kUnroll <= n; i += kUnroll) {
+            float cur[kUnroll][VEC];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) ld<VEC>(x + (row0 + t0 + i + u) * C + c0, nc, cur[u]);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) emit(row0 + t0 + i + u, cur[u]);
+        }
+        for (; i < n; ++i) {
+            float cur[VEC];
+            ld<VEC>(x + (row0 + t0 + i) * C + c0, nc, cur);
+            emit(row0 + t0 + i, cur);
         }
         if (tile == 0) {
             float ns[VEC];
