@@ -10,8 +10,9 @@
 //   S_S  = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
 // gamma_S is the last entry of the same cumulative sum.
 //
-// Work split.  A workgroup owns a DVT-wide slice (DVT = min(dv, 64)) of one
-// value head of one prompt and walks the prompt's chunks; it has DVT/16 waves
+// Work split.  A workgroup owns a DVT-wide slice (the whole head for dv = 128,
+// else min(dv, 64)) of one value head of one prompt and walks the prompt's
+// chunks; it has DVT/16 waves
 // and wave w owns state columns 16w .. 16w+15 of the slice.  A wave's [dk x 16] state slice, and its columns of RHS, U
 // and Q S_0, stay in MFMA accumulators in registers for the whole prompt.
 // Only operands every wave needs sit in LDS: the chunk's K, Q, V, K^T, the
@@ -115,7 +116,7 @@ struct MfmaSmem {
 __constant__ int kPairs[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 template <int DK, int DVT>
-__global__ __launch_bounds__(DVT * 4, DVT == 64 ? 2 : 1) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(DVT * 4, DVT >= 64 ? 2 : 1) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           const float* __restrict__ beta,
@@ -463,6 +464,7 @@ hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, con
                                 float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
                                 int dv, hipStream_t st) {
     if (dv == 32) return launch_dk<32>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    if (dv == 128) return launch_dk<128>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
     return launch_dk<64>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
 }
 
