@@ -14,8 +14,10 @@
 // Mapping on CDNA4: a thread owns VEC adjacent channels (16 bytes: 4 fp32 or
 // 8 bf16) of a tile of kTile rows; consecutive threads own consecutive
 // channels, so every row of a tile is one contiguous 16-byte-per-lane access.
-// The K-1 halo rows above a tile are re-read from L2.  Taps and accumulation
-// are FP32 in tap order 0 .. K-1; bf16 outputs round to nearest even.  The
+// The K-1 halo rows above a tile are re-read from L2.  Rows are loaded in
+// groups of 8 before they are computed, so their loads are in flight
+// together.  Taps and accumulation are FP32 in tap order 0 .. K-1; bf16
+// outputs round to nearest even (the hardware conversion).  The
 // tile-0 thread of each (prompt, channel group) is the only reader of the
 // incoming state for those channels; it loads the new state's rows before it
 // writes them, so the state may be updated in place.
@@ -27,6 +29,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;
+constexpr int kUnroll = 8;
 
 template <typename T>
 struct Io;
@@ -57,14 +60,16 @@ struct Io<uint16_t> {
             out[2 * i + 1] = __uint_as_float(wds[i] & 0xffff0000u);
         }
     }
+    // Round to nearest even with the hardware conversion (two values per instruction).
     __device__ static void store(uint16_t* p, const float* in) {
-        uint32_t wds[4];
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        bf16x8 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wds[i] = uint32_t(f32_to_bf16(in[2 * i])) | (uint32_t(f32_to_bf16(in[2 * i + 1])) << 16);
-        *reinterpret_cast<uint4*>(p) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        for (int i = 0; i < 8; ++i) v[i] = static_cast<__bf16>(in[i]);
+        *reinterpret_cast<bf16x8*>(p) = v;
     }
     __device__ static float one(const uint16_t* p) { return bf16_to_f32(*p); }
-    __device__ static void put(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+    __device__ static void put(uint16_t* p, float x) { *reinterpret_cast<__bf16*>(p) = static_cast<__bf16>(x); }
 };
 
 // Loads VEC channels (or fewer at the ragged channel tail) of one row.
@@ -130,9 +135,7 @@ __global__ __launch_bounds__(kThreads) void conv_rows_kernel(const T* __restrict
                 load_row<T, VEC, FULL>(x + (row0 + t) * C + c0, nc, win[r]);
         }
         const int n = min(kTile, L - t0);
-        for (int i = 0; i < n; ++i) {
-            float cur[VEC];
-            load_row<T, VEC, FULL>(x + (row0 + t0 + i) * C + c0, nc, cur);
+        auto emit = [&](int i, const float* cur) {
             float out[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -151,6 +154,20 @@ __global__ __launch_bounds__(kThreads) void conv_rows_kernel(const T* __restrict
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) win[H - 1][e] = cur[e];
             }
+        };
+        int i = 0;
+        // groups of kUnroll rows: all loads first, so they are in flight together
+        for (; i + kUnroll <= n; i += kUnroll) {
+            float cur[kUnroll][VEC];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) load_row<T, VEC, FULL>(x + (row0 + t0 + i + u) * C + c0, nc, cur[u]);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) emit(i + u, cur[u]);
+        }
+        for (; i < n; ++i) {
+            float cur[VEC];
+            load_row<T, VEC, FULL>(x + (row0 + t0 + i) * C + c0, nc, cur);
+            emit(i, cur);
         }
         if (tile == 0 && H > 0) {
             // New state: rows L .. L+H-1 of the state-extended sequence.
