@@ -12,14 +12,14 @@
 //
 // Work split.  A workgroup owns a DVT-wide slice (the whole head for dv = 128,
 // else min(dv, 64)) of one value head of one prompt and walks the prompt's
-// chunks; it has DVT/16 waves
-// and wave w owns state columns 16w .. 16w+15 of the slice.  A wave's [dk x 16] state slice, and its columns of RHS, U
-// and Q S_0, stay in MFMA accumulators in registers for the whole prompt.
-// Only operands every wave needs sit in LDS: the chunk's K, Q, V, K^T, the
-// FP32 matrix A -> T for the inverse, T and P.  The waves share the
-// per-chunk work that does not depend on the column (the masked products,
-// the inverse, K^T); after the inverse no barrier is needed until the next
-// chunk.
+// chunks; it has DVT/16 waves and wave w owns state columns 16w .. 16w+15 of
+// the slice.  A wave's [dk x 16] state slice, and its columns of V, RHS, U and
+// Q S_0, stay in registers (MFMA accumulator layout) for the whole prompt.
+// Only operands every wave needs sit in LDS: the chunk's K and Q, K^T, the
+// FP32 matrix A -> T of the inverse, T and P as hi/lo bf16, and the per-row
+// gamma, Gamma, beta and state-update decay.  The waves share the per-chunk
+// work that does not depend on the column (the masked products, the inverse,
+// K^T).
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
 // of lane l is row l%16 with 8 k-values, the B operand column l%16 with the
@@ -41,7 +41,8 @@
 // e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
 // The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) runs in
 // FP32 on the FP32 matrix cores.  The next chunk's K, Q, V, beta and g are loaded
-// into registers while the current chunk computes.
+// into registers once the inverse is done, while U, O and the state update
+// compute.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 #include "tri_inverse.h"
