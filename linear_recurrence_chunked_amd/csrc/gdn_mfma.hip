@@ -10,16 +10,24 @@
 //   S_S  = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
 // gamma_S is the last entry of the same cumulative sum.
 //
-// Work split.  A workgroup owns a DVT-wide slice (the whole head for dv = 128,
-// else min(dv, 64)) of one value head of one prompt and walks the prompt's
-// chunks; it has DVT/16 waves and wave w owns state columns 16w .. 16w+15 of
-// the slice.  A wave's [dk x 16] state slice, and its columns of V, RHS, U and
-// Q S_0, stay in registers (MFMA accumulator layout) for the whole prompt.
-// Only operands every wave needs sit in LDS: the chunk's K and Q, K^T, the
-// FP32 matrix A -> T of the inverse, T and P as hi/lo bf16, and the per-row
-// gamma, Gamma, beta and state-update decay.  The waves share the per-chunk
-// work that does not depend on the column (the masked products, the inverse,
-// K^T).
+// Work split.  One workgroup owns a whole value head of one prompt and walks
+// its chunks.  It holds two kinds of waves, which run the same sequence of
+// workgroup barriers, five per step (segments A .. E):
+//  * dv/32 state waves, each owning 32 columns of the [dk x dv] state in MFMA
+//    accumulators for the whole prompt.  In step n they run the chain that
+//    depends on the state for chunk n: K S_0, Q S_0 and the right-hand side
+//    (A), U (B), O (C), the state update (D), and they build K^T of chunk n+1
+//    (E).  A lane's two 16-column groups are the even and the odd columns of
+//    the wave's 32, so that V, O and the state move as column pairs.
+//  * 4 prep waves, which in step n prepare chunk n+1, the part that does not
+//    depend on the state: the inverse (diagonal tiles in A, level 16 in B,
+//    level 32 in C and D, each tile of T split to hi/lo bf16 once final) and
+//    the masked decayed Q K^T (D); they stage chunk n+2 into LDS (B) and form
+//    its masked K K^T (E), and keep the rows of chunk n+3 in flight.
+// LDS holds K and Q of two chunks (by chunk parity), the per-row gamma,
+// Gamma, beta and state-update decay of three, and one copy of A -> T (FP32),
+// T and P (hi/lo bf16) and K^T: each is written in a segment where no wave
+// reads the copy it replaces.  About 147 KiB, one workgroup per CU.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
 // of lane l is row l%16 with 8 k-values, the B operand column l%16 with the
@@ -40,9 +48,7 @@
 // per element; below them it is the product e^{gamma_i - gamma_c}
 // e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
 // The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) runs in
-// FP32 on the FP32 matrix cores.  The next chunk's K, Q, V, beta and g are loaded
-// into registers once the inverse is done, while U, O and the state update
-// compute.
+// FP32 on the FP32 matrix cores.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 #include "tri_inverse.h"
@@ -53,32 +59,39 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int L64 = 64 + 8;  // row stride (bf16) of 64-column operands
+constexpr int kPrep = 4;     // waves that prepare the next chunk
+constexpr int CG = 2;        // 16-column groups of a state wave: its even and its odd columns
 
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// Contiguous fragment: 8 k-values from one 16-byte run.
 __device__ __forceinline__ bf16x8 frag(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-// Permuted fragment: k-values {4g..4g+3} and {16+4g..16+4g+3} of a 32-wide k-step.
 __device__ __forceinline__ bf16x8 frag_perm(const __bf16* row_ks, int g) {
     const bf16x4 a = *reinterpret_cast<const bf16x4*>(row_ks + 4 * g);
     const bf16x4 b = *reinterpret_cast<const bf16x4*>(row_ks + 16 + 4 * g);
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two FP32 values as packed bf16 hi = bf16(x) and lo = bf16(x - hi) (round to
+// nearest even both times): one conversion for each pair, the hi parts
+// unpacked with a shift and a mask.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+    const float ra = a - __uint_as_float(hi << 16);
+    const float rb = b - __uint_as_float(hi & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(ra), static_cast<__bf16>(rb)});
+}
 // B fragment from two accumulator tiles (rows 16t.. and 16t+16..): hi and lo parts.
 __device__ __forceinline__ void acc_frag(const floatx4& t0, const floatx4& t1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const __bf16 h0 = static_cast<__bf16>(t0[r]);
-        const __bf16 h1 = static_cast<__bf16>(t1[r]);
-        hi[r] = h0;
-        hi[4 + r] = h1;
-        lo[r] = static_cast<__bf16>(t0[r] - static_cast<float>(h0));
-        lo[4 + r] = static_cast<__bf16>(t1[r] - static_cast<float>(h1));
-    }
+    uint4 h, l;
+    split_pair(t0[0], t0[1], h.x, l.x);
+    split_pair(t0[2], t0[3], h.y, l.y);
+    split_pair(t1[0], t1[1], h.z, l.z);
+    split_pair(t1[2], t1[3], h.w, l.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
@@ -88,351 +101,499 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
     }
 }
 
-// LDS of one workgroup, kept under 80 KiB so that two workgroups share a CU.
-// One buffer holds, in turn, Q (staging .. masked products), T as hi/lo
-// (after the inverse .. U) and K^T (after U .. state update).
-template <int DK, int DVT>
-struct MfmaSmem {
+// Scheduling hint for an unrolled run of N steps that each read R fragments
+// from LDS and issue M products: the reads run AHEAD steps ahead of the
+// products, so that the waits before the products are partial.
+template <int N, int R, int M, int AHEAD>
+__device__ __forceinline__ void read_ahead() {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < N - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M * AHEAD, 0);
+}
+
+template <int DK>
+struct PipeSmem {
     static constexpr int LDK = DK + 8;
-    __bf16 K[64 * LDK];
-    union {
-        __bf16 Q[64 * LDK];
-        struct {
-            __bf16 hi[64 * L64];  // (I + A)^-1
-            __bf16 lo[64 * L64];
-        } T;
-        __bf16 KT[DK * L64];     // K^T, exact
-    } u;
+    __bf16 K[2][64 * LDK];  // chunk rows, by parity of the chunk index
+    __bf16 Q[2][64 * LDK];
+    __bf16 KT[DK * L64];    // K^T of the chunk whose state update comes next
+    __bf16 T_hi[64 * L64];  // (I + A)^-1 as hi/lo bf16
+    __bf16 T_lo[64 * L64];
     __bf16 P_hi[64 * L64];  // masked decayed Q K^T
     __bf16 P_lo[64 * L64];
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
-    float gam[64];
-    float Gam[64];          // e^gamma
-    float beta[64];
-    float decS[64];         // e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
+    float gam[3][64];       // per-row values, by chunk index mod 3
+    float Gam[3][64];       // e^gamma
+    float beta[3][64];
+    float decS[3][64];      // e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
 };
 
-// Lower-triangular 16x16 tile pairs (query tile, key tile) of the 64x64 masks.
-__constant__ int kPairs[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
+// Lower-triangular 16x16 tile pair pr = 0 .. 9 (query tile ti, key tile tj) of
+// the 64x64 masks, row by row: (0,0), (1,0), (1,1), (2,0), ...  Formed with
+// scalar arithmetic: a table in memory would be read with scalar loads, whose
+// waits also wait for every LDS read in flight.
+__device__ __forceinline__ void tile_pair(int pr, int& ti, int& tj) {
+    ti = (pr >= 1) + (pr >= 3) + (pr >= 6);
+    tj = pr - ti * (ti + 1) / 2;
+}
 
-template <int DK, int DVT>
-__global__ __launch_bounds__(DVT * 4, DVT >= 64 ? 2 : 1) void gdn_mfma_kernel(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          const float* __restrict__ beta,
-                                                          const float* __restrict__ g, float* __restrict__ o,
-                                                          const float* S_in, float* S_out, Batch bt, int Hk, int Hv,
-                                                          int dv) {
-    using Sm = MfmaSmem<DK, DVT>;
-    constexpr int NW = DVT / 16;           // waves: one per 16 state columns
-    constexpr int NT = NW * 64;
+// Decays e^{gamma_i - gamma_j} for query i = 16 ti + lr and keys
+// j = 16 tj + lq .. +3; zero above the diagonal.
+__device__ __forceinline__ floatx4 tile_decay(const float* gam, int ti, int tj, int lr, int lq) {
+    const int i = 16 * ti + lr;
+    const float gi = gam[i];
+    const floatx4 gj = *reinterpret_cast<const floatx4*>(&gam[16 * tj + lq]);
+    floatx4 dec;
+    if (ti > tj) {
+        const float gc = gam[16 * ti];
+        const float rowf = fast_exp(gi - gc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - gj[r]);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dec[r] = i >= 16 * tj + lq + r ? fast_exp(gi - gj[r]) : 0.f;
+    }
+    return dec;
+}
+
+// One 16x16 tile of the FP32 matrix into the hi/lo bf16 copies.
+__device__ __forceinline__ void split_tile(const float* M, __bf16* hi, __bf16* lo, int ti, int tj, int lane) {
+    const int r = 16 * ti + (lane >> 2), c = 16 * tj + 4 * (lane & 3);
+    const floatx4 x = *reinterpret_cast<const floatx4*>(&M[r * kTriLd + c]);
+    bf16x4 h, l;
+    split4(x, h, l);
+    *reinterpret_cast<bf16x4*>(&hi[r * L64 + c]) = h;
+    *reinterpret_cast<bf16x4*>(&lo[r * L64 + c]) = l;
+}
+
+// Grid (value heads, prompts); NS = dv / 32 state waves, then kPrep prep waves.
+template <int DK, int NS>
+__global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const uint16_t* __restrict__ q,
+                                                                        const uint16_t* __restrict__ k,
+                                                                        const uint16_t* __restrict__ v,
+                                                                        const float* __restrict__ beta,
+                                                                        const float* __restrict__ g,
+                                                                        float* __restrict__ o, const float* S_in,
+                                                                        float* S_out, Batch bt, int Hk, int Hv,
+                                                                        int dv) {
+    static_assert(CG == 2, "a lane's column pair is one even and one odd column");
+    using Sm = PipeSmem<DK>;
     constexpr int LDK = Sm::LDK;
-    constexpr int KS = DK / 32;            // k-steps over dk
-    constexpr int RT = DK / 16;            // state row tiles
-    constexpr int PK = 64 * DK / 8;        // 16-byte pieces of a K (or Q) chunk
-    constexpr int NK = (PK + NT - 1) / NT;
+    constexpr int KS = DK / 32;             // k-steps over dk
+    constexpr int RT = DK / 16;             // state row tiles
+    constexpr int PK = 64 * DK / 8;         // 16-byte pieces of a K (or Q) chunk
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = lane & 15;        // fragment row / column within a tile
-    const int lg = lane >> 4;        // lane group
-    const int lk = lg * 8;           // contiguous fragment k offset
-    const int lq = lg * 4;           // accumulator row offset
-    const int ntile = dv / DVT;
-    const int h = blockIdx.x / ntile;
-    const int c0v = (blockIdx.x % ntile) * DVT;  // first column of the slice
+    const bool is_state = w < NS;
+    const int pw = w - NS;  // prep wave index
+    const int h = blockIdx.x;
     const int kh = h / (Hv / Hk);
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
-    const long sbase = ((long)p * Hv + h) * DK * dv + c0v + 16 * w;
-
-    // Per-lane address offsets pass through an empty asm wherever they are
-    // used, so that the compiler recomputes addresses (a few adds) instead of
-    // keeping dozens of 64-bit addresses alive across the chunk loop.
-    int s_lane = lq * dv + lr;
-    asm volatile("" : "+v"(s_lane));
-    floatx4 sacc[RT];
-#pragma unroll
-    for (int tr = 0; tr < RT; ++tr)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[tr][r] = S_in[sbase + s_lane + (long)(16 * tr + r) * dv];
-    // The masks' tiles above the diagonal stay zero for the whole prompt.
-    for (int e = tid; e < 64 * kTriLd; e += NT) sm.M[e] = 0.f;
-    for (int e = tid; e < 64 * L64; e += NT) sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
-
-    uint4 pk[NK], pq[NK];
-    uint16_t pv[16];  // next chunk's V in accumulator layout: rows 16t + 4(l/16) + r, column l%16 of this wave's slice
-    u16x2 vc2[8];     // this chunk's V, two rows a word
-    float pg = 0.f, pb = 0.f;
-    // Addresses: a 64-bit base per chunk (scalar) plus 32-bit lane offsets
-    // formed with 24-bit multiplies (heads x head size stays below 2^24).
+    const int nc = (L + 63) / 64;
     const uint32_t rowK = Hk * DK, rowV = Hv * dv;
-    auto fetch = [&](int c0) {
-        const int S = min(64, L - c0);
-        const uint16_t* kc = k + ((row0 + c0) * Hk + kh) * (long)DK;
-        const uint16_t* qc = q + ((row0 + c0) * Hk + kh) * (long)DK;
+    if (is_state) {
+        // ================= state waves: chunk n, 32 state columns each
+        // Lane l of a state wave holds columns col0 + 2 (l%16) + c, c = 0, 1: the
+        // two column groups are the even and the odd columns, so that V, O and
+        // the state move as pairs of adjacent columns.
+        const int col0 = 32 * w;
+        int s_lane = (lane >> 4) * 4 * dv + 2 * (lane & 15);
+        asm volatile("" : "+v"(s_lane));
+        const long sbase = ((long)p * Hv + h) * DK * dv + col0;
+        floatx4 sacc[CG][RT];
 #pragma unroll
-        for (int x = 0; x < NK; ++x) {
-            const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            pk[x] = pq[x] = make_uint4(0, 0, 0, 0);
-            if (e < PK && r < S) {
-                const uint32_t off = __umul24(r, rowK) + c8;
-                pk[x] = *reinterpret_cast<const uint4*>(kc + off);
-                pq[x] = *reinterpret_cast<const uint4*>(qc + off);
+        for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float2 x = *reinterpret_cast<const float2*>(&S_in[sbase + s_lane + (long)(16 * tr + r) * dv]);
+                sacc[0][tr][r] = x.x;
+                sacc[1][tr][r] = x.y;
             }
-        }
-        const uint16_t* vc = v + (row0 + c0) * (long)rowV + (long)h * dv + c0v + 16 * w;
-        int v_lane = lr;
-        asm volatile("" : "+v"(v_lane));
-        // Rows past the chunk re-read its last row and are zeroed where V is
-        // used; the values are packed only at staging, so nothing waits here.
+        // V of the next chunk in accumulator layout: rows 16t + 4(l/16) + r, both columns of the lane
+        uint32_t pv[16];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pv[4 * t + r] = vc[__umul24(min(16 * t + lq + r, S - 1), rowV) + v_lane];
-        pg = pb = 0.f;
-        if (tid < S) {
-            const long gi = (row0 + c0) * Hv + h + __umul24(tid, Hv);
-            pg = g[gi];
-            pb = beta[gi];
-        }
-    };
+        for (int x = 0; x < 16; ++x) pv[x] = 0;
+        __syncthreads();  // prologue: chunk 0 staged
+        __syncthreads();  // prologue: A of chunk 0 in M
 
-    if (L > 0) fetch(0);
-    for (int c0 = 0; c0 < L; c0 += 64) {
-        const int S = min(64, L - c0);
-        // The lane indices pass through an empty asm once per chunk, so that
-        // the LDS addresses derived from them are recomputed here instead of
-        // being held in registers across the whole prompt.
-        int tid_c = tid;
-        asm volatile("" : "+v"(tid_c));
-        const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
-        __syncthreads();  // previous chunk done with every LDS buffer
-        // ---- stage the prefetched chunk: K, Q, V, beta, gamma, Gamma, decay of the state update
-#pragma unroll
-        for (int x = 0; x < NK; ++x) {
-            const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            if (e < PK) {
-                *reinterpret_cast<uint4*>(&sm.K[r * LDK + c8]) = pk[x];
-                *reinterpret_cast<uint4*>(&sm.u.Q[r * LDK + c8]) = pq[x];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < 8; ++x) vc2[x] = u16x2{pv[2 * x], pv[2 * x + 1]};
-        if (tid < 64) {
-            sm.beta[tid] = pb;
-            const float x = wave_prefix_sum(pg);  // gamma, inclusive over the chunk rows
-            sm.gam[tid] = x;
-            sm.Gam[tid] = fast_exp(x);
-            const float gS = readlane_f(x, S - 1);  // the last cumulative sum
-            sm.decS[tid] = tid < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
-        }
-        __syncthreads();
+        for (int n = -1; n < nc; ++n) {
+            const int cb = n & 1, nb = cb ^ 1;  // K/Q buffers of chunks n, n+1
+            const int rb = (n + 3) % 3;         // row buffer of chunk n
+            const bool do_state = n >= 0, do_next = n + 1 < nc;
+            const int Sn = min(64, L - 64 * n);
+            int tid_c = tid;
+            asm volatile("" : "+v"(tid_c));
+            const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lq = lg * 4;
+            floatx4 ks0[CG][4], qs0[CG][4], u[CG][4];
 
-        // ---- private: K S_0 and Q S_0 for this wave's columns (B from the state accumulators)
-        floatx4 ks0[4], qs0[4];
+            // ---- A: K S_0, Q S_0 and RHS = diag(beta) V - diag(beta Gamma) K S_0
+            if (do_state) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ks0[t] = qs0[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < CG; ++c)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            bf16x8 bh, bl;
-            acc_frag(sacc[2 * s], sacc[2 * s + 1], bh, bl);
+                    for (int t = 0; t < 4; ++t) ks0[c][t] = qs0[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bf16x8 ak = frag_perm(&sm.K[(16 * t + lr) * LDK + 32 * s], lg);
-                const bf16x8 aq = frag_perm(&sm.u.Q[(16 * t + lr) * LDK + 32 * s], lg);
-                ks0[t] = mfma(ak, bh, ks0[t]);
-                ks0[t] = mfma(ak, bl, ks0[t]);
-                qs0[t] = mfma(aq, bh, qs0[t]);
-                qs0[t] = mfma(aq, bl, qs0[t]);
+                for (int s = 0; s < KS; ++s) {
+                    bf16x8 bh[CG], bl[CG];
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) acc_frag(sacc[c][2 * s], sacc[c][2 * s + 1], bh[c], bl[c]);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const bf16x8 ak = frag_perm(&sm.K[cb][(16 * t + lr) * LDK + 32 * s], lg);
+                        const bf16x8 aq = frag_perm(&sm.Q[cb][(16 * t + lr) * LDK + 32 * s], lg);
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) {
+                            ks0[c][t] = mfma(ak, bh[c], ks0[c][t]);
+                            ks0[c][t] = mfma(ak, bl[c], ks0[c][t]);
+                            qs0[c][t] = mfma(aq, bh[c], qs0[c][t]);
+                            qs0[c][t] = mfma(aq, bl[c], qs0[c][t]);
+                        }
+                    }
+                }
+                read_ahead<4 * KS, 2, 4 * CG, 2>();
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const floatx4 b4 = *reinterpret_cast<const floatx4*>(&sm.beta[rb][16 * t + lq]);
+                    const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[rb][16 * t + lq]);
+#pragma unroll
+                    for (int c = 0; c < CG; ++c)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            // rows past the chunk hold a copy of its last row of V; beta is 0 there
+                            const float vv = c ? __uint_as_float(pv[4 * t + r] & 0xffff0000u)
+                                               : __uint_as_float(pv[4 * t + r] << 16);
+                            ks0[c][t][r] = b4[r] * (vv - G4[r] * ks0[c][t][r]);
+                        }
+                }
             }
+            __syncthreads();
+
+            // ---- B: U = T RHS (T lower triangular: k-steps up to the row tile's diagonal)
+            if (do_state) {
+#pragma unroll
+                for (int c = 0; c < CG; ++c)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) u[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    bf16x8 bh[CG], bl[CG];
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) acc_frag(ks0[c][2 * s], ks0[c][2 * s + 1], bh[c], bl[c]);
+#pragma unroll
+                    for (int t = 2 * s; t < 4; ++t) {
+                        const bf16x8 ah = frag_perm(&sm.T_hi[(16 * t + lr) * L64 + 32 * s], lg);
+                        const bf16x8 al = frag_perm(&sm.T_lo[(16 * t + lr) * L64 + 32 * s], lg);
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) {
+                            u[c][t] = mfma(ah, bh[c], u[c][t]);
+                            u[c][t] = mfma(ah, bl[c], u[c][t]);
+                            u[c][t] = mfma(al, bh[c], u[c][t]);
+                        }
+                    }
+                }
+                read_ahead<6, 2, 3 * CG, 2>();
+            }
+            __syncthreads();
+
+            // ---- C: O = diag(Gamma) Q S_0 + P U
+            if (do_state) {
+                floatx4 pu[CG][4];
+#pragma unroll
+                for (int c = 0; c < CG; ++c)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) pu[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    bf16x8 bh[CG], bl[CG];
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) acc_frag(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
+#pragma unroll
+                    for (int t = 2 * s; t < 4; ++t) {
+                        const bf16x8 ah = frag_perm(&sm.P_hi[(16 * t + lr) * L64 + 32 * s], lg);
+                        const bf16x8 al = frag_perm(&sm.P_lo[(16 * t + lr) * L64 + 32 * s], lg);
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) {
+                            pu[c][t] = mfma(ah, bh[c], pu[c][t]);
+                            pu[c][t] = mfma(ah, bl[c], pu[c][t]);
+                            pu[c][t] = mfma(al, bh[c], pu[c][t]);
+                        }
+                    }
+                }
+                read_ahead<6, 2, 3 * CG, 2>();
+                float* oc = o + (row0 + 64 * n) * (long)rowV + (long)h * dv + col0;
+                uint32_t o_lane = __umul24(lq, rowV) + 2 * lr;
+                asm volatile("" : "+v"(o_lane));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[rb][16 * t + lq]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * t + lq + r < Sn)
+                            *reinterpret_cast<float2*>(&oc[o_lane + (16 * t + r) * rowV]) =
+                                float2{fmaf(G4[r], qs0[0][t][r], pu[0][t][r]), fmaf(G4[r], qs0[1][t][r], pu[1][t][r])};
+                }
+            }
+            __syncthreads();
+
+            // ---- D: S_S = e^{gamma_S} S_0 + K^T (decS U); V of chunk n+1
+            if (do_state) {
+                const float GS = sm.Gam[rb][Sn - 1];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sm.decS[rb][16 * t + lq]);
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) u[c][t] *= d4;
+                }
+#pragma unroll
+                for (int c = 0; c < CG; ++c)
+#pragma unroll
+                    for (int tr = 0; tr < RT; ++tr) sacc[c][tr] = sacc[c][tr] * GS;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    bf16x8 bh[CG], bl[CG];
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) acc_frag(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
+#pragma unroll
+                    for (int tr = 0; tr < RT; ++tr) {
+                        const bf16x8 a = frag_perm(&sm.KT[(16 * tr + lr) * L64 + 32 * s], lg);
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) {
+                            sacc[c][tr] = mfma(a, bh[c], sacc[c][tr]);
+                            sacc[c][tr] = mfma(a, bl[c], sacc[c][tr]);
+                        }
+                    }
+                }
+                read_ahead<2 * RT, 2, 2 * CG, 2>();
+            }
+            if (do_next) {
+                // Rows past the chunk re-read its last row and are zeroed where V is used.
+                const int c0 = 64 * (n + 1), S = min(64, L - c0);
+                const uint16_t* vc = v + (row0 + c0) * (long)rowV + (long)h * dv + col0;
+                int v_lane = 2 * lr, v_q = lq;
+                asm volatile("" : "+v"(v_lane), "+v"(v_q));
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pv[4 * t + r] = *reinterpret_cast<const uint32_t*>(
+                            &vc[__umul24(min(16 * t + v_q + r, S - 1), rowV) + v_lane]);
+            }
+            __syncthreads();
+
+            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks
+            if (do_next) {
+                for (int b = tid; b < 2 * DK; b += 64 * NS) {
+                    const int nn = b & 15, m = b >> 4;  // rows 4nn .. 4nn+3, columns 8m .. 8m+7
+                    uint4 rw[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        rw[a] = *reinterpret_cast<const uint4*>(&sm.K[nb][(4 * nn + a) * LDK + 8 * m]);
+                    const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
+                    const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
+                    const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
+                    const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
+                        uint2 out;
+                        out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
+                        out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
+                        *reinterpret_cast<uint2*>(&sm.KT[(8 * m + e) * L64 + 4 * nn]) = out;
+                    }
+                }
+            }
+            __syncthreads();
         }
-        // ---- shared: masked products, transposed (keys as rows) -> A (FP32) and P (hi/lo)
-        {
-            constexpr int PPW = (10 + NW - 1) / NW;  // tile pairs per wave
-            floatx4 kk[PPW], qk[PPW];
-            int ti[PPW], tj[PPW];
+        asm volatile("" : "+v"(s_lane));
 #pragma unroll
-            for (int q = 0; q < PPW; ++q) {
-                const int pr = min(w + q * NW, 9);
-                ti[q] = kPairs[pr][0];
-                tj[q] = kPairs[pr][1];
-                kk[q] = qk[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<float2*>(&S_out[sbase + s_lane + (long)(16 * tr + r) * dv]) =
+                    float2{sacc[0][tr][r], sacc[1][tr][r]};
+    } else {
+        // ================= prep waves: inverse of chunk n+1, staging of chunk n+2, A of chunk n+2
+        constexpr int PT = 64 * kPrep;
+        constexpr int NF = (2 * PK + PT - 1) / PT;
+        const int pt = tid - 64 * NS;  // thread index among the prep waves
+        uint4 pf[NF];                  // K and Q rows of a chunk, in flight to LDS
+        float pg = 0.f, pb = 0.f;      // its g and beta (last prep wave)
+        auto fetch = [&](int c0) {
+            const int S = min(64, L - c0);
+            const uint16_t* kc = k + ((row0 + c0) * Hk + kh) * (long)DK;
+            const uint16_t* qc = q + ((row0 + c0) * Hk + kh) * (long)DK;
+#pragma unroll
+            for (int x = 0; x < NF; ++x) {
+                const int e = min(pt + x * PT, 2 * PK - 1);
+                const bool isq = e >= PK;
+                const int ee = isq ? e - PK : e, r = ee / (DK / 8), c8 = (ee % (DK / 8)) * 8;
+                const uint32_t off = __umul24(min(r, S - 1), rowK) + c8;
+                pf[x] = *reinterpret_cast<const uint4*>((isq ? qc : kc) + off);
             }
+            if (pw == kPrep - 1) {
+                const long gi = (row0 + c0) * Hv + h + __umul24(min(lane, S - 1), Hv);
+                pg = g[gi];
+                pb = beta[gi];
+            }
+        };
+        // Rows past the chunk are written as zeros; gamma stays flat there.
+        auto stage = [&](int c0, int b, int rbuf) {
+            const int S = min(64, L - c0);
+#pragma unroll
+            for (int x = 0; x < NF; ++x) {
+                const int e = pt + x * PT;
+                if (e < 2 * PK) {
+                    const bool isq = e >= PK;
+                    const int ee = isq ? e - PK : e, r = ee / (DK / 8), c8 = (ee % (DK / 8)) * 8;
+                    const uint4 val = r < S ? pf[x] : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(&(isq ? sm.Q[b] : sm.K[b])[r * LDK + c8]) = val;
+                }
+            }
+            if (pw == kPrep - 1) {
+                const float x = wave_prefix_sum(lane < S ? pg : 0.f);  // gamma, inclusive over the chunk rows
+                sm.gam[rbuf][lane] = x;
+                sm.Gam[rbuf][lane] = fast_exp(x);
+                sm.beta[rbuf][lane] = lane < S ? pb : 0.f;
+                const float gS = readlane_f(x, S - 1);  // the last cumulative sum
+                sm.decS[rbuf][lane] = lane < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
+            }
+        };
+        // masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M, by tile pairs
+        auto masked_kk = [&](int b, int rbuf) {
+            int tid_c = tid;
+            asm volatile("" : "+v"(tid_c));
+            const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
+            constexpr int PPW = (10 + kPrep - 1) / kPrep;
+            floatx4 kk[PPW];
+#pragma unroll
+            for (int x = 0; x < PPW; ++x) kk[x] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s)
 #pragma unroll
-                for (int q = 0; q < PPW; ++q) {
-                    const bf16x8 ak = frag(&sm.K[(16 * tj[q] + lr) * LDK + 32 * s + lk]);
-                    kk[q] = mfma(ak, frag(&sm.K[(16 * ti[q] + lr) * LDK + 32 * s + lk]), kk[q]);
-                    qk[q] = mfma(ak, frag(&sm.u.Q[(16 * ti[q] + lr) * LDK + 32 * s + lk]), qk[q]);
+                for (int x = 0; x < PPW; ++x) {
+                    int ti, tj;
+                    tile_pair(min(pw + x * kPrep, 9), ti, tj);  // past the last pair: computed, not stored
+                    kk[x] = mfma(frag(&sm.K[b][(16 * tj + lr) * LDK + 32 * s + lk]),
+                                 frag(&sm.K[b][(16 * ti + lr) * LDK + 32 * s + lk]), kk[x]);
                 }
+            read_ahead<KS * PPW, 2, 1, 3>();
 #pragma unroll
-            for (int q = 0; q < PPW; ++q) {
-                if (w + q * NW >= 10) break;
-                const int i = 16 * ti[q] + lr;
-                const float gi = sm.gam[i];
-                const floatx4 gj = *reinterpret_cast<const floatx4*>(&sm.gam[16 * tj[q] + lq]);
-                floatx4 dec;
-                if (ti[q] > tj[q]) {
-                    const float gc = sm.gam[16 * ti[q]];
-                    const float rowf = fast_exp(gi - gc);
+            for (int x = 0; x < PPW; ++x)
+                if (pw + x * kPrep < 10) {
+                    int ti, tj;
+                        tile_pair(pw + x * kPrep, ti, tj);
+                    const floatx4 dec = tile_decay(sm.gam[rbuf], ti, tj, lr, lq);
+                    const int i = 16 * ti + lr;
+                    const float bi = sm.beta[rbuf][i];
+                    floatx4 av;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dec[r] = rowf * fast_exp(gc - gj[r]);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * tj[q] + lq + r;
-                        dec[r] = i >= j ? fast_exp(gi - gj[r]) : 0.f;
-                    }
+                    for (int r = 0; r < 4; ++r) av[r] = i > 16 * tj + lq + r ? bi * dec[r] * kk[x][r] : 0.f;
+                    *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
                 }
-                const float bi = sm.beta[i];
-                floatx4 av, pv4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * tj[q] + lq + r;
-                    av[r] = i > j ? bi * dec[r] * kk[q][r] : 0.f;
-                    pv4[r] = dec[r] * qk[q][r];
-                }
-                *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj[q] + lq]) = av;
-                bf16x4 ph, pl;
-                split4(pv4, ph, pl);
-                *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj[q] + lq]) = ph;
-                *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj[q] + lq]) = pl;
-            }
-        }
-        // ---- private: RHS = diag(beta) V - diag(beta Gamma) K S_0, in registers
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const floatx4 b4 = *reinterpret_cast<const floatx4*>(&sm.beta[16 * t + lq]);
-            const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[16 * t + lq]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint16_t raw = (r & 1) ? vc2[2 * t + r / 2].y : vc2[2 * t + r / 2].x;
-                const float vv = 16 * t + lq + r < S ? bf16_to_f32(raw) : 0.f;
-                ks0[t][r] = b4[r] * (vv - G4[r] * ks0[t][r]);
-            }
-        }
-        // ---- shared: T = (I + A)^-1 in FP32 (barriers inside), then T as hi/lo bf16
-        tri_inverse64<NW>(sm.M, sm.scratch);
-        if (c0 + 64 < L) fetch(c0 + 64);  // next chunk's rows, in flight during U, O and the state update
-#pragma unroll
-        for (int xi = 0; xi < 512 / NT; ++xi) {
-            const int x = tid + xi * NT;
-            const int r = x >> 3, c = (x & 7) * 8;
-            const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c]);
-            const floatx4 b = *reinterpret_cast<const floatx4*>(&sm.M[r * kTriLd + c + 4]);
-            bf16x4 ah, al, bh, bl;
-            split4(a, ah, al);
-            split4(b, bh, bl);
-            *reinterpret_cast<bf16x8*>(&sm.u.T.hi[r * L64 + c]) = bf16x8{ah[0], ah[1], ah[2], ah[3], bh[0], bh[1], bh[2], bh[3]};
-            *reinterpret_cast<bf16x8*>(&sm.u.T.lo[r * L64 + c]) = bf16x8{al[0], al[1], al[2], al[3], bl[0], bl[1], bl[2], bl[3]};
-        }
-        __syncthreads();
+        };
 
-        // ---- private: U = T RHS (T lower triangular: k-steps up to the row tile's diagonal)
-        floatx4 u[4];
+        // masked decayed Q K^T of the chunk in buffers (b, rbuf) -> P as hi/lo, transposed (keys as rows)
+        auto masked_qk = [&](int b, int rbuf) {
+            int tid_c = tid;
+            asm volatile("" : "+v"(tid_c));
+            const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
+            constexpr int PPW = (10 + kPrep - 1) / kPrep;
+            floatx4 qk[PPW];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) u[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int x = 0; x < PPW; ++x) qk[x] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            bf16x8 bh, bl;
-            acc_frag(ks0[2 * s], ks0[2 * s + 1], bh, bl);
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int t = 2 * s; t < 4; ++t) {
-                const bf16x8 ah = frag_perm(&sm.u.T.hi[(16 * t + lr) * L64 + 32 * s], lg);
-                const bf16x8 al = frag_perm(&sm.u.T.lo[(16 * t + lr) * L64 + 32 * s], lg);
-                u[t] = mfma(ah, bh, u[t]);
-                u[t] = mfma(ah, bl, u[t]);
-                u[t] = mfma(al, bh, u[t]);
-            }
-        }
-        __syncthreads();  // every wave is done reading T
-        // ---- shared: K^T by 4-row x 8-column blocks, into the buffer T occupied
-        for (int b = tid; b < 2 * DK; b += NT) {
-            const int n = b & 15, m = b >> 4;  // rows 4n .. 4n+3, columns 8m .. 8m+7
-            uint4 rw[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) rw[a] = *reinterpret_cast<const uint4*>(&sm.K[(4 * n + a) * LDK + 8 * m]);
-            const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
-            const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
-            const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
-            const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
-                uint2 out;
-                out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
-                out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
-                *reinterpret_cast<uint2*>(&sm.u.KT[(8 * m + e) * L64 + 4 * n]) = out;
-            }
-        }
-        // ---- private: O = diag(Gamma) Q S_0 + P U for this wave's columns
-        {
-            floatx4 pu[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) pu[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                bf16x8 bh, bl;
-                acc_frag(u[2 * s], u[2 * s + 1], bh, bl);
-#pragma unroll
-                for (int t = 2 * s; t < 4; ++t) {
-                    const bf16x8 ah = frag_perm(&sm.P_hi[(16 * t + lr) * L64 + 32 * s], lg);
-                    const bf16x8 al = frag_perm(&sm.P_lo[(16 * t + lr) * L64 + 32 * s], lg);
-                    pu[t] = mfma(ah, bh, pu[t]);
-                    pu[t] = mfma(ah, bl, pu[t]);
-                    pu[t] = mfma(al, bh, pu[t]);
+                for (int x = 0; x < PPW; ++x) {
+                    int ti, tj;
+                    tile_pair(min(pw + x * kPrep, 9), ti, tj);  // past the last pair: computed, not stored
+                    qk[x] = mfma(frag(&sm.K[b][(16 * tj + lr) * LDK + 32 * s + lk]),
+                                 frag(&sm.Q[b][(16 * ti + lr) * LDK + 32 * s + lk]), qk[x]);
                 }
-            }
-            float* oc = o + (row0 + c0) * (long)rowV + (long)h * dv + c0v + 16 * w;
-            uint32_t o_lane = __umul24(lq, rowV) + lr;
-            asm volatile("" : "+v"(o_lane));
+            read_ahead<KS * PPW, 2, 1, 3>();
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[16 * t + lq]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * t + lq + r < S) oc[o_lane + (16 * t + r) * rowV] = fmaf(G4[r], qs0[t][r], pu[t][r]);
-            }
-        }
-        __syncthreads();  // K^T complete
-        // ---- private: S_S = e^{gamma_S} S_0 + K^T (decS * U), in the state accumulators
-        {
-            const float GS = sm.Gam[S - 1];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) u[t] *= *reinterpret_cast<const floatx4*>(&sm.decS[16 * t + lq]);
-#pragma unroll
-            for (int tr = 0; tr < RT; ++tr) sacc[tr] = sacc[tr] * GS;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                bf16x8 bh, bl;
-                acc_frag(u[2 * s], u[2 * s + 1], bh, bl);
-#pragma unroll
-                for (int tr = 0; tr < RT; ++tr) {
-                    const bf16x8 a = frag_perm(&sm.u.KT[(16 * tr + lr) * L64 + 32 * s], lg);
-                    sacc[tr] = mfma(a, bh, sacc[tr]);
-                    sacc[tr] = mfma(a, bl, sacc[tr]);
+            for (int x = 0; x < PPW; ++x)
+                if (pw + x * kPrep < 10) {
+                    int ti, tj;
+                    tile_pair(pw + x * kPrep, ti, tj);
+                    const floatx4 pv4 = tile_decay(sm.gam[rbuf], ti, tj, lr, lq) * qk[x];
+                    const int i = 16 * ti + lr;
+                    bf16x4 ph, pl;
+                    split4(pv4, ph, pl);
+                    *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj + lq]) = ph;
+                    *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj + lq]) = pl;
                 }
+        };
+
+        // Tiles above the diagonal stay zero for the whole prompt.
+        for (int e = pt; e < 64 * kTriLd; e += PT) sm.M[e] = 0.f;
+        for (int e = pt; e < 64 * L64; e += PT)
+            sm.T_hi[e] = sm.T_lo[e] = sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
+        if (nc > 0) {
+            fetch(0);
+            stage(0, 0, 0);
+        }
+        if (nc > 1) fetch(64);
+        __syncthreads();  // prologue: chunk 0 staged
+        if (nc > 0) masked_kk(0, 0);
+        __syncthreads();  // prologue: A of chunk 0 in M
+
+        for (int n = -1; n < nc; ++n) {
+            const bool do_next = n + 1 < nc, do_stage = n + 2 < nc;
+            const int nb = (n + 1) & 1, nrb = (n + 4) % 3;  // buffers of chunk n+1
+
+            // ---- A: diagonal tiles of the inverse of chunk n+1
+            if (do_next) tri::diag<kPrep>(sm.M, sm.scratch, pw);
+            __syncthreads();
+
+            // ---- B: level 16; chunk n+2 into the buffers chunk n used, chunk n+3 in flight
+            if (do_next) tri::lvl16<kPrep>(sm.M, pw);
+            if (do_stage) {
+                stage(64 * (n + 2), n & 1, (n + 5) % 3);
+                if (n + 3 < nc) fetch(64 * (n + 3));
             }
+            __syncthreads();
+
+            // ---- C: level 32 (first half); the tiles of T that are final go to hi/lo
+            if (do_next) {
+                tri::lvl32a<kPrep>(sm.M, sm.scratch, pw);
+                split_tile(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
+                if (pw == 0) split_tile(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
+                if (pw == 1) split_tile(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
+            }
+            __syncthreads();
+
+            // ---- D: level 32 (second half) and its tile of T; P of chunk n+1
+            if (do_next) {
+                tri::lvl32b<kPrep>(sm.M, sm.scratch, pw);
+                tri::wave_sync();
+                split_tile(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
+                masked_qk(nb, nrb);
+            }
+            __syncthreads();
+
+            // ---- E: A of chunk n+2 into M (T of chunk n+1 is in hi/lo now)
+            if (do_stage) masked_kk(n & 1, (n + 5) % 3);
+            __syncthreads();
         }
     }
-    asm volatile("" : "+v"(s_lane));
-#pragma unroll
-    for (int tr = 0; tr < RT; ++tr)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S_out[sbase + s_lane + (long)(16 * tr + r) * dv] = sacc[tr][r];
 }
 
-template <int DK, int DVT>
-hipError_t launch_mfma(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
+template <int DK, int NS>
+hipError_t launch_pipe(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                        const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dv, hipStream_t st) {
-    auto kern = gdn_mfma_kernel<DK, DVT>;
-    const size_t smem = sizeof(MfmaSmem<DK, DVT>);
+    auto kern = gdn_pipe_kernel<DK, NS>;
+    const size_t smem = sizeof(PipeSmem<DK>);
     static bool configured = false;
     if (!configured) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -440,21 +601,21 @@ hipError_t launch_mfma(const void* q, const void* k, const void* v, const float*
         if (e != hipSuccess) return e;
         configured = true;
     }
-    const dim3 grid((unsigned)(Hv * (dv / DVT)), (unsigned)bt.P);
-    hipLaunchKernelGGL(kern, grid, dim3(DVT * 4), smem, st, static_cast<const uint16_t*>(q),
+    const dim3 grid((unsigned)Hv, (unsigned)bt.P);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * (NS + kPrep)), smem, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, g, o, S_in, S_out, bt,
                        Hk, Hv, dv);
     return hipGetLastError();
 }
 
-template <int DVT>
+template <int NS>
 hipError_t launch_dk(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                      const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
                      hipStream_t st) {
     switch (dk) {
-        case 32: return launch_mfma<32, DVT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-        case 64: return launch_mfma<64, DVT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-        case 128: return launch_mfma<128, DVT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 32: return launch_pipe<32, NS>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 64: return launch_pipe<64, NS>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 128: return launch_pipe<128, NS>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
     }
     return hipErrorInvalidValue;
 }
@@ -464,9 +625,10 @@ hipError_t launch_dk(const void* q, const void* k, const void* v, const float* b
 hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, const float* beta, const float* g,
                                 float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
                                 int dv, hipStream_t st) {
-    if (dv == 32) return launch_dk<32>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
-    if (dv == 128) return launch_dk<128>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
-    return launch_dk<64>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    if (dv == 32) return launch_dk<1>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    if (dv == 64) return launch_dk<2>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    if (dv == 128) return launch_dk<4>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace lrc

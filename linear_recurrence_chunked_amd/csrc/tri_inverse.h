@@ -20,7 +20,8 @@
 // diagonal blocks, D = (I - N)(I + N^2)(I + N^4) inverts both at once, and the
 // level-8 step is T = D - D (L D) with L the tile's lower-left 8x8 block of A.
 // The level-16 and level-32 steps follow with workgroup barriers between
-// them (five barriers in all).  Products run in FP32 with FP32 accumulation.
+// them (five barriers in all); the phases are also available one by one, for
+// callers that interleave other work between the barriers.  Products run in FP32 with FP32 accumulation.
 //
 // Tile product Z = X Y: lane l holds, for X, the row segment
 // X[l%16][4g .. 4g+3] (g = l/16) and, for Y, the accumulator-layout column
@@ -67,27 +68,33 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace tri
 
+// The inverse in four phases, each run by NW waves numbered w = 0 .. NW-1
+// and separated by workgroup barriers that the caller provides:
+//   diag    each diagonal 16x16 tile: Neumann on its 8x8 blocks, level 8
+//   lvl16   T21 of the two 32x32 diagonal blocks
+//   lvl32a  Y = L21 T11 of the 64x64 matrix, into scratch
+//   lvl32b  T21 = -T22 Y
 // In:  M[i * kTriLd + j] holds A_ij for j < i; entries above the diagonal
 //      must be zero; diagonal entries are ignored.
 // Out: M holds T = (I + A)^-1 (ones on the diagonal, zeros above).
-// All NW waves of the block must call it; it begins and ends with a barrier.
-template <int NW>
-__device__ inline void tri_inverse64(float* M, float* scratch) {
-    using tri::ld_acc;
-    using tri::ld_row;
-    using tri::mm;
-    using tri::st_acc;
-    constexpr int ld = kTriLd;
+namespace tri {
+
+__device__ __forceinline__ void lanes(int& lr, int& g) {
     // lane index through an empty asm: addresses are formed per call, not
     // kept in registers by a caller that calls this in a loop
     int tl = threadIdx.x;
     asm volatile("" : "+v"(tl));
-    const int lane = tl & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lr = lane & 15, g = lane >> 4;
-    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
+    const int lane = tl & 63;
+    lr = lane & 15;
+    g = lane >> 4;
+}
 
-    // ---- diagonal 16x16 tiles: Neumann on the 8x8 blocks, then the level-8 step
+template <int NW>
+__device__ inline void diag(float* M, float* scratch, int w) {
+    constexpr int ld = kTriLd;
+    int lr, g;
+    lanes(lr, g);
+    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int t = w; t < 4; t += NW) {
         float* Mt = M + 16 * t * ld + 16 * t;
         float* S = scratch + t * 16 * 20;
@@ -106,50 +113,88 @@ __device__ inline void tri_inverse64(float* M, float* scratch) {
         const tri_f4 n2 = mm(zero, nrow, nacc);   // N^2
         const tri_f4 nn2 = mm(zero, nrow, n2);    // N N^2
         st_acc(S, 20, lr, g, n2);
-        tri::wave_sync();
+        wave_sync();
         const tri_f4 n4 = mm(zero, ld_row(S, 20, lr, g), n2);  // N^4
         tri_f4 x;                                               // (I - N)(I + N^2)
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = (4 * g + k == lr ? 1.f : 0.f) - nacc[k] + n2[k] - nn2[k];
-        tri::wave_sync();
+        wave_sync();
         st_acc(S, 20, lr, g, x);
-        tri::wave_sync();
+        wave_sync();
         const tri_f4 d = x + mm(zero, ld_row(S, 20, lr, g), n4);  // D = X (I + N^4)
         const tri_f4 y = mm(zero, lorow, d);                       // L D
-        tri::wave_sync();
+        wave_sync();
         st_acc(S, 20, lr, g, d);
-        tri::wave_sync();
+        wave_sync();
         const tri_f4 z = mm(zero, ld_row(S, 20, lr, g), y);       // D L D
         st_acc(Mt, ld, lr, g, d - z);
     }
-    __syncthreads();
-    // ---- level 16: blocks b = 0, 1 (rows 32b+16 .., columns 32b ..)
+}
+
+// level 16: blocks b = 0, 1 (rows 32b+16 .., columns 32b ..)
+template <int NW>
+__device__ inline void lvl16(float* M, int w) {
+    constexpr int ld = kTriLd;
+    int lr, g;
+    lanes(lr, g);
+    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int b = w; b < 2; b += NW) {
         float* L21 = M + (32 * b + 16) * ld + 32 * b;
         const tri_f4 y = mm(zero, ld_row(L21, ld, lr, g), ld_acc(M + 32 * b * ld + 32 * b, ld, lr, g));
         const tri_f4 z = mm(zero, ld_row(M + (32 * b + 16) * ld + 32 * b + 16, ld, lr, g), y);
         st_acc(L21, ld, lr, g, -z);
     }
-    __syncthreads();
-    // ---- level 32: Y = L21 T11, then T21 = -T22 Y, by 16x16 output tiles (ta, tb)
-    float* Y = scratch;  // 32 x 36
+}
+
+// level 32, first half: Y = L21 T11 by 16x16 output tiles (ta, tb), into scratch (32 x 36)
+template <int NW>
+__device__ inline void lvl32a(float* M, float* scratch, int w) {
+    constexpr int ld = kTriLd;
+    int lr, g;
+    lanes(lr, g);
+    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int q = w; q < 4; q += NW) {
         const int ta = q >> 1, tb = q & 1;
         tri_f4 acc = zero;
         for (int c = tb; c < 2; ++c)  // T11 is block lower triangular
             acc = mm(acc, ld_row(M + (32 + 16 * ta) * ld + 16 * c, ld, lr, g),
                      ld_acc(M + 16 * c * ld + 16 * tb, ld, lr, g));
-        st_acc(Y + 16 * ta * 36 + 16 * tb, 36, lr, g, acc);
+        st_acc(scratch + 16 * ta * 36 + 16 * tb, 36, lr, g, acc);
     }
-    __syncthreads();
+}
+
+// level 32, second half: T21 = -T22 Y
+template <int NW>
+__device__ inline void lvl32b(float* M, const float* scratch, int w) {
+    constexpr int ld = kTriLd;
+    int lr, g;
+    lanes(lr, g);
+    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int q = w; q < 4; q += NW) {
         const int ta = q >> 1, tb = q & 1;
         tri_f4 acc = zero;
         for (int c = 0; c <= ta; ++c)  // T22 is block lower triangular
             acc = mm(acc, ld_row(M + (32 + 16 * ta) * ld + 32 + 16 * c, ld, lr, g),
-                     ld_acc(Y + 16 * c * 36 + 16 * tb, 36, lr, g));
+                     ld_acc(scratch + 16 * c * 36 + 16 * tb, 36, lr, g));
         st_acc(M + (32 + 16 * ta) * ld + 16 * tb, ld, lr, g, -acc);
     }
+}
+
+}  // namespace tri
+
+// The whole inverse for a workgroup of NW waves.  All NW waves of the block
+// must call it; it begins and ends with a barrier.
+template <int NW>
+__device__ inline void tri_inverse64(float* M, float* scratch) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __syncthreads();
+    tri::diag<NW>(M, scratch, w);
+    __syncthreads();
+    tri::lvl16<NW>(M, w);
+    __syncthreads();
+    tri::lvl32a<NW>(M, scratch, w);
+    __syncthreads();
+    tri::lvl32b<NW>(M, scratch, w);
     __syncthreads();
 }
 
