@@ -34,15 +34,20 @@ constexpr int kUnroll = 8;
 template <typename T>
 struct Io;
 
+// The 16-byte row accesses of the streamed inputs and outputs are nontemporal:
+// each row is read (or written) once, so it need not stay in the caches.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <>
 struct Io<float> {
     static constexpr int VEC = 4;
     __device__ static void load(const float* p, float* out) {
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
     }
     __device__ static void store(float* p, const float* in) {
-        *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+        __builtin_nontemporal_store(f32x4{in[0], in[1], in[2], in[3]}, reinterpret_cast<f32x4*>(p));
     }
     __device__ static float one(const float* p) { return *p; }
     __device__ static void put(float* p, float x) { *p = x; }
@@ -52,8 +57,8 @@ template <>
 struct Io<uint16_t> {
     static constexpr int VEC = 8;
     __device__ static void load(const uint16_t* p, float* out) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const uint32_t wds[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             out[2 * i] = __uint_as_float(wds[i] << 16);
@@ -66,7 +71,7 @@ struct Io<uint16_t> {
         bf16x8 v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = static_cast<__bf16>(in[i]);
-        *reinterpret_cast<bf16x8*>(p) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p));
     }
     __device__ static float one(const uint16_t* p) { return bf16_to_f32(*p); }
     __device__ static void put(uint16_t* p, float x) { *reinterpret_cast<__bf16*>(p) = static_cast<__bf16>(x); }

@@ -27,6 +27,7 @@
 //     read follows the write of its source too closely.
 //  3. h_t = A_t h0 + B_t; the new carried state is read from lane S-1; the
 //     h column goes back to LDS and leaves as row-contiguous 16-byte stores.
+//  The row loads and stores are nontemporal: every byte is used once.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
@@ -40,6 +41,11 @@ namespace {
 constexpr int kScanCols = 256;
 
 constexpr int kColsPerWave = 16;
+
+// a, b and h are touched once each: the 16-byte accesses are marked
+// nontemporal (streaming), which measured 5% faster than plain accesses on
+// the mixed prefill shape (plain stores with nontemporal loads were slower).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LRC_SCAN_ROUND(CTRL)                                   \
     "v_fmac_f32_dpp %0, %0, %4 " CTRL "\n"                    \
@@ -110,8 +116,10 @@ __global__ __launch_bounds__(COLS * 4) void scan_rows_kernel(const float* __rest
             if (VEC4) {
                 float4 va = make_float4(1.f, 1.f, 1.f, 1.f), vb = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (row < S && lcol_ok) {
-                    va = *reinterpret_cast<const float4*>(a + off);
-                    vb = *reinterpret_cast<const float4*>(b + off);
+                    const f32x4 xa = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a + off));
+                    const f32x4 xb = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(b + off));
+                    va = make_float4(xa[0], xa[1], xa[2], xa[3]);
+                    vb = make_float4(xb[0], xb[1], xb[2], xb[3]);
                 }
                 ra[r][0] = va.x; ra[r][1] = va.y; ra[r][2] = va.z; ra[r][3] = va.w;
                 rb[r][0] = vb.x; rb[r][1] = vb.y; rb[r][2] = vb.z; rb[r][3] = vb.w;
@@ -167,7 +175,8 @@ __global__ __launch_bounds__(COLS * 4) void scan_rows_kernel(const float* __rest
                 const long off = (row0 + c0 + row) * E + tile0 + lc;
                 const float* src = &As[row * kLd + lc];
                 if (VEC4) {
-                    if (lcol_ok) *reinterpret_cast<float4*>(h + off) = make_float4(src[0], src[1], src[2], src[3]);
+                    if (lcol_ok)
+                        __builtin_nontemporal_store(f32x4{src[0], src[1], src[2], src[3]}, reinterpret_cast<f32x4*>(h + off));
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)

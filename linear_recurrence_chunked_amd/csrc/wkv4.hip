@@ -150,7 +150,8 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
     float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R];  // ring of row buffers
     // Loads are issued unconditionally (rows past the prompt re-read its last
     // row) so that the compiler can count them and wait only for the chunk
-    // about to be used, not for the one being prefetched.
+    // about to be used, not for the one being prefetched.  k, v and the
+    // output are touched once: their accesses are nontemporal (streaming).
     // Row offsets within a chunk are 32-bit (64 rows x C); the base moves per chunk.
     auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R]) {
         const int r0 = min(c0 + R * wv, L - 1);
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int off = min(i, last) * C;
-            kb[i] = kc[off];
-            vb[i] = vc[off];
+            kb[i] = __builtin_nontemporal_load(kc + off);
+            vb[i] = __builtin_nontemporal_load(vc + off);
         }
     };
     int buf = 0;
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const float o = out_row(s, wc, uc, kb[i], vb[i]);
-                if (valid) op[i * C] = o;
+                if (valid) __builtin_nontemporal_store(o, op + i * C);
                 if (i + 1 < R) push_row(s, wc, kb[i], vb[i]);
             }
         } else if (nb > 0) {
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
             for (int i = 0; i < R; ++i)
                 if (i < nb) {
                     const float o = out_row(s, wc, uc, kb[i], vb[i]);
-                    if (valid) op[i * C] = o;
+                    if (valid) __builtin_nontemporal_store(o, op + i * C);
                     if (i + 1 < nb) push_row(s, wc, kb[i], vb[i]);
                 }
         }
