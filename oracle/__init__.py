@@ -52,6 +52,7 @@ def _load():
         lib.oracle_conv_rows.argtypes = [P, P, P, P, I, I, I, P, P]
         lib.oracle_scan.argtypes = [P, P, P, I, ctypes.c_long, P, P]
         lib.oracle_wkv4.argtypes = [P, P, P, P, I, I, P, P, P, P]
+        lib.oracle_wkv_tdecay.argtypes = [P, P, P, P, I, I, P, P, P, P]
         lib.oracle_gdn.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P]
         lib.oracle_unit_lower_inverse.argtypes = [P, I, I, P]
         lib.oracle_time_shift.argtypes = [P, P, P, I, I, I, P, P]
@@ -122,6 +123,20 @@ def wkv4(k, v, w, u, num, den, mx):
     assert v.shape == (S, C) and w.shape == (C,) and u.shape == (C,) and n.shape == (C,)
     out = np.empty((S, C))
     _load().oracle_wkv4(_p(k), _p(v), _p(w), _p(u), S, C, _p(n), _p(d), _p(m), _p(out))
+    return out, n, d, m
+
+
+def wkv_tdecay(k, v, w, u, num, den, mx):
+    """WKV token loop with a decay per row.  k, v, w [S, C]; u, num, den, mx [C].
+
+    Returns (wkv [S, C], num_S, den_S, max_S).
+    """
+    k, v, w, u = _f64(k), _f64(v), _f64(w), _f64(u)
+    S, C = k.shape
+    n, d, m = _f64(num).copy(), _f64(den).copy(), _f64(mx).copy()
+    assert v.shape == (S, C) and w.shape == (S, C) and u.shape == (C,) and n.shape == (C,)
+    out = np.empty((S, C))
+    _load().oracle_wkv_tdecay(_p(k), _p(v), _p(w), _p(u), S, C, _p(n), _p(d), _p(m), _p(out))
     return out, n, d, m
 
 

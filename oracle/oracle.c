@@ -150,6 +150,47 @@ void oracle_wkv4(const double* k, const double* v, const double* w, const double
 }
 
 /*
+ * WKV with a token-dependent decay ("perf(rwkv): ...", Notes For Future
+ * Readers: RWKV versions whose decay depends on the token need another chunk
+ * form).  The pages give no formula for those versions; the reading here is
+ * the RWKV-4 step above with the channel decay w replaced by a decay w_t of
+ * the row (w_t < 0), applied where the state moves past row t:
+ *   A_t = e^{w_t} A_{t-1} + e^{k_t} v_t,  B_t = e^{w_t} B_{t-1} + e^{k_t},
+ *   wkv_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t}),
+ * with the same shifts by the largest exponent (update: q = max(max + w_t, k_t)).
+ * A constant w_t = w is the RWKV-4 step.
+ *
+ * k, v, w, wkv: [S][C]; u: [C]; num, den, mx: [C], updated in place.
+ */
+void oracle_wkv_tdecay(const double* k, const double* v, const double* w, const double* u,
+                       int S, int C, double* num, double* den, double* mx, double* wkv) {
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < C; ++c) {
+        double aa = num[c], bb = den[c], pp = mx[c];
+        const double uc = u[c];
+        for (int t = 0; t < S; ++t) {
+            const size_t i = (size_t)t * C + c;
+            const double key = k[i], val = v[i], wt = w[i];
+            /* output of row t: state before the row plus the bonus term */
+            const double bonus = uc + key;
+            const double top = pp > bonus ? pp : bonus;
+            const double fs = exp(pp - top), fb = exp(bonus - top);
+            wkv[i] = (fs * aa + fb * val) / (fs * bb + fb);
+            /* state update with the row's decay e^{w_t} and the new key */
+            const double decayed = pp + wt;
+            const double q = decayed > key ? decayed : key;
+            const double gs = exp(decayed - q), gk = exp(key - q);
+            aa = gs * aa + gk * val;
+            bb = gs * bb + gk;
+            pp = q;
+        }
+        num[c] = aa;
+        den[c] = bb;
+        mx[c] = pp;
+    }
+}
+
+/*
  * Gated DeltaNet, one token at a time ("perf(qwen3_5): ...", Implementation).
  * The page gives the chunk form; its one-row case (A = 0, Gamma = e^{g_t})
  * is this step, for value head h with key head kh = h / (Hv / Hk):

@@ -17,6 +17,7 @@ import test_oracle_conv as T_conv
 import test_oracle_gdn as T_gdn
 import test_oracle_next as T_next
 import test_oracle_scan as T_scan
+import test_oracle_tdecay as T_td
 import test_oracle_wkv as T_wkv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -40,6 +41,13 @@ MUTATIONS = [
      [(T_wkv.test_wkv_matches_decimal_definition, {})]),
     ("wkv wrong max sign", "const double q = ed > kt ? ed : kt;", "const double q = ed < kt ? ed : kt;",
      [(T_wkv.test_wkv_matches_decimal_definition, {}), (T_wkv.test_wkv_finite_at_range_edges, {})]),
+    ("tdecay uses the previous row's decay", "const double key = k[i], val = v[i], wt = w[i];",
+     "const double key = k[i], val = v[i], wt = w[t > 0 ? i - (size_t)C : i];",
+     [(T_td.test_tdecay_matches_brute_force_sums, {})]),
+    ("tdecay update misses decay", "const double decayed = pp + wt;", "const double decayed = pp;",
+     [(T_td.test_tdecay_matches_brute_force_sums, {}), (T_td.test_tdecay_constant_decay_is_rwkv4, {})]),
+    ("tdecay bonus drops u", "const double bonus = uc + key;", "const double bonus = key;",
+     [(T_td.test_tdecay_matches_brute_force_sums, {}), (T_td.test_tdecay_zero_decay_is_a_running_mean, {})]),
     ("gdn prediction misses decay", "uvec[j] = bt * (vt[j] - dec * sk);", "uvec[j] = bt * (vt[j] - sk);",
      [(T_gdn.test_gdn_token_loop_equals_page_chunk_form, dict(splits=[7, 4]))]),
     ("gdn wrong key head", "const int kh = h / grp;", "const int kh = h % Hk;",
