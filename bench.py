@@ -294,8 +294,9 @@ MIXER_SLOTS_PER_STEP = 8
 
 def measure_next_rows(lrc, dev, lens, reps=10):
     """Time the rows beyond the step's hot path -- the RWKV-4 time shift (three mixed inputs at
-    the RWKV width) and the fused Mamba mixer rows (Mamba width) -- on the same prompt lengths,
-    from fresh states, with HIP events on the launch stream."""
+    the RWKV width), the fused Mamba mixer rows (Mamba width) and the WKV with a token-dependent
+    decay (RWKV width) -- on the same prompt lengths, from fresh states, with HIP events on the
+    launch stream."""
     import torch
 
     from linear_recurrence_chunked_amd import inputs
@@ -304,16 +305,22 @@ def measure_next_rows(lrc, dev, lens, reps=10):
     R, P = int(sum(lens)), len(lens)
     m = inputs.mixed_mamba_mixer(lens, dev)
     t = inputs.mixed_time_shift(lens, dev)
+    td = inputs.mixed_wkv_tdecay(lens, dev)
     Dm, N = sh["mamba_d_inner"], sh["mamba_d_state"]
     C, M = t["x"].shape[1], t["mix"].shape[0]
     y = torch.empty_like(m["x"])
     out = torch.empty((M, R, C), device=dev)
+    Ct = td["k"].shape[1]
+    tdo = torch.empty_like(td["k"])
     runs = {
         "time_shift": (lambda: lrc.time_shift_prefill(t["x"], out, t["state"], t["mix"], lens),
                        R * C * 4 * (1 + M) + P * C * 8 + M * C * 4, None),
         "mamba_mixer": (lambda: lrc.mamba_mixer_prefill(m["x"], m["dt"], m["A"], m["B"], m["C"], m["D"], y,
                                                         m["h0"], lens),
                         R * Dm * 12 + R * N * 8 + P * Dm * N * 8 + Dm * N * 4 + Dm * 4, R * Dm * N),
+        "wkv_tdecay": (lambda: lrc.wkv_tdecay_prefill(td["k"], td["v"], td["w"], td["u"], tdo, td["num"], td["den"],
+                                                      td["max"], lens),
+                       R * Ct * 16 + P * Ct * 24 + Ct * 4, None),
     }
     stream = torch.cuda.current_stream(dev)
     res = {}
@@ -337,7 +344,7 @@ def measure_next_rows(lrc, dev, lens, reps=10):
         else:
             d["bound"] = "hbm"
         res[name] = d
-    del m, t, y, out
+    del m, t, y, out, td, tdo
     return res
 
 

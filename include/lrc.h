@@ -231,6 +231,28 @@ lrc_status lrc_mamba_mixer_prefill(const float* x, const float* dt, const float*
                                    const float* Cm, const float* Dp, float* y, float* state,
                                    const int* lens_host, int P, int D, int N, void* stream);
 
+/* ------------------------------------------------------------------------
+ * WKV with a token-dependent decay.  [rwkv], Notes For Future Readers, says
+ * that RWKV versions whose decay depends on the token need another chunk
+ * form, and gives none; this is the reading that the RWKV-4 recurrence above
+ * takes a decay w_t per row and channel in place of w:
+ *   A_t = e^{w_t} A_{t-1} + e^{k_t} v_t,  B_t = e^{w_t} B_{t-1} + e^{k_t},
+ *   wkv_t = (A_{t-1} + e^{u+k_t} v_t) / (B_{t-1} + e^{u+k_t}).
+ * The state is the same (num, den, max) triple as for K2, and a decay that is
+ * the same on every row gives the K2 result.
+ *  k, v, w, wkv [B, S, C] float (w < 0)
+ *  u            [C] float
+ *  num, den, mx [B, C] float, read and updated in place
+ *  C >= 1, 0 <= S <= LRC_MAX_ROWS, B >= 0.  Errors: as for the other chunk calls.
+ * ---------------------------------------------------------------------- */
+lrc_status lrc_wkv_tdecay_rows(const float* k, const float* v, const float* w, const float* u, float* wkv,
+                               float* num, float* den, float* mx, int B, int S, int C, void* stream);
+
+/* Driver: k, v, w, wkv [R, C] packed rows; num, den, mx [P, C] in place. */
+lrc_status lrc_wkv_tdecay_prefill(const float* k, const float* v, const float* w, const float* u, float* wkv,
+                                  float* num, float* den, float* mx, const int* lens_host, int P, int C,
+                                  void* stream);
+
 /* ------------------------------------------------------------------------ */
 const char* lrc_status_string(lrc_status s);
 /* Detail of the last error on the calling thread ("" if none). */

@@ -150,6 +150,30 @@ lrc_status wkv_common(const float* k, const float* v, const float* w, const floa
     return LRC_OK;
 }
 
+// ---------------------------------------------------------------- WKV, token-dependent decay
+lrc_status wkv_td_common(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
+                         float* den, float* mx, long rows, int P, int C) {
+    REQUIRE_PTR_IF(k, rows > 0); REQUIRE_PTR_IF(v, rows > 0); REQUIRE_PTR_IF(w, rows > 0); REQUIRE_PTR(u);
+    REQUIRE_PTR_IF(wkv, rows > 0);
+    REQUIRE_PTR_IF(num, P > 0); REQUIRE_PTR_IF(den, P > 0); REQUIRE_PTR_IF(mx, P > 0);
+    REQUIRE(C >= 1, LRC_ERR_SHAPE, "channels %d < 1", C);
+    REQUIRE((uint64_t)rows * C < kMaxElems, LRC_ERR_SHAPE, "tensor too large");
+    REQUIRE_ALIGN(k); REQUIRE_ALIGN(v); REQUIRE_ALIGN(w); REQUIRE_ALIGN(u); REQUIRE_ALIGN(wkv);
+    REQUIRE_ALIGN(num); REQUIRE_ALIGN(den); REQUIRE_ALIGN(mx);
+    const uint64_t tb = (uint64_t)rows * C * 4, sb = (uint64_t)P * C * 4;
+    REQUIRE(!overlap(wkv, tb, k, tb) && !overlap(wkv, tb, v, tb) && !overlap(wkv, tb, w, tb), LRC_ERR_ALIAS,
+            "wkv overlaps k, v or w");
+    const float* st[3] = {num, den, mx};
+    for (int i = 0; i < 3; ++i) {
+        REQUIRE(!overlap(wkv, tb, st[i], sb), LRC_ERR_ALIAS, "wkv overlaps the state");
+        REQUIRE(!overlap(st[i], sb, k, tb) && !overlap(st[i], sb, v, tb) && !overlap(st[i], sb, w, tb),
+                LRC_ERR_ALIAS, "state overlaps k, v or w");
+        for (int j = i + 1; j < 3; ++j)
+            REQUIRE(!overlap(st[i], sb, st[j], sb), LRC_ERR_ALIAS, "num, den and max overlap each other");
+    }
+    return LRC_OK;
+}
+
 // ---------------------------------------------------------------- K3 gdn
 lrc_status gdn_common(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                       const float* S_in, float* S_out, long rows, int P, int Hk, int Hv, int dk, int dv,
@@ -291,6 +315,30 @@ lrc_status lrc_wkv4_prefill(const float* k, const float* v, const float* w, cons
     if ((s = wkv_common(k, v, w, u, wkv, num, den, mx, rows, P, C)) != LRC_OK) return s;
     auto st = static_cast<hipStream_t>(stream);
     return check_launch(lrc::launch_wkv4(k, v, w, u, wkv, num, den, mx, bt, C, st), st, "wkv4 prefill");
+}
+
+lrc_status lrc_wkv_tdecay_rows(const float* k, const float* v, const float* w, const float* u, float* wkv,
+                               float* num, float* den, float* mx, int B, int S, int C, void* stream) {
+    lrc::Batch bt;
+    lrc_status s = uniform_batch(B, S, bt);
+    if (s != LRC_OK) return s;
+    if ((s = wkv_td_common(k, v, w, u, wkv, num, den, mx, (long)B * S, B, C)) != LRC_OK) return s;
+    if (B == 0) return ok();
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_wkv_tdecay(k, v, w, u, wkv, num, den, mx, bt, C, st), st, "wkv tdecay");
+}
+
+lrc_status lrc_wkv_tdecay_prefill(const float* k, const float* v, const float* w, const float* u, float* wkv,
+                                  float* num, float* den, float* mx, const int* lens_host, int P, int C,
+                                  void* stream) {
+    thread_local lrc::Batch bt;
+    long rows = 0;
+    lrc_status s = packed_batch(lens_host, P, bt, rows);
+    if (s != LRC_OK) return s;
+    if ((s = wkv_td_common(k, v, w, u, wkv, num, den, mx, rows, P, C)) != LRC_OK) return s;
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_wkv_tdecay(k, v, w, u, wkv, num, den, mx, bt, C, st), st,
+                        "wkv tdecay prefill");
 }
 
 lrc_status lrc_gdn_chunk(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,

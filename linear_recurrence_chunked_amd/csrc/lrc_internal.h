@@ -39,6 +39,8 @@ hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0
                        long E, hipStream_t st);
 hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st);
+hipError_t launch_wkv_tdecay(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
+                             float* den, float* mx, const Batch& bt, int C, hipStream_t st);
 hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                       const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
                       lrc_dtype dt, hipStream_t st);

@@ -128,6 +128,20 @@ def rwkv_169m(seed: int | None = None, rows: int = 128, channels: int = 768 * 12
             "splits": [MAX_ROWS] * (rows // MAX_ROWS) + ([rows % MAX_ROWS] if rows % MAX_ROWS else [])}
 
 
+def rwkv_tdecay(seed: int | None = None, rows: int = 128, channels: int = 768 * 12, warmup: int = 32) -> dict:
+    """The RWKV-4 recipe above with a decay per row and channel: w_t = -exp(d_t),
+    d_t ~ U(-6, 2); the warm-up rows carry their own decays ``warm_w``."""
+    rng = np.random.default_rng(seed_for(8) if seed is None else seed)
+    u = rng.uniform(-2.0, 2.0, size=channels)
+    k = _rwkv_keys(rng, (rows, channels))
+    v = rng.standard_normal((rows, channels))
+    w = -np.exp(rng.uniform(-6.0, 2.0, size=(rows, channels)))
+    wk = _rwkv_keys(rng, (warmup, channels))
+    wv = rng.standard_normal((warmup, channels))
+    ww = -np.exp(rng.uniform(-6.0, 2.0, size=(warmup, channels)))
+    return {"k": _t(k), "v": _t(v), "w": _t(w), "u": _t(u), "warm_k": _t(wk), "warm_v": _t(wv), "warm_w": _t(ww)}
+
+
 # --------------------------------------------------------------------------
 # Gated DeltaNet small: 8 heads, dk = dv = 64, 75 rows (64 + 11).
 # --------------------------------------------------------------------------
@@ -292,6 +306,25 @@ def mixed_mamba_mixer(lens, device, seed: int | None = None, d_inner=5120, d_sta
         "D": torch.randn((d_inner,), **f),
         "h0": torch.zeros((P, d_inner, d_state), device=device, dtype=torch.float32),
     }
+
+
+def mixed_wkv_tdecay(lens, device, seed: int | None = None, channels=2560) -> dict:
+    """Packed rows of the token-dependent-decay WKV at the RWKV-4 width of the mixed workload:
+    the mixed RWKV-4 recipe with w_t = -exp(d_t), d_t ~ U(-6, 2) per row and channel (fresh state)."""
+    gen = _gen(device, (seed_for(5) if seed is None else seed) * 8 + 6)
+    R = int(sum(lens))
+    P = len(lens)
+    f = dict(device=device, dtype=torch.float32, generator=gen)
+    u = torch.rand((channels,), **f) * 4.0 - 2.0
+    k = torch.randn((R, channels), **f) * 3.0
+    spike = torch.rand((R, channels), **f) < 0.01
+    sign = torch.where(torch.rand((R, channels), **f) < 0.5, -1.0, 1.0)
+    k = torch.where(spike, sign * 30.0, k)
+    v = torch.randn((R, channels), **f)
+    w = -torch.exp(torch.rand((R, channels), **f) * 8.0 - 6.0)
+    return {"k": k, "v": v, "w": w, "u": u,
+            "num": torch.zeros((P, channels), device=device), "den": torch.zeros((P, channels), device=device),
+            "max": torch.full((P, channels), -1e38, device=device)}
 
 
 def mixed_time_shift(lens, device, seed: int | None = None, channels=2560, mixes=3) -> dict:

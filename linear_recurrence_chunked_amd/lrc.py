@@ -43,6 +43,8 @@ _SIGS = {
     "lrc_scan_prefill": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
     "lrc_wkv4_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "lrc_wkv4_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _P],
+    "lrc_wkv_tdecay_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
+    "lrc_wkv_tdecay_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _P],
     "lrc_gdn_chunk": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P],
     "lrc_gdn_prefill": [_P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _I, _I, _P],
     "lrc_unit_lower_inverse": [_P, _P, _I, _I, _P],
@@ -212,6 +214,36 @@ def wkv4_prefill(k, v, w, u, wkv, num, den, mx, lens):
         _need(t, torch.float32, (P, C), n)
     _check(lib.lrc_wkv4_prefill(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(wkv), _ptr(num), _ptr(den), _ptr(mx),
                                 arr, P, C, _stream(k)))
+
+
+# ------------------------------------------------------------------ WKV, token-dependent decay
+def wkv_tdecay_rows(k, v, w, u, wkv, num, den, mx):
+    """k, v, w, wkv [B, S, C] f32 (w: decay of each row); u [C]; num, den, mx [B, C] updated in place."""
+    _dev(k, v, w, u, wkv, num, den, mx)
+    B, S, C = k.shape
+    for t, n in ((k, "k"), (v, "v"), (w, "w"), (wkv, "wkv")):
+        _need(t, torch.float32, (B, S, C), n)
+    _need(u, torch.float32, (C,), "u")
+    for t, n in ((num, "num"), (den, "den"), (mx, "max")):
+        _need(t, torch.float32, (B, C), n)
+    _check(lib.lrc_wkv_tdecay_rows(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(wkv), _ptr(num), _ptr(den), _ptr(mx),
+                                   B, S, C, _stream(k)))
+
+
+def wkv_tdecay_prefill(k, v, w, u, wkv, num, den, mx, lens):
+    """k, v, w, wkv [R, C] packed rows; num, den, mx [P, C] updated in place."""
+    _dev(k, v, w, u, wkv, num, den, mx)
+    R, C = k.shape
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but k has {R} rows")
+    for t, n in ((k, "k"), (v, "v"), (w, "w"), (wkv, "wkv")):
+        _need(t, torch.float32, (R, C), n)
+    _need(u, torch.float32, (C,), "u")
+    for t, n in ((num, "num"), (den, "den"), (mx, "max")):
+        _need(t, torch.float32, (P, C), n)
+    _check(lib.lrc_wkv_tdecay_prefill(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(wkv), _ptr(num), _ptr(den),
+                                      _ptr(mx), arr, P, C, _stream(k)))
 
 
 # ------------------------------------------------------------------ K3 gdn

@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     for n in ["lrc_conv_rows", "lrc_conv_prefill", "lrc_scan_rows", "lrc_scan_prefill", "lrc_wkv4_rows",
               "lrc_wkv4_prefill", "lrc_gdn_chunk", "lrc_gdn_prefill", "lrc_unit_lower_inverse",
               "lrc_time_shift_rows", "lrc_time_shift_prefill", "lrc_mamba_mixer_rows", "lrc_mamba_mixer_prefill",
-              "lrc_status_string", "lrc_last_error", "lrc_version"]:
+              "lrc_wkv_tdecay_rows", "lrc_wkv_tdecay_prefill", "lrc_status_string", "lrc_last_error", "lrc_version"]:
         assert n in names
 
 
@@ -102,6 +102,18 @@ def test_wkv_rejects(L):
     assert _st(L, f(A0, A1, A2, A3, A4, A5, A5, A7, 1, 8, 8, None)) == "LRC_ERR_ALIAS"
     assert _st(L, f(A0, A1, A2, A3, A4, A5, A6, None, 1, 8, 8, None)) == "LRC_ERR_NULL"
     assert _st(L, f(A0, A1, A2, A3, A4, A5, A6, A7, 1, 8, 0, None)) == "LRC_ERR_SHAPE"
+
+
+def test_wkv_tdecay_rejects(L):
+    f = L.lib.lrc_wkv_tdecay_rows
+    assert _st(L, f(A0, A1, A2, A3, A4, A5, A6, A7, 1, 65, 8, None)) == "LRC_ERR_ROWS"
+    assert _st(L, f(A0, A1, A2, A3, A2, A5, A6, A7, 1, 8, 8, None)) == "LRC_ERR_ALIAS"  # wkv over the decays
+    assert _st(L, f(A0, A1, A2, A3, A4, A5, A6, A2, 1, 8, 8, None)) == "LRC_ERR_ALIAS"  # state over the decays
+    assert _st(L, f(A0, A1, None, A3, A4, A5, A6, A7, 1, 8, 8, None)) == "LRC_ERR_NULL"
+    assert _st(L, f(A0, A1, MIS, A3, A4, A5, A6, A7, 1, 8, 8, None)) == "LRC_ERR_ALIGN"
+    assert _st(L, f(A0, A1, A2, A3, A4, A5, A6, A7, 1, 8, 0, None)) == "LRC_ERR_SHAPE"
+    lens = (ctypes.c_int * 2)(8, -1)
+    assert _st(L, L.lib.lrc_wkv_tdecay_prefill(A0, A1, A2, A3, A4, A5, A6, A7, lens, 2, 8, None)) == "LRC_ERR_ROWS"
 
 
 def test_gdn_rejects(L):
