@@ -194,8 +194,17 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool is_state = w < NS;
     const int pw = w - NS;  // prep wave index
-    const int h = blockIdx.x;
-    const int kh = h / (Hv / Hk);
+    // The value heads of one key head read the same K and Q rows.  Workgroups
+    // are dealt to the 8 XCDs in launch order, so heads that are 8 workgroups
+    // apart share an XCD and its L2: the G = Hv/Hk siblings of a key head are
+    // placed 8 apart, and the second read of each K, Q row is an L2 hit.
+    const int G = Hv / Hk;
+    int h = blockIdx.x;
+    if (G > 1 && Hv % (8 * G) == 0) {
+        const int r = h % (8 * G);
+        h = h - r + (r % 8) * G + r / 8;
+    }
+    const int kh = h / G;
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
