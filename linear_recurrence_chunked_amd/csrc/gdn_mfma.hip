@@ -101,6 +101,14 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
     }
 }
 
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+// Raw buffer resource over `bytes` bytes from p (stride 0, 32-bit data
+// format): a load past the end returns 0 and a store past it is dropped.
+// The range check covers the per-lane offset only, so row offsets go there.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
 // Scheduling hint for an unrolled run of N steps that each read R fragments
 // from LDS and issue M products: the reads run AHEAD steps ahead of the
 // products, so that the waits before the products are partial.
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            // rows past the chunk hold a copy of its last row of V; beta is 0 there
+                            // rows past the chunk read V as zero; beta is 0 there as well
                             const float vv = c ? __uint_as_float(pv[4 * t + r] & 0xffff0000u)
                                                : __uint_as_float(pv[4 * t + r] << 16);
                             ks0[c][t][r] = b4[r] * (vv - G4[r] * ks0[c][t][r]);
@@ -339,17 +347,21 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     }
                 }
                 read_ahead<6, 2, 3 * CG, 2>();
-                float* oc = o + (row0 + 64 * n) * (long)rowV + (long)h * dv + col0;
-                uint32_t o_lane = __umul24(lq, rowV) + 2 * lr;
+                // Through a buffer resource that ends after the chunk's Sn rows: the
+                // stores of rows past it are dropped, with no per-row test.
+                const auto orsrc = chunk_rsrc(o + (row0 + 64 * n) * (long)rowV + (long)h * dv + col0,
+                                              (uint32_t)Sn * rowV * 4);
+                uint32_t o_lane = (__umul24(lq, rowV) + 2 * lr) * 4;
                 asm volatile("" : "+v"(o_lane));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[rb][16 * t + lq]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (16 * t + lq + r < Sn)
-                            *reinterpret_cast<float2*>(&oc[o_lane + (16 * t + r) * rowV]) =
-                                float2{fmaf(G4[r], qs0[0][t][r], pu[0][t][r]), fmaf(G4[r], qs0[1][t][r], pu[1][t][r])};
+                    for (int r = 0; r < 4; ++r) {
+                        const u32x2 pair = {__float_as_uint(fmaf(G4[r], qs0[0][t][r], pu[0][t][r])),
+                                            __float_as_uint(fmaf(G4[r], qs0[1][t][r], pu[1][t][r]))};
+                        __builtin_amdgcn_raw_buffer_store_b64(pair, orsrc, o_lane + (16 * t + r) * rowV * 4, 0, 0);
+                    }
                 }
             }
             __syncthreads();
@@ -385,17 +397,18 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 read_ahead<2 * RT, 2, 2 * CG, 2>();
             }
             if (do_next) {
-                // Rows past the chunk re-read its last row and are zeroed where V is used.
+                // Through a buffer resource that ends after the chunk's S rows: rows
+                // past it read as zero (beta is zero there too).
                 const int c0 = 64 * (n + 1), S = min(64, L - c0);
-                const uint16_t* vc = v + (row0 + c0) * (long)rowV + (long)h * dv + col0;
-                int v_lane = 2 * lr, v_q = lq;
-                asm volatile("" : "+v"(v_lane), "+v"(v_q));
+                const auto vrsrc = chunk_rsrc(v + (row0 + c0) * (long)rowV + (long)h * dv + col0,
+                                              (uint32_t)S * rowV * 2);
+                uint32_t v_lane = (__umul24(lq, rowV) + 2 * lr) * 2;
+                asm volatile("" : "+v"(v_lane));
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        pv[4 * t + r] = *reinterpret_cast<const uint32_t*>(
-                            &vc[__umul24(min(16 * t + v_q + r, S - 1), rowV) + v_lane]);
+                        pv[4 * t + r] = __builtin_amdgcn_raw_buffer_load_b32(vrsrc, v_lane + (16 * t + r) * rowV * 2, 0, 0);
             }
             __syncthreads();
 
