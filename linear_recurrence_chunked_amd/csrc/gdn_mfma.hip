@@ -104,12 +104,6 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-// Raw buffer resource over `bytes` bytes from p (stride 0, 32-bit data
-// format): a load past the end returns 0 and a store past it is dropped.
-// The range check covers the per-lane offset only, so row offsets go there.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
 
 // Scheduling hint for an unrolled run of N steps that each read R fragments
 // from LDS and issue M products: the reads run AHEAD steps ahead of the
@@ -351,7 +345,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 read_ahead<6, 2, 3 * CG, 2>();
                 // Through a buffer resource that ends after the chunk's Sn rows: the
                 // stores of rows past it are dropped, with no per-row test.
-                const auto orsrc = chunk_rsrc(o + (row0 + 64 * n) * (long)rowV + (long)h * dv + col0,
+                const auto orsrc = buffer_rsrc(o + (row0 + 64 * n) * (long)rowV + (long)h * dv + col0,
                                               (uint32_t)Sn * rowV * 4);
                 uint32_t o_lane = (__umul24(lq, rowV) + 2 * lr) * 4;
                 asm volatile("" : "+v"(o_lane));
@@ -402,7 +396,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 // Through a buffer resource that ends after the chunk's S rows: rows
                 // past it read as zero (beta is zero there too).
                 const int c0 = 64 * (n + 1), S = min(64, L - c0);
-                const auto vrsrc = chunk_rsrc(v + (row0 + c0) * (long)rowV + (long)h * dv + col0,
+                const auto vrsrc = buffer_rsrc(v + (row0 + c0) * (long)rowV + (long)h * dv + col0,
                                               (uint32_t)S * rowV * 2);
                 uint32_t v_lane = (__umul24(lq, rowV) + 2 * lr) * 2;
                 asm volatile("" : "+v"(v_lane));

@@ -48,6 +48,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return uint16_t(u >> 16);
 }
 
+// Raw buffer resource over `bytes` bytes from p (stride 0, 32-bit data
+// format, the gfx9 descriptor word).  Loads whose per-lane offset lies past
+// the end return 0 and such stores are dropped; the scalar offset is not part
+// of that check, so only uniform offsets that stay in range go there.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNontemporal = 2;  // cache-policy argument of the buffer builtins: streaming access
+
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 

@@ -144,25 +144,29 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
     const long sidx = (long)p * C + cl;
     const float wc = w[cl], uc = u[cl];
     WkvState carry{num[sidx], den[sidx], mx[sidx], 0.f};
-    const float* kp = k + row0 * C + cl;
-    const float* vp = v + row0 * C + cl;
 
     float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R];  // ring of row buffers
     // Loads are issued unconditionally (rows past the prompt re-read its last
     // row) so that the compiler can count them and wait only for the chunk
     // about to be used, not for the one being prefetched.  k, v and the
     // output are touched once: their accesses are nontemporal (streaming).
-    // Row offsets within a chunk are 32-bit (64 rows x C); the base moves per chunk.
+    // R rows x C channels of a buffer resource stay below 2^31 bytes.
+    // The rows go through buffer resources based at the wave's first row: the
+    // row offsets are uniform and ride in the scalar offset, the channel
+    // offset is the same for every row, so no address is formed per load.
+    const uint32_t lane_off = (uint32_t)(cl - blockIdx.x * 64) * 4;
+    const float* k0 = k + row0 * C + blockIdx.x * 64;  // the workgroup's first channel of the prompt's row 0
+    const float* v0 = v + row0 * C + blockIdx.x * 64;
     auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R]) {
         const int r0 = min(c0 + R * wv, L - 1);
-        const float* kc = kp + (long)r0 * C;
-        const float* vc = vp + (long)r0 * C;
+        const auto krs = buffer_rsrc(k0 + (long)r0 * C, (uint32_t)R * C * 4);
+        const auto vrs = buffer_rsrc(v0 + (long)r0 * C, (uint32_t)R * C * 4);
         const int last = L - 1 - r0;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const int off = min(i, last) * C;
-            kb[i] = __builtin_nontemporal_load(kc + off);
-            vb[i] = __builtin_nontemporal_load(vc + off);
+            const int soff = min(i, last) * C * 4;
+            kb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(krs, lane_off, soff, kNontemporal));
+            vb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vrs, lane_off, soff, kNontemporal));
         }
     };
     int buf = 0;
@@ -199,12 +203,14 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
             carry = e;
         }
         buf ^= 1;
-        float* op = wkv + (row0 + c0 + R * wv) * C + cl;
+        // lanes past C store at an offset past the resource's end: dropped
+        const auto ors = buffer_rsrc(wkv + (row0 + c0 + R * wv) * C + blockIdx.x * 64, (uint32_t)R * C * 4);
+        const uint32_t st_off = valid ? lane_off : 0x80000000u;
         if (nb == R) {  // full block: straight-line code
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const float o = out_row(s, wc, uc, kb[i], vb[i]);
-                if (valid) __builtin_nontemporal_store(o, op + i * C);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ors, st_off, i * C * 4, kNontemporal);
                 if (i + 1 < R) push_row(s, wc, kb[i], vb[i]);
             }
         } else if (nb > 0) {
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
             for (int i = 0; i < R; ++i)
                 if (i < nb) {
                     const float o = out_row(s, wc, uc, kb[i], vb[i]);
-                    if (valid) __builtin_nontemporal_store(o, op + i * C);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ors, st_off, i * C * 4, kNontemporal);
                     if (i + 1 < nb) push_row(s, wc, kb[i], vb[i]);
                 }
         }

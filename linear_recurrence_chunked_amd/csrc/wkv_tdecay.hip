@@ -138,9 +138,14 @@ __global__ __launch_bounds__(NW * 64) void wkv_tdecay_kernel(const float* __rest
     const long sidx = (long)p * C + cl;
     const float uc = u[cl];
     TdState carry{num[sidx], den[sidx], (double)mx[sidx]};
-    const float* kp = k + row0 * C + cl;
-    const float* vp = v + row0 * C + cl;
-    const float* wp = w + row0 * C + cl;
+    // Rows go through buffer resources based at the workgroup's first channel
+    // and the wave's first row: row offsets are uniform (scalar offset), the
+    // channel offset is the same for every row, so no address is formed per
+    // access.  R rows x C channels of a resource stay below 2^31 bytes.
+    const uint32_t lane_off = (uint32_t)(cl - blockIdx.x * 64) * 4;
+    const float* k0 = k + row0 * C + blockIdx.x * 64;
+    const float* v0 = v + row0 * C + blockIdx.x * 64;
+    const float* w0 = w + row0 * C + blockIdx.x * 64;
 
     float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R], wb_[DEPTH + 1][R];  // ring of row buffers
     // Loads are issued unconditionally (rows past the prompt re-read its last
@@ -148,14 +153,16 @@ __global__ __launch_bounds__(NW * 64) void wkv_tdecay_kernel(const float* __rest
     // the output are touched once, so their accesses are nontemporal.
     auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R], float (&wb)[R]) {
         const int r0 = min(c0 + R * wv, L - 1);
-        const long base = (long)r0 * C;
+        const auto krs = buffer_rsrc(k0 + (long)r0 * C, (uint32_t)R * C * 4);
+        const auto vrs = buffer_rsrc(v0 + (long)r0 * C, (uint32_t)R * C * 4);
+        const auto wrs = buffer_rsrc(w0 + (long)r0 * C, (uint32_t)R * C * 4);
         const int last = L - 1 - r0;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const int off = min(i, last) * C;
-            kb[i] = __builtin_nontemporal_load(kp + base + off);
-            vb[i] = __builtin_nontemporal_load(vp + base + off);
-            wb[i] = __builtin_nontemporal_load(wp + base + off);
+            const int soff = min(i, last) * C * 4;
+            kb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(krs, lane_off, soff, kNontemporal));
+            vb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vrs, lane_off, soff, kNontemporal));
+            wb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wrs, lane_off, soff, kNontemporal));
         }
     };
     int buf = 0;
@@ -193,12 +200,14 @@ __global__ __launch_bounds__(NW * 64) void wkv_tdecay_kernel(const float* __rest
             carry = e;
         }
         buf ^= 1;
-        float* op = wkv + (row0 + c0 + R * wv) * C + cl;
+        // lanes past C store at an offset past the resource's end: dropped
+        const auto ors = buffer_rsrc(wkv + (row0 + c0 + R * wv) * C + blockIdx.x * 64, (uint32_t)R * C * 4);
+        const uint32_t st_off = valid ? lane_off : 0x80000000u;
 #pragma unroll
         for (int i = 0; i < R; ++i)
             if (i < nb) {
                 const float o = out_row(s, uc, kb[i], vb[i]);
-                if (valid) __builtin_nontemporal_store(o, op + i * C);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ors, st_off, i * C * 4, kNontemporal);
                 if (i + 1 < nb) push_row(s, wb[i], kb[i], vb[i]);
             }
     };
