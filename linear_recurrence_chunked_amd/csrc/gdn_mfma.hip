@@ -175,6 +175,44 @@ __device__ __forceinline__ void split_tile(const float* M, __bf16* hi, __bf16* l
     *reinterpret_cast<bf16x4*>(&lo[r * L64 + c]) = l;
 }
 
+// Masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M: tile
+// pairs first, first + stride, ... (NP of them; pairs past the last one are
+// computed but not stored).
+template <int DK, int NP>
+__device__ __forceinline__ void masked_kk(PipeSmem<DK>& sm, int b, int rbuf, int first, int stride) {
+    constexpr int LDK = PipeSmem<DK>::LDK;
+    constexpr int KS = DK / 32;
+    int tid_c = threadIdx.x;
+    asm volatile("" : "+v"(tid_c));
+    const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
+    floatx4 kk[NP];
+#pragma unroll
+    for (int x = 0; x < NP; ++x) kk[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int x = 0; x < NP; ++x) {
+            int ti, tj;
+            tile_pair(min(first + x * stride, 9), ti, tj);
+            kk[x] = mfma(frag(&sm.K[b][(16 * tj + lr) * LDK + 32 * s + lk]),
+                         frag(&sm.K[b][(16 * ti + lr) * LDK + 32 * s + lk]), kk[x]);
+        }
+    read_ahead<KS * NP, 2, 1, (NP < 3 ? NP : 3)>();
+#pragma unroll
+    for (int x = 0; x < NP; ++x)
+        if (first + x * stride < 10) {
+            int ti, tj;
+            tile_pair(first + x * stride, ti, tj);
+            const floatx4 dec = tile_decay(sm.gam[rbuf], ti, tj, lr, lq);
+            const int i = 16 * ti + lr;
+            const float bi = sm.beta[rbuf][i];
+            floatx4 av;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) av[r] = i > 16 * tj + lq + r ? bi * dec[r] * kk[x][r] : 0.f;
+            *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
+        }
+}
+
 // Grid (value heads, prompts); NS = dv / 32 state waves, then kPrep prep waves.
 template <int DK, int NS>
 __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const uint16_t* __restrict__ q,
@@ -408,7 +446,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             }
             __syncthreads();
 
-            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks
+            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks; tile pairs 8, 9 of A of chunk n+2
+            if (n + 2 < nc && w < 2) masked_kk<DK, (NS == 1 ? 2 : 1)>(sm, cb, (n + 5) % 3, 8 + w, NS);
             if (do_next) {
                 for (int b = tid; b < 2 * DK; b += 64 * NS) {
                     const int nn = b & 15, m = b >> 4;  // rows 4nn .. 4nn+3, columns 8m .. 8m+7
@@ -486,40 +525,6 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 sm.decS[rbuf][lane] = lane < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
             }
         };
-        // masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M, by tile pairs
-        auto masked_kk = [&](int b, int rbuf) {
-            int tid_c = tid;
-            asm volatile("" : "+v"(tid_c));
-            const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
-            constexpr int PPW = (10 + kPrep - 1) / kPrep;
-            floatx4 kk[PPW];
-#pragma unroll
-            for (int x = 0; x < PPW; ++x) kk[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int x = 0; x < PPW; ++x) {
-                    int ti, tj;
-                    tile_pair(min(pw + x * kPrep, 9), ti, tj);  // past the last pair: computed, not stored
-                    kk[x] = mfma(frag(&sm.K[b][(16 * tj + lr) * LDK + 32 * s + lk]),
-                                 frag(&sm.K[b][(16 * ti + lr) * LDK + 32 * s + lk]), kk[x]);
-                }
-            read_ahead<KS * PPW, 2, 1, 3>();
-#pragma unroll
-            for (int x = 0; x < PPW; ++x)
-                if (pw + x * kPrep < 10) {
-                    int ti, tj;
-                        tile_pair(pw + x * kPrep, ti, tj);
-                    const floatx4 dec = tile_decay(sm.gam[rbuf], ti, tj, lr, lq);
-                    const int i = 16 * ti + lr;
-                    const float bi = sm.beta[rbuf][i];
-                    floatx4 av;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) av[r] = i > 16 * tj + lq + r ? bi * dec[r] * kk[x][r] : 0.f;
-                    *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
-                }
-        };
-
         // masked decayed Q K^T of the chunk in buffers (b, rbuf) -> P as hi/lo, transposed (keys as rows)
         auto masked_qk = [&](int b, int rbuf) {
             int tid_c = tid;
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         }
         if (nc > 1) fetch(64);
         __syncthreads();  // prologue: chunk 0 staged
-        if (nc > 0) masked_kk(0, 0);
+        if (nc > 0) masked_kk<DK, 3>(sm, 0, 0, pw, kPrep);
         __syncthreads();  // prologue: A of chunk 0 in M
 
         for (int n = -1; n < nc; ++n) {
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             __syncthreads();
 
             // ---- E: A of chunk n+2 into M (T of chunk n+1 is in hi/lo now)
-            if (do_stage) masked_kk(n & 1, (n + 5) % 3);
+            if (do_stage) masked_kk<DK, 2>(sm, n & 1, (n + 5) % 3, pw, kPrep);  // tile pairs 0 .. 7
             __syncthreads();
         }
     }
