@@ -579,20 +579,21 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (do_next) tri::diag<kPrep>(sm.M, sm.scratch, pw);
             __syncthreads();
 
-            // ---- B: level 16; chunk n+2 into the buffers chunk n used, chunk n+3 in flight
+            // ---- B: level 16
             if (do_next) tri::lvl16<kPrep>(sm.M, pw);
-            if (do_stage) {
-                stage(64 * (n + 2), n & 1, (n + 5) % 3);
-                if (n + 3 < nc) fetch(64 * (n + 3));
-            }
             __syncthreads();
 
-            // ---- C: level 32 (first half); the tiles of T that are final go to hi/lo
+            // ---- C: level 32 (first half); the tiles of T that are final go to hi/lo;
+            //      chunk n+2 into the buffers chunk n used, chunk n+3 in flight
             if (do_next) {
                 tri::lvl32a<kPrep>(sm.M, sm.scratch, pw);
                 split_tile(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
                 if (pw == 0) split_tile(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
                 if (pw == 1) split_tile(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
+            }
+            if (do_stage) {
+                stage(64 * (n + 2), n & 1, (n + 5) % 3);
+                if (n + 3 < nc) fetch(64 * (n + 3));
             }
             __syncthreads();
 
