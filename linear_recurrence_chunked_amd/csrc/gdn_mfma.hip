@@ -17,15 +17,16 @@
 //    accumulators for the whole prompt.  In step n they run the chain that
 //    depends on the state for chunk n: K S_0, Q S_0 and the right-hand side
 //    (A), U (B), O (C), the state update and the loads of V of chunk n+1 (D),
-//    and they build K^T of chunk n+1 (E).  A lane's two 16-column groups are
+//    and they build K^T of chunk n+1 and two tile pairs of chunk n+2's A (E).  A lane's two 16-column groups are
 //    the even and the odd columns of the wave's 32, so that V, O and the
 //    state move as column pairs.  V and O go through buffer resources that
 //    end after the chunk's rows, so rows past it need no test.
 //  * 4 prep waves, which in step n prepare chunk n+1, the part that does not
 //    depend on the state: the inverse (diagonal tiles in A, level 16 in B,
 //    level 32 in C and D, each tile of T split to hi/lo bf16 once final) and
-//    the masked decayed Q K^T (D); they stage chunk n+2 into LDS (B) and form
-//    its masked K K^T (E), and keep the rows of chunk n+3 in flight.
+//    the masked decayed Q K^T (D); they stage chunk n+2 into LDS (C) and form
+//    the rest of its masked K K^T (E), and keep the rows of chunk n+3 in
+//    flight.
 // LDS holds K and Q of two chunks (by chunk parity), the per-row gamma,
 // Gamma, beta and state-update decay of three, and one copy of A -> T (FP32),
 // T and P (hi/lo bf16) and K^T: each is written in a segment where no wave
