@@ -105,6 +105,7 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
 }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Scheduling hint for an unrolled run of N steps that each read R fragments
 // from LDS and issue M products: the reads run AHEAD steps ahead of the
@@ -486,42 +487,45 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         const int pt = tid - 64 * NS;  // thread index among the prep waves
         uint4 pf[NF];                  // K and Q rows of a chunk, in flight to LDS
         float pg = 0.f, pb = 0.f;      // its g and beta (last prep wave)
+        // Rows of a chunk through buffer resources that end after its S rows:
+        // rows past it read as zero.  The piece offsets are a per-lane part and
+        // a per-slot constant.  PT is a multiple of 2 PK / NF, so every slot is
+        // all K or all Q.
+        static_assert((2 * PK) % PT == 0, "every prep thread loads the same number of pieces");
+        const uint32_t kq_lane = (__umul24(pt / (DK / 8), rowK) + (pt % (DK / 8)) * 8) * 2;
         auto fetch = [&](int c0) {
             const int S = min(64, L - c0);
-            const uint16_t* kc = k + ((row0 + c0) * Hk + kh) * (long)DK;
-            const uint16_t* qc = q + ((row0 + c0) * Hk + kh) * (long)DK;
+            const auto krs = buffer_rsrc(k + ((row0 + c0) * Hk + kh) * (long)DK, (uint32_t)S * rowK * 2);
+            const auto qrs = buffer_rsrc(q + ((row0 + c0) * Hk + kh) * (long)DK, (uint32_t)S * rowK * 2);
 #pragma unroll
             for (int x = 0; x < NF; ++x) {
-                const int e = min(pt + x * PT, 2 * PK - 1);
-                const bool isq = e >= PK;
-                const int ee = isq ? e - PK : e, r = ee / (DK / 8), c8 = (ee % (DK / 8)) * 8;
-                const uint32_t off = __umul24(min(r, S - 1), rowK) + c8;
-                pf[x] = *reinterpret_cast<const uint4*>((isq ? qc : kc) + off);
+                const bool isq = x * PT >= PK;
+                const uint32_t slot = (uint32_t)((x * PT - (isq ? PK : 0)) / (DK / 8)) * rowK * 2;
+                const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(isq ? qrs : krs, kq_lane + slot, 0, 0);
+                pf[x] = make_uint4(d[0], d[1], d[2], d[3]);
             }
             if (pw == kPrep - 1) {
-                const long gi = (row0 + c0) * Hv + h + __umul24(min(lane, S - 1), Hv);
-                pg = g[gi];
-                pb = beta[gi];
+                const auto grs = buffer_rsrc(g + (row0 + c0) * Hv + h, (uint32_t)S * Hv * 4);
+                const auto brs = buffer_rsrc(beta + (row0 + c0) * Hv + h, (uint32_t)S * Hv * 4);
+                pg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, __umul24(lane, Hv) * 4, 0, 0));
+                pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, __umul24(lane, Hv) * 4, 0, 0));
             }
         };
-        // Rows past the chunk are written as zeros; gamma stays flat there.
+        // Rows past the chunk arrive as zeros; gamma stays flat there.
         auto stage = [&](int c0, int b, int rbuf) {
             const int S = min(64, L - c0);
 #pragma unroll
             for (int x = 0; x < NF; ++x) {
                 const int e = pt + x * PT;
-                if (e < 2 * PK) {
-                    const bool isq = e >= PK;
-                    const int ee = isq ? e - PK : e, r = ee / (DK / 8), c8 = (ee % (DK / 8)) * 8;
-                    const uint4 val = r < S ? pf[x] : make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4*>(&(isq ? sm.Q[b] : sm.K[b])[r * LDK + c8]) = val;
-                }
+                const bool isq = x * PT >= PK;
+                const int ee = isq ? e - PK : e, r = ee / (DK / 8), c8 = (ee % (DK / 8)) * 8;
+                *reinterpret_cast<uint4*>(&(isq ? sm.Q[b] : sm.K[b])[r * LDK + c8]) = pf[x];
             }
             if (pw == kPrep - 1) {
-                const float x = wave_prefix_sum(lane < S ? pg : 0.f);  // gamma, inclusive over the chunk rows
+                const float x = wave_prefix_sum(pg);  // gamma, inclusive over the chunk rows
                 sm.gam[rbuf][lane] = x;
                 sm.Gam[rbuf][lane] = fast_exp(x);
-                sm.beta[rbuf][lane] = lane < S ? pb : 0.f;
+                sm.beta[rbuf][lane] = pb;
                 const float gS = readlane_f(x, S - 1);  // the last cumulative sum
                 sm.decS[rbuf][lane] = lane < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
             }
