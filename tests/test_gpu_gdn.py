@@ -141,6 +141,39 @@ def test_gdn_ragged_batch(L, orc, dk, dv, Hk, Hv):
         r += n
 
 
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(32, 32, 8, 16), (64, 32, 16, 64), (32, 64, 12, 24), (32, 32, 4, 4),
+                                         (64, 128, 2, 32), (32, 32, 8, 128)])
+def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv):
+    """The bf16 matrix-core path over ragged prompts with value-head groups of 1, 2, 4 and 16.
+    Groups whose value heads fill whole multiples of 8 groups are placed so that siblings share
+    an XCD; the others keep the plain order: both must give every head its own key head."""
+    rng = np.random.default_rng(900 + dk + dv + Hk + Hv)
+    lens = [1, 64, 0, 65, 130, 7]
+    R, P = sum(lens), len(lens)
+    q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((R, Hv, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((R, Hv))))
+    g = -np.logaddexp(0, rng.standard_normal((R, Hv))) * 0.5
+    S0 = rng.normal(0, 0.1, (P, Hv, dk, dv))
+    t = {n: torch.from_numpy(a).float() for n, a in dict(beta=beta, g=g, S0=S0).items()}
+    for n, a in dict(q=q, k=k, v=v).items():
+        t[n] = torch.from_numpy(a).to(torch.bfloat16)
+    dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+    o = torch.full((R, Hv, dv), float("nan"), device="cuda")
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+    torch.cuda.synchronize()
+    r = 0
+    for p, n in enumerate(lens):
+        sl = slice(r, r + n)
+        ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
+                               f64(t["g"][sl]), f64(t["S0"][p]))
+        if n:
+            assert rel_err(f64(o[sl]), ref_o) < TOL_BF16
+        assert rel_err(f64(dS[p]), ref_s) < TOL_BF16
+        r += n
+
+
 def test_gdn_rejects_65_rows(L):
     q = torch.randn(1, 65, 1, 32, device="cuda")
     v = torch.randn(1, 65, 1, 32, device="cuda")
