@@ -285,13 +285,10 @@ hipError_t launch_f32_path(const void* q, const void* k, const void* v, const fl
                            const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dv, hipStream_t st) {
     auto kern = gdn_f32_kernel<TIN, DK, DVT>;
     const size_t smem = sizeof(GdnSmem<DK, DVT>);
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    // Opt in to more than 64 KiB of LDS once per process (a thread-safe static).
+    static const hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (configured != hipSuccess) return configured;
     const dim3 grid((unsigned)(Hv * (dv / DVT)), (unsigned)bt.P);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, static_cast<const TIN*>(q), static_cast<const TIN*>(k),
                        static_cast<const TIN*>(v), beta, g, o, S_in, S_out, bt, Hk, Hv, dv);

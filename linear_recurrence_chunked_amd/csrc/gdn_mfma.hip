@@ -623,13 +623,10 @@ hipError_t launch_pipe(const void* q, const void* k, const void* v, const float*
                        const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dv, hipStream_t st) {
     auto kern = gdn_pipe_kernel<DK, NS>;
     const size_t smem = sizeof(PipeSmem<DK>);
-    static bool configured = false;
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    // Opt in to more than 64 KiB of LDS once per process (a thread-safe static).
+    static const hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (configured != hipSuccess) return configured;
     const dim3 grid((unsigned)Hv, (unsigned)bt.P);
     hipLaunchKernelGGL(kern, grid, dim3(64 * (NS + kPrep)), smem, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, g, o, S_in, S_out, bt,
