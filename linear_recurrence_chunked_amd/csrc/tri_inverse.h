@@ -34,7 +34,7 @@
 namespace lrc {
 
 constexpr int kTriLd = 68;            // row stride of the 64x64 matrix in LDS (floats), 16-byte aligned rows
-constexpr int kTriScratch = 4 * 16 * 20;  // floats: four 16x20 tiles, later the 32x36 level-32 product
+constexpr int kTriScratch = 32 * 36;  // floats: the 32x36 level-32 product
 
 typedef float tri_f4 __attribute__((ext_vector_type(4)));
 
@@ -90,14 +90,13 @@ __device__ __forceinline__ void lanes(int& lr, int& g) {
 }
 
 template <int NW>
-__device__ inline void diag(float* M, float* scratch, int w) {
+__device__ inline void diag(float* M, float* /*scratch*/, int w) {
     constexpr int ld = kTriLd;
     int lr, g;
     lanes(lr, g);
     const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int t = w; t < 4; t += NW) {
         float* Mt = M + 16 * t * ld + 16 * t;
-        float* S = scratch + t * 16 * 20;
         tri_f4 nrow = ld_row(Mt, ld, lr, g), nacc = ld_acc(Mt, ld, lr, g);
         tri_f4 lorow = nrow;
 #pragma unroll
@@ -110,23 +109,26 @@ __device__ inline void diag(float* M, float* scratch, int w) {
             nrow[k] = in_row ? nrow[k] : 0.f;
             nacc[k] = in_acc ? nacc[k] : 0.f;
         }
-        const tri_f4 n2 = mm(zero, nrow, nacc);   // N^2
-        const tri_f4 nn2 = mm(zero, nrow, n2);    // N N^2
-        st_acc(S, 20, lr, g, n2);
-        wave_sync();
-        const tri_f4 n4 = mm(zero, ld_row(S, 20, lr, g), n2);  // N^4
-        tri_f4 x;                                               // (I - N)(I + N^2)
+        // Every product that is needed again as a row operand is also formed
+        // in row layout, as the transposed product: mm(Y_acc, X_row) is
+        // (X Y)^T in accumulator layout, i.e. X Y in row layout.  That trades
+        // the LDS round trips of a layout change for three more products.
+        const tri_f4 n2 = mm(zero, nrow, nacc);     // N^2
+        const tri_f4 n2r = mm(zero, nacc, nrow);    // N^2, row layout
+        const tri_f4 nn2 = mm(zero, nrow, n2);      // N N^2
+        const tri_f4 nn2r = mm(zero, n2, nrow);     // N N^2, row layout
+        const tri_f4 n4 = mm(zero, n2r, n2);        // N^4
+        tri_f4 x, xr;                               // (I - N)(I + N^2), both layouts
 #pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = (4 * g + k == lr ? 1.f : 0.f) - nacc[k] + n2[k] - nn2[k];
-        wave_sync();
-        st_acc(S, 20, lr, g, x);
-        wave_sync();
-        const tri_f4 d = x + mm(zero, ld_row(S, 20, lr, g), n4);  // D = X (I + N^4)
-        const tri_f4 y = mm(zero, lorow, d);                       // L D
-        wave_sync();
-        st_acc(S, 20, lr, g, d);
-        wave_sync();
-        const tri_f4 z = mm(zero, ld_row(S, 20, lr, g), y);       // D L D
+        for (int k = 0; k < 4; ++k) {
+            const float id = 4 * g + k == lr ? 1.f : 0.f;
+            x[k] = id - nacc[k] + n2[k] - nn2[k];
+            xr[k] = id - nrow[k] + n2r[k] - nn2r[k];
+        }
+        const tri_f4 d = x + mm(zero, xr, n4);     // D = X (I + N^4)
+        const tri_f4 dr = xr + mm(zero, n4, xr);   // D, row layout
+        const tri_f4 y = mm(zero, lorow, d);       // L D
+        const tri_f4 z = mm(zero, dr, y);          // D L D
         st_acc(Mt, ld, lr, g, d - z);
     }
 }
