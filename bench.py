@@ -137,6 +137,25 @@ def measure_copy_gbps(dev, nbytes=4 << 30, reps=5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def measure_add_gbps(dev, nbytes=2 << 30, reps=5):
+    """Bandwidth of torch's elementwise add c = a + b (two reads per write, the scan's mix; GB/s)."""
+    import torch
+
+    a = torch.empty(nbytes // 4, device=dev)
+    b, c = torch.empty_like(a), torch.empty_like(a)
+    torch.add(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.add(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 3 * nbytes / (ms * 1e-3) / 1e9
+
+
 def run_kernel(lrc, W, name):
     lens = W["lens"]
     if name == "conv_mamba":
@@ -449,6 +468,7 @@ def main():
         nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
     dom = max(kernels, key=lambda k: per_k[k])
     copy_gbps = measure_copy_gbps(dev)
+    add_gbps = measure_add_gbps(dev)
     if dom == "gdn":
         roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": kern[dom]["mfma_bf16_frac"], "traffic": stored_traffic(dom),
@@ -456,9 +476,11 @@ def main():
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kern[dom]["hbm_frac"], "traffic": stored_traffic(dom),
-                "algorithmic_per_launch": work[dom]["bytes"], "frac_of_measured_copy": kern[dom]["GBps"] / copy_gbps}
+                "algorithmic_per_launch": work[dom]["bytes"], "frac_of_measured_copy": kern[dom]["GBps"] / copy_gbps,
+                "frac_of_measured_add": kern[dom]["GBps"] / add_gbps}
     roof["avg_launch_ms"] = per_k[dom]
     roof["measured_copy_GBps"] = copy_gbps
+    roof["measured_add_GBps"] = add_gbps
 
     out = {
         "metric": "prefill rows/s per kernel at 1 GPU; % HBM or MFMA peak; max rel err vs oracle",

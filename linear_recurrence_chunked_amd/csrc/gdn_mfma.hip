@@ -52,6 +52,10 @@
 // e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
 // The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) runs in
 // FP32 on the FP32 matrix cores.
+#include <algorithm>
+#include <cstddef>
+#include <cstring>
+
 #include "lrc_device.h"
 #include "lrc_internal.h"
 #include "tri_inverse.h"
@@ -137,6 +141,46 @@ struct PipeSmem {
     float Gam[3][64];       // e^gamma
     float beta[3][64];
     float decS[3][64];      // e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
+    alignas(16) int meta[4][4];  // by chunk index mod 4: its first row, its rows, its prompt
+};
+static_assert(offsetof(PipeSmem<128>, meta) % 16 == 0 && offsetof(PipeSmem<32>, meta) % 16 == 0,
+              "a chunk's record is written as one 16-byte store");
+
+// Which prompts a workgroup row runs.  With n == 0, row y runs the prompt in
+// slot y of the batch order alone; otherwise row y is a lane that runs slots
+// off[y] .. off[y+1]-1 one after the other.
+struct GdnLanes {
+    int n;
+    unsigned short off[LRC_MAX_PROMPTS + 1];
+};
+
+// A lane's chunks are those of its prompts in slot order (slots up to i1),
+// prompts without rows skipped.  The cursor names one of them: slot i, prompt
+// p, the chunk's first row, and the end of the prompt's rows.  All of it is
+// uniform across the workgroup.  Past the lane's last chunk it names an empty
+// chunk.
+struct ChunkCursor {
+    int i, p, row, end;
+    __device__ void enter(const Batch& bt, int i1) {  // the first prompt with rows from slot i on
+        for (; i < i1; ++i) {
+            p = batch_prompt(bt, i);
+            const int L = batch_len(bt, p);
+            if (L > 0) {
+                row = batch_row0(bt, p);
+                end = row + L;
+                return;
+            }
+        }
+        row = end = 0;
+    }
+    __device__ void next(const Batch& bt, int i1) {
+        row += 64;
+        if (row >= end) {
+            ++i;
+            enter(bt, i1);
+        }
+    }
+    __device__ int rows() const { return min(64, end - row); }
 };
 
 // Lower-triangular 16x16 tile pair pr = 0 .. 9 (query tile ti, key tile tj) of
@@ -223,8 +267,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                                                                         const float* __restrict__ beta,
                                                                         const float* __restrict__ g,
                                                                         float* __restrict__ o, const float* S_in,
-                                                                        float* S_out, Batch bt, int Hk, int Hv,
-                                                                        int dv) {
+                                                                        float* S_out, Batch bt, GdnLanes lanes,
+                                                                        int Hk, int Hv, int dv) {
     static_assert(CG == 2, "a lane's column pair is one even and one odd column");
     using Sm = PipeSmem<DK>;
     constexpr int LDK = Sm::LDK;
@@ -249,10 +293,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         h = h - r + (r % 8) * G + r / 8;
     }
     const int kh = h / G;
-    const int p = batch_prompt(bt, blockIdx.y);
-    const long row0 = batch_row0(bt, p);
-    const int L = batch_len(bt, p);
-    const int nc = (L + 63) / 64;
+    const int i0 = lanes.n ? lanes.off[blockIdx.y] : blockIdx.y;
+    const int i1 = lanes.n ? lanes.off[blockIdx.y + 1] : blockIdx.y + 1;
+    int nc = 0;  // chunks of the lane
+    for (int i = i0; i < i1; ++i) nc += (batch_len(bt, batch_prompt(bt, i)) + 63) >> 6;
     const uint32_t rowK = Hk * DK, rowV = Hv * dv;
     if (is_state) {
         // ================= state waves: chunk n, 32 state columns each
@@ -262,16 +306,47 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         const int col0 = 32 * w;
         int s_lane = (lane >> 4) * 4 * dv + 2 * (lane & 15);
         asm volatile("" : "+v"(s_lane));
-        const long sbase = ((long)p * Hv + h) * DK * dv + col0;
         floatx4 sacc[CG][RT];
+        // The state block of prompt p through a buffer resource; the row
+        // offsets are formed where they are used, not kept across the loop.
+        auto state_rsrc = [&](const float* base, int p) {
+            return buffer_rsrc(base + ((long)p * Hv + h) * DK * dv + col0, (uint32_t)(DK * dv * 4));
+        };
+        auto load_state = [&](int p) {
+            const auto rs = state_rsrc(S_in, p);
+            int sl = s_lane * 4, dv4 = dv * 4;
+            asm volatile("" : "+v"(sl), "+s"(dv4));
 #pragma unroll
-        for (int tr = 0; tr < RT; ++tr)
+            for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float2 x = *reinterpret_cast<const float2*>(&S_in[sbase + s_lane + (long)(16 * tr + r) * dv]);
-                sacc[0][tr][r] = x.x;
-                sacc[1][tr][r] = x.y;
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, sl, (16 * tr + r) * dv4, 0);
+                    sacc[0][tr][r] = __uint_as_float(x[0]);
+                    sacc[1][tr][r] = __uint_as_float(x[1]);
+                }
+        };
+        auto store_state = [&](int p) {
+            const auto rs = state_rsrc(S_out, p);
+            int sl = s_lane * 4, dv4 = dv * 4;
+            asm volatile("" : "+v"(sl), "+s"(dv4));
+#pragma unroll
+            for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{__float_as_uint(sacc[0][tr][r]), __float_as_uint(sacc[1][tr][r])}, rs, sl,
+                        (16 * tr + r) * dv4, 0);
+        };
+        // Where a chunk's rows are and which prompt it belongs to, as the prep
+        // waves recorded it when they fetched the chunk.
+        auto meta = [&](int j, int f) { return __builtin_amdgcn_readfirstlane(sm.meta[j & 3][f]); };
+        ChunkCursor first{i0};
+        first.enter(bt, i1);
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+            for (int tr = 0; tr < RT; ++tr) sacc[c][tr] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (nc > 0) load_state(first.p);
         // V of the next chunk in accumulator layout: rows 16t + 4(l/16) + r, both columns of the lane
         uint32_t pv[16];
 #pragma unroll
@@ -283,7 +358,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             const int cb = n & 1, nb = cb ^ 1;  // K/Q buffers of chunks n, n+1
             const int rb = (n + 3) % 3;         // row buffer of chunk n
             const bool do_state = n >= 0, do_next = n + 1 < nc;
-            const int Sn = min(64, L - 64 * n);
+            int Sn = 0;
             int tid_c = tid;
             asm volatile("" : "+v"(tid_c));
             const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lq = lg * 4;
@@ -385,7 +460,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 read_ahead<6, 2, 3 * CG, 2>();
                 // Through a buffer resource that ends after the chunk's Sn rows: the
                 // stores of rows past it are dropped, with no per-row test.
-                const auto orsrc = buffer_rsrc(o + (row0 + 64 * n) * (long)rowV + (long)h * dv + col0,
+                Sn = meta(n, 1);
+                const auto orsrc = buffer_rsrc(o + meta(n, 0) * (long)rowV + (long)h * dv + col0,
                                               (uint32_t)Sn * rowV * 4);
                 uint32_t o_lane = (__umul24(lq, rowV) + 2 * lr) * 4;
                 asm volatile("" : "+v"(o_lane));
@@ -435,8 +511,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (do_next) {
                 // Through a buffer resource that ends after the chunk's S rows: rows
                 // past it read as zero (beta is zero there too).
-                const int c0 = 64 * (n + 1), S = min(64, L - c0);
-                const auto vrsrc = buffer_rsrc(v + (row0 + c0) * (long)rowV + (long)h * dv + col0,
+                const int S = meta(n + 1, 1);
+                const auto vrsrc = buffer_rsrc(v + meta(n + 1, 0) * (long)rowV + (long)h * dv + col0,
                                               (uint32_t)S * rowV * 2);
                 uint32_t v_lane = (__umul24(lq, rowV) + 2 * lr) * 2;
                 asm volatile("" : "+v"(v_lane));
@@ -448,7 +524,15 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             }
             __syncthreads();
 
-            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks; tile pairs 8, 9 of A of chunk n+2
+            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks; tile pairs 8, 9 of A of chunk n+2;
+            //      after a prompt's last chunk, its state goes out and the next prompt's comes in
+            if (do_state) {
+                const int pn = meta(n, 2), pnext = do_next ? meta(n + 1, 2) : -1;
+                if (pnext != pn) {
+                    store_state(pn);
+                    if (do_next) load_state(pnext);
+                }
+            }
             if (n + 2 < nc && w < 2) masked_kk<DK, (NS == 1 ? 2 : 1)>(sm, cb, (n + 5) % 3, 8 + w, NS);
             if (do_next) {
                 for (int b = tid; b < 2 * DK; b += 64 * NS) {
@@ -473,13 +557,15 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             }
             __syncthreads();
         }
-        asm volatile("" : "+v"(s_lane));
-#pragma unroll
-        for (int tr = 0; tr < RT; ++tr)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<float2*>(&S_out[sbase + s_lane + (long)(16 * tr + r) * dv]) =
-                    float2{sacc[0][tr][r], sacc[1][tr][r]};
+        // Prompts without rows keep their state.
+        if (S_in != S_out)
+            for (int i = i0; i < i1; ++i) {
+                const int p = batch_prompt(bt, i);
+                if (batch_len(bt, p) == 0) {
+                    load_state(p);
+                    store_state(p);
+                }
+            }
     } else {
         // ================= prep waves: inverse of chunk n+1, staging of chunk n+2, A of chunk n+2
         constexpr int PT = 64 * kPrep;
@@ -493,10 +579,14 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         // all K or all Q.
         static_assert((2 * PK) % PT == 0, "every prep thread loads the same number of pieces");
         const uint32_t kq_lane = (__umul24(pt / (DK / 8), rowK) + (pt % (DK / 8)) * 8) * 2;
-        auto fetch = [&](int c0) {
-            const int S = min(64, L - c0);
-            const auto krs = buffer_rsrc(k + ((row0 + c0) * Hk + kh) * (long)DK, (uint32_t)S * rowK * 2);
-            const auto qrs = buffer_rsrc(q + ((row0 + c0) * Hk + kh) * (long)DK, (uint32_t)S * rowK * 2);
+        ChunkCursor fc{i0};    // the next chunk to fetch
+        fc.enter(bt, i1);
+        int fetched_rows = 0;  // rows of the chunk in pf
+        auto fetch = [&](int j) {  // chunk j of the lane
+            const int S = fc.rows();
+            const long r0 = fc.row;
+            const auto krs = buffer_rsrc(k + (r0 * Hk + kh) * (long)DK, (uint32_t)S * rowK * 2);
+            const auto qrs = buffer_rsrc(q + (r0 * Hk + kh) * (long)DK, (uint32_t)S * rowK * 2);
 #pragma unroll
             for (int x = 0; x < NF; ++x) {
                 const bool isq = x * PT >= PK;
@@ -505,15 +595,18 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 pf[x] = make_uint4(d[0], d[1], d[2], d[3]);
             }
             if (pw == kPrep - 1) {
-                const auto grs = buffer_rsrc(g + (row0 + c0) * Hv + h, (uint32_t)S * Hv * 4);
-                const auto brs = buffer_rsrc(beta + (row0 + c0) * Hv + h, (uint32_t)S * Hv * 4);
+                const auto grs = buffer_rsrc(g + r0 * Hv + h, (uint32_t)S * Hv * 4);
+                const auto brs = buffer_rsrc(beta + r0 * Hv + h, (uint32_t)S * Hv * 4);
                 pg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, __umul24(lane, Hv) * 4, 0, 0));
                 pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, __umul24(lane, Hv) * 4, 0, 0));
             }
+            if (pw == kPrep - 1 && lane == 0) *reinterpret_cast<int4*>(sm.meta[j & 3]) = make_int4(fc.row, S, fc.p, 0);
+            fetched_rows = S;
+            fc.next(bt, i1);
         };
         // Rows past the chunk arrive as zeros; gamma stays flat there.
-        auto stage = [&](int c0, int b, int rbuf) {
-            const int S = min(64, L - c0);
+        auto stage = [&](int b, int rbuf) {
+            const int S = fetched_rows;
 #pragma unroll
             for (int x = 0; x < NF; ++x) {
                 const int e = pt + x * PT;
@@ -569,9 +662,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             sm.T_hi[e] = sm.T_lo[e] = sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
         if (nc > 0) {
             fetch(0);
-            stage(0, 0, 0);
+            stage(0, 0);
         }
-        if (nc > 1) fetch(64);
+        if (nc > 1) fetch(1);
         __syncthreads();  // prologue: chunk 0 staged
         if (nc > 0) masked_kk<DK, 3>(sm, 0, 0, pw, kPrep);
         __syncthreads();  // prologue: A of chunk 0 in M
@@ -597,8 +690,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 if (pw == 1) split_tile(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
             }
             if (do_stage) {
-                stage(64 * (n + 2), n & 1, (n + 5) % 3);
-                if (n + 3 < nc) fetch(64 * (n + 3));
+                stage(n & 1, (n + 5) % 3);
+                if (n + 3 < nc) fetch(n + 3);
             }
             __syncthreads();
 
@@ -618,6 +711,150 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
     }
 }
 
+// ---------------------------------------------------------------- lanes (host)
+// A workgroup needs most of a CU's LDS, so a CU runs one at a time.  When the
+// prompts' workgroups outnumber the CUs, the hardware starts each waiting
+// workgroup on the first CU that frees up, and a short prompt can land behind
+// a long one.  Instead the launch runs at most one row of Hv workgroups per
+// group of Hv CUs, as lanes: each lane runs a set of prompts back to back, its
+// chunks flowing through one pipeline.  The sets are chosen so that the
+// largest lane (in chunks, plus a little per prompt for the state reload) is
+// as small as the search below finds.
+
+struct LanePlanner {
+    int n = 0, k = 0, lb = 0, best_ms = 0;
+    long nodes = 0, limit = 0;
+    int cost[LRC_MAX_PROMPTS], item[LRC_MAX_PROMPTS], suffix[LRC_MAX_PROMPTS + 1];
+    int load[LRC_MAX_PROMPTS], lane_of[LRC_MAX_PROMPTS], best[LRC_MAX_PROMPTS];
+
+    // Longest first, each to the least loaded lane: the starting bound.
+    void greedy() {
+        for (int j = 0; j < k; ++j) load[j] = 0;
+        for (int t = 0; t < n; ++t) {
+            int j = 0;
+            for (int x = 1; x < k; ++x)
+                if (load[x] < load[j]) j = x;
+            load[j] += cost[item[t]];
+            best[item[t]] = j;
+        }
+        best_ms = 0;
+        for (int j = 0; j < k; ++j) best_ms = std::max(best_ms, load[j]);
+        for (int j = 0; j < k; ++j) load[j] = 0;
+    }
+    // Depth first over the items in decreasing cost, each tried in the lanes
+    // of the few smallest distinct current loads that keep it below the best
+    // found so far; a node budget bounds the search.
+    void search(int t) {
+        if (best_ms <= lb || nodes >= limit) return;
+        ++nodes;
+        if (t == n) {
+            int ms = 0;
+            for (int j = 0; j < k; ++j) ms = std::max(ms, load[j]);
+            if (ms < best_ms) {
+                best_ms = ms;
+                for (int x = 0; x < n; ++x) best[item[x]] = lane_of[item[x]];
+            }
+            return;
+        }
+        long room = 0;
+        for (int j = 0; j < k; ++j) room += std::max(0, best_ms - 1 - load[j]);
+        if (room < suffix[t]) return;
+        const int c = cost[item[t]];
+        // the lanes of the kBranch smallest distinct loads, in increasing load
+        constexpr int kBranch = 4;
+        int by[kBranch], nb = 0;
+        for (int j = 0; j < k; ++j) {
+            bool dup = false;
+            for (int x = 0; x < nb && !dup; ++x) dup = load[by[x]] == load[j];
+            if (dup) continue;
+            int x = nb < kBranch ? nb++ : kBranch;
+            for (; x > 0 && load[by[x - 1]] > load[j]; --x)
+                if (x < kBranch) by[x] = by[x - 1];
+            if (x < kBranch) by[x] = j;
+        }
+        for (int x = 0; x < nb; ++x) {
+            const int j = by[x];
+            if (load[j] + c >= best_ms) break;
+            load[j] += c;
+            lane_of[item[t]] = j;
+            search(t + 1);
+            load[j] -= c;
+            if (best_ms <= lb || nodes >= limit) return;
+        }
+    }
+};
+
+// Fills lanes.off and a copy of the batch whose order lists the lanes' slots
+// back to back.  Prompts without rows go to lane 0 (they only copy state).
+void plan_lanes(const Batch& bt, int k, Batch& out, GdnLanes& lanes) {
+    LanePlanner pl;
+    pl.k = k;
+    long total = 0;
+    int empty[LRC_MAX_PROMPTS], ne = 0;
+    for (int s = 0; s < bt.P; ++s) {
+        const int p = batch_prompt(bt, s), L = batch_len(bt, p);
+        if (L == 0) {
+            empty[ne++] = p;
+            continue;
+        }
+        pl.cost[p] = 4 * ((L + 63) / 64) + 1;
+        pl.item[pl.n++] = p;  // the batch order is by decreasing length already
+        total += pl.cost[p];
+    }
+    pl.suffix[pl.n] = 0;
+    for (int t = pl.n - 1; t >= 0; --t) pl.suffix[t] = pl.suffix[t + 1] + pl.cost[pl.item[t]];
+    pl.lb = std::max(pl.n ? pl.cost[pl.item[0]] : 0, (int)((total + k - 1) / k));
+    pl.greedy();
+    pl.limit = std::min(2048, std::max(16, 8192 / k));  // a node costs a few k steps
+    pl.search(0);
+    out = bt;
+    lanes.n = k;
+    int s = 0;
+    for (int j = 0; j < k; ++j) {
+        lanes.off[j] = (unsigned short)s;
+        for (int t = 0; t < pl.n; ++t)
+            if (pl.best[pl.item[t]] == j) out.order[s++] = pl.item[t];
+        if (j == 0)
+            for (int x = 0; x < ne; ++x) out.order[s++] = empty[x];
+    }
+    lanes.off[k] = (unsigned short)s;
+}
+
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+// The lanes of a packed batch (n == 0: one prompt per workgroup row).  The
+// last plan is kept per host thread and reused for the same lengths.
+void lanes_for(const Batch& bt, int Hv, Batch& run, GdnLanes& lanes) {
+    lanes.n = 0;
+    run = bt;
+    if (bt.uniform >= 0 || bt.P < 2) return;
+    const int k = compute_units() / Hv;
+    if (k < 1 || k >= bt.P) return;
+    thread_local struct {
+        int P = -1, k = 0;
+        int row_off[LRC_MAX_PROMPTS + 1];
+        Batch run;
+        GdnLanes lanes;
+    } memo;
+    if (memo.P == bt.P && memo.k == k &&
+        std::memcmp(memo.row_off, bt.row_off, sizeof(int) * (bt.P + 1)) == 0) {
+        run = memo.run;
+        lanes = memo.lanes;
+        return;
+    }
+    plan_lanes(bt, k, run, lanes);
+    memo.P = bt.P;
+    memo.k = k;
+    std::memcpy(memo.row_off, bt.row_off, sizeof(int) * (bt.P + 1));
+    memo.run = run;
+    memo.lanes = lanes;
+}
+
 template <int DK, int NS>
 hipError_t launch_pipe(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                        const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dv, hipStream_t st) {
@@ -627,10 +864,13 @@ hipError_t launch_pipe(const void* q, const void* k, const void* v, const float*
     static const hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (configured != hipSuccess) return configured;
-    const dim3 grid((unsigned)Hv, (unsigned)bt.P);
+    Batch run;
+    GdnLanes lanes;
+    lanes_for(bt, Hv, run, lanes);
+    const dim3 grid((unsigned)Hv, (unsigned)(lanes.n ? lanes.n : bt.P));
     hipLaunchKernelGGL(kern, grid, dim3(64 * (NS + kPrep)), smem, st, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, g, o, S_in, S_out, bt,
-                       Hk, Hv, dv);
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, g, o, S_in, S_out, run,
+                       lanes, Hk, Hv, dv);
     return hipGetLastError();
 }
 

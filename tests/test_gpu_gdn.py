@@ -174,6 +174,45 @@ def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv):
         r += n
 
 
+@pytest.mark.parametrize("dk,dv", [(32, 32), (128, 128)])
+def test_gdn_bf16_lanes(L, orc, dk, dv):
+    """16 value-head pairs of 16 key heads over 16 ragged prompts: more workgroups than compute
+    units, so the prompts run as lanes, several per workgroup row, with chunks of different
+    prompts back to back in one pipeline and the state swapped at each prompt boundary."""
+    Hk, Hv = 16, 32
+    lens = [300, 0, 64, 65, 1, 257, 130, 190, 17, 128, 45, 99, 200, 33, 70, 150]
+    R, P = sum(lens), len(lens)
+    assert P * Hv > torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(910 + dk)
+    q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((R, Hv, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((R, Hv))))
+    g = -np.logaddexp(0, rng.standard_normal((R, Hv))) * 0.5
+    S0 = rng.normal(0, 0.1, (P, Hv, dk, dv))
+    t = {n: torch.from_numpy(a).float() for n, a in dict(beta=beta, g=g, S0=S0).items()}
+    for n, a in dict(q=q, k=k, v=v).items():
+        t[n] = torch.from_numpy(a).to(torch.bfloat16)
+    dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+    o = torch.full((R, Hv, dv), float("nan"), device="cuda")
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+    torch.cuda.synchronize()
+    first = (o.clone(), dS.clone())
+    dS.copy_(to_dev(t["S0"]))
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)  # same lengths again: the kept plan
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], o) and torch.equal(first[1], dS)
+    r = 0
+    for p, n in enumerate(lens):
+        sl = slice(r, r + n)
+        ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
+                               f64(t["g"][sl]), f64(t["S0"][p]))
+        if n:
+            assert rel_err(f64(o[sl]), ref_o) < TOL_BF16
+        assert rel_err(f64(dS[p]), ref_s) < TOL_BF16
+        r += n
+
+
 def test_gdn_rejects_65_rows(L):
     q = torch.randn(1, 65, 1, 32, device="cuda")
     v = torch.randn(1, 65, 1, 32, device="cuda")
