@@ -10,16 +10,18 @@
 //   S_S  = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
 // gamma_S is the last entry of the same cumulative sum.
 //
-// Work split.  One workgroup owns a whole value head of one prompt and walks
-// its chunks.  It holds two kinds of waves, which run the same sequence of
+// Work split.  One workgroup owns a whole value head of one prompt, or of a
+// lane of prompts run back to back (see the launcher), and walks their
+// chunks.  It holds two kinds of waves, which run the same sequence of
 // workgroup barriers, five per step (segments A .. E):
 //  * dv/32 state waves, each owning 32 columns of the [dk x dv] state in MFMA
-//    accumulators for the whole prompt.  In step n they run the chain that
-//    depends on the state for chunk n: K S_0, Q S_0 and the right-hand side
-//    (A), U (B), O (C), the state update and the loads of V of chunk n+1 (D),
-//    and they build K^T of chunk n+1 and two tile pairs of chunk n+2's A (E).  A lane's two 16-column groups are
-//    the even and the odd columns of the wave's 32, so that V, O and the
-//    state move as column pairs.  V and O go through buffer resources that
+//    accumulators, swapped at each prompt boundary.  In step n they run the
+//    chain that depends on the state for chunk n: K S_0, Q S_0 and the
+//    right-hand side (A), U (B), O (C), the state update and the loads of V
+//    of chunk n+1 (D), and they build K^T of chunk n+1 and two tile pairs of
+//    chunk n+2's A (E).  A lane's two 16-column groups are the even and the
+//    odd columns of the wave's 32, so that V, O and the state move as column
+//    pairs.  V, O and the state go through buffer resources; those of V and O
 //    end after the chunk's rows, so rows past it need no test.
 //  * 4 prep waves, which in step n prepare chunk n+1, the part that does not
 //    depend on the state: the inverse (diagonal tiles in A, level 16 in B,
@@ -28,7 +30,8 @@
 //    the rest of its masked K K^T (E), and keep the rows of chunk n+3 in
 //    flight.
 // LDS holds K and Q of two chunks (by chunk parity), the per-row gamma,
-// Gamma, beta and state-update decay of three, and one copy of A -> T (FP32),
+// Gamma, beta and state-update decay of three, where the rows of four are
+// and which prompt they belong to, and one copy of A -> T (FP32),
 // T and P (hi/lo bf16) and K^T: each is written in a segment where no wave
 // reads the copy it replaces.  About 147 KiB, one workgroup per CU.
 //
@@ -600,7 +603,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 pg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, __umul24(lane, Hv) * 4, 0, 0));
                 pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, __umul24(lane, Hv) * 4, 0, 0));
             }
-            if (pw == kPrep - 1 && lane == 0) *reinterpret_cast<int4*>(sm.meta[j & 3]) = make_int4(fc.row, S, fc.p, 0);
+            if (pw == kPrep - 1 && lane == 0)
+                *reinterpret_cast<int4*>(sm.meta[j & 3]) = make_int4(fc.row, S, fc.p, 0);
             fetched_rows = S;
             fc.next(bt, i1);
         };
