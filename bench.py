@@ -53,7 +53,7 @@ def parse():
 def make_workload(dev):
     import torch
 
-    from linear_recurrence_chunked_amd import inputs
+    from linear_recurrence_chunked_amd import inputs, lrc
 
     lens = inputs.mixed_lengths()
     sh = inputs.MIXED_SHAPES
@@ -68,6 +68,8 @@ def make_workload(dev):
         "xm": m["conv_x"], "ym": torch.empty_like(m["conv_x"]), "sm": m["conv_state"], "wm": m["conv_w"],
         "a": m["a"].view(R, D, N), "b": m["b"].view(R, D, N), "h": torch.empty((R, D, N), device=dev),
         "hs": m["h0"].view(len(lens), D, N),
+        # the tiled scan's completion flags (zero-filled once, reused by every step)
+        "scan_ws": torch.zeros(lrc.scan_workspace_size(len(lens), D, N), dtype=torch.uint8, device=dev),
         # RWKV-4
         "k": r["k"], "v": r["v"], "w": r["w"], "u": r["u"], "wkv": torch.empty_like(r["k"]),
         "num": r["num"], "den": r["den"], "max": r["max"],
@@ -161,7 +163,7 @@ def run_kernel(lrc, W, name):
     if name == "conv_mamba":
         lrc.conv_prefill(W["xm"], W["ym"], W["sm"], W["wm"], lens)
     elif name == "scan":
-        lrc.scan_prefill(W["a"], W["b"], W["h"], W["hs"], lens)
+        lrc.scan_prefill_ws(W["a"], W["b"], W["h"], W["hs"], lens, W["scan_ws"])
     elif name == "wkv4":
         lrc.wkv4_prefill(W["k"], W["v"], W["w"], W["u"], W["wkv"], W["num"], W["den"], W["max"], lens)
     elif name == "conv_gdn":

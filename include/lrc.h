@@ -119,6 +119,30 @@ lrc_status lrc_scan_rows(const float* a, const float* b, float* h, const float* 
 lrc_status lrc_scan_prefill(const float* a, const float* b, float* h, float* state,
                             const int* lens_host, int P, int D, int N, void* stream);
 
+/* K1 driver, tiled form [mamba]: the same result as lrc_scan_prefill, bit for
+ * bit (every chunk is the same doubling scan with the carried state applied
+ * last).  The work is cut into tiles of (chunk, block of 128 state elements),
+ * handed out in row order to persistent workgroups, instead of one workgroup
+ * walking all chunks of a (prompt, block).  A tile takes its carry, the
+ * previous chunk's last h row, from h once that chunk's tile has flagged it,
+ * so the tiles in flight at any moment read whole rows together.
+ *
+ *  workspace        device memory of at least lrc_scan_workspace_size(P, D, N)
+ *                   bytes, 16-byte aligned, owned by the caller.  It must be
+ *                   zero-filled before its first use; the library never needs
+ *                   it cleared again (every call tags its flags with a new
+ *                   generation).  Calls that may run at the same time must not
+ *                   share a workspace.
+ *  The workspace begins with a 32-bit count of hand-overs that timed out
+ *  (about 0.2 s each; the flags follow at byte 256); it stays 0 unless
+ *  workgroups of one launch could not all make progress.  Returns LRC_ERR_SHAPE if the workspace
+ *  is too small or the launch would need 2^31 workgroups or more.  With
+ *  D * N not a multiple of 4 it runs the lrc_scan_prefill kernel. */
+size_t lrc_scan_workspace_size(int P, int D, int N);
+lrc_status lrc_scan_prefill_ws(const float* a, const float* b, float* h, float* state,
+                               const int* lens_host, int P, int D, int N,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * K2  RWKV-4 WKV over rows  [rwkv]
  *

@@ -295,6 +295,33 @@ lrc_status lrc_scan_prefill(const float* a, const float* b, float* h, float* sta
     return check_launch(lrc::launch_scan(a, b, h, state, state, bt, (long)D * N, st), st, "scan prefill");
 }
 
+size_t lrc_scan_workspace_size(int P, int D, int N) {
+    if (P < 1 || D < 1 || N < 1) return 0;
+    return lrc::scan_workspace_bytes(P, (long)D * N);
+}
+
+lrc_status lrc_scan_prefill_ws(const float* a, const float* b, float* h, float* state, const int* lens_host, int P,
+                               int D, int N, void* workspace, size_t workspace_bytes, void* stream) {
+    thread_local lrc::Batch bt;
+    long rows = 0;
+    lrc_status s = packed_batch(lens_host, P, bt, rows);
+    if (s != LRC_OK) return s;
+    if ((s = scan_common(a, b, h, state, state, rows, P, D, N)) != LRC_OK) return s;
+    const long E = (long)D * N;
+    const size_t need = lrc::scan_workspace_bytes(P, E);
+    REQUIRE_PTR(workspace);
+    REQUIRE(aligned16(workspace), LRC_ERR_ALIGN, "workspace is not 16-byte aligned");
+    REQUIRE(workspace_bytes >= need, LRC_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const uint64_t tb = (uint64_t)rows * E * 4, sb = (uint64_t)P * E * 4;
+    REQUIRE(!overlap(workspace, need, a, tb) && !overlap(workspace, need, b, tb) && !overlap(workspace, need, h, tb) &&
+                !overlap(workspace, need, state, sb),
+            LRC_ERR_ALIAS, "workspace overlaps a tensor");
+    REQUIRE((uint64_t)(rows / 64 + P) * (uint64_t)((E + 255) / 256) < (1ull << 31), LRC_ERR_SHAPE,
+            "too many tiles for one launch");
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_scan_tiled(a, b, h, state, bt, E, workspace, st), st, "scan prefill (tiled)");
+}
+
 lrc_status lrc_wkv4_rows(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                          float* den, float* mx, int B, int S, int C, void* stream) {
     lrc::Batch bt;

@@ -37,6 +37,9 @@ hipError_t launch_conv(const void* x, void* y, const void* state_in, void* state
                        const float* bias, const Batch& bt, int C, int K, lrc_dtype dt, hipStream_t st);
 hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt,
                        long E, hipStream_t st);
+size_t scan_workspace_bytes(int P, long E);
+hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
+                             void* workspace, hipStream_t st);
 hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st);
 hipError_t launch_wkv_tdecay(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,

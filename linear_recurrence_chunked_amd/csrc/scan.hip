@@ -28,6 +28,9 @@
 //  3. h_t = A_t h0 + B_t; the new carried state is read from lane S-1; the
 //     h column goes back to LDS and leaves as row-contiguous 16-byte stores.
 //  The row loads and stores are nontemporal: every byte is used once.
+#include <algorithm>
+#include <atomic>
+
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
@@ -41,6 +44,28 @@ namespace {
 constexpr int kScanCols = 256;
 
 constexpr int kColsPerWave = 16;
+
+// State elements per workgroup of the tiled form: a tile's LDS (2 x 64 x 129
+// floats at 128) lets two workgroups share a CU, so that one loads or stores
+// while the other scans.
+#ifndef LRC_SCAN_TILE_COLS
+#define LRC_SCAN_TILE_COLS 128
+#endif
+constexpr int kScanTileCols = LRC_SCAN_TILE_COLS;
+// Persistent workgroups per CU of the tiled form (as many as the tile's LDS lets share a CU).
+constexpr int kScanTileBlocksPerCU = (160 * 1024) / (2 * kWave * (kScanTileCols + 1) * 4 + 64);
+
+// Polls of a chunk's hand-over flag before the tiled form gives up and
+// records an error (a poll is a load from memory, about a microsecond, and a
+// 128-cycle sleep: about 0.2 s in all).
+constexpr int kScanWaitLimit = 1 << 17;
+
+// Tiles of the tiled form: chunk_off[s] is the first chunk of batch slot s
+// in the tiled launch (slots in batch order), chunk_off[P] the total.
+struct ScanTiles {
+    int ncb;
+    int chunk_off[LRC_MAX_PROMPTS + 1];
+};
 
 // a, b and h are touched once each: the 16-byte accesses are marked
 // nontemporal (streaming), which measured 5% faster than plain accesses on
@@ -194,6 +219,214 @@ __global__ __launch_bounds__(COLS * 4) void scan_rows_kernel(const float* __rest
     }
 }
 
+// ---------------------------------------------------------------- tiled form
+// The same chunk arithmetic over tiles of (chunk, COLS-element block).  Tiles
+// are numbered prompt by prompt, chunk by chunk, block-fastest within a chunk,
+// and handed out in that order from a ticket counter to persistent
+// workgroups, so the tiles in flight at any moment cover whole rows of the
+// same chunks (the long-lived form lets the blocks of a prompt drift apart,
+// and rows are then read in pieces at different times, which loses
+// DRAM-page locality).  A workgroup prefetches its next tile's rows while it
+// scans the current one.  A tile is scanned from a zero carry first; only then
+// does it wait for the previous chunk of its block, whose last h row is the
+// carry, and finish h_t = A_t h0 + B_t.
+//
+// Hand-over: the last h row of a chunk is written with device-coherent
+// stores; the writing wave waits for them, the workgroup meets at a barrier,
+// and one thread then stores the chunk's completion into the flag of the
+// (prompt, block) chain as (generation << 32) | (chunk + 1).  The next chunk
+// polls that flag with device-coherent loads (bounded: after about 0.2 s it
+// records an error and goes on rather than hang), meets its workgroup at a
+// barrier and reads the carry with device-coherent loads.  A generation that
+// is new for every call makes stale flags from earlier calls harmless.
+// Tickets are taken in increasing order, so the tile a workgroup waits for
+// was taken earlier by a workgroup that is running: progress does not depend
+// on how many workgroups are resident.
+struct TileAt {
+    int p, j, S, cb;
+    long row0;
+    bool last;
+};
+
+__device__ __forceinline__ TileAt tile_at(const Batch& bt, const ScanTiles& tl, int ticket) {
+    TileAt x;
+    x.cb = ticket % tl.ncb;
+    const int t = ticket / tl.ncb;
+    int lo = 0, hi = bt.P;  // the slot whose chunks include t: chunk_off[lo] <= t < chunk_off[lo + 1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tl.chunk_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    x.p = batch_prompt(bt, lo);
+    x.j = t - tl.chunk_off[lo];
+    x.row0 = batch_row0(bt, x.p);
+    const int L = batch_len(bt, x.p);
+    x.S = min(kWave, L - kWave * x.j);
+    x.last = kWave * (x.j + 1) >= L;
+    return x;
+}
+
+__global__ void scan_ticket_reset(unsigned* ctl) { ctl[1] = 0; }
+
+template <int COLS>
+__global__ __launch_bounds__(COLS * 4) void scan_tile_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                            float* __restrict__ h, float* state, Batch bt,
+                                                            ScanTiles tl, long E, unsigned long long* flags,
+                                                            unsigned* ctl, unsigned gen, int ntickets) {
+    constexpr int kLd = COLS + 1;
+    constexpr int kLoadThreadsPerRow = COLS / 4;
+    __shared__ float As[kWave * kLd];
+    __shared__ float Bs[kWave * kLd];
+    __shared__ int ticket_sh;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = tid / kLoadThreadsPerRow;  // load phase: rows lr + 16 r, 4 columns at lc
+    const int lc = (tid % kLoadThreadsPerRow) * 4;
+    const int cw = wave * kColsPerWave;       // column phase: this wave's 16 columns
+
+    float ra[4][4], rb[4][4];
+    auto issue_loads = [&](const TileAt& x) {
+        const long tile0 = (long)x.cb * COLS;
+        const bool ok = tile0 + lc < E;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = lr + 16 * r;
+            f32x4 xa = {1.f, 1.f, 1.f, 1.f}, xb = {0.f, 0.f, 0.f, 0.f};
+            if (row < x.S && ok) {
+                const long off = (x.row0 + kWave * x.j + row) * E + tile0 + lc;
+                xa = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a + off));
+                xb = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(b + off));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[r][i] = xa[i];
+                rb[r][i] = xb[i];
+            }
+        }
+    };
+    auto take_ticket = [&]() {
+        if (tid == 0) ticket_sh = (int)__hip_atomic_fetch_add(&ctl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int t = ticket_sh;
+        return t;
+    };
+
+    int cur = take_ticket();
+    if (cur >= ntickets) return;
+    TileAt x = tile_at(bt, tl, cur);
+    issue_loads(x);
+    while (true) {
+        __syncthreads();  // the previous tile's h rows have left LDS, and every wave has read ticket_sh
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                As[(lr + 16 * r) * kLd + lc + i] = ra[r][i];
+                Bs[(lr + 16 * r) * kLd + lc + i] = rb[r][i];
+            }
+        const int nxt = take_ticket();  // its barrier also publishes the tile in LDS
+        TileAt y;
+        if (nxt < ntickets) {
+            y = tile_at(bt, tl, nxt);
+            issue_loads(y);  // the next tile's rows are in flight during this tile
+        }
+
+        // Column phase from a zero carry: lane = row, 16 columns per wave.
+        const long tile0 = (long)x.cb * COLS;
+        float A[kColsPerWave], B[kColsPerWave];
+#pragma unroll
+        for (int g = 0; g < kColsPerWave; g += 4) {
+            float a4[4], b4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a4[i] = As[lane * kLd + cw + g + i];
+                b4[i] = Bs[lane * kLd + cw + g + i];
+            }
+            wave_scan4(a4, b4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                A[g + i] = a4[i];
+                B[g + i] = b4[i];
+            }
+        }
+
+        // The carry: the incoming state for a prompt's first chunk, otherwise
+        // the previous chunk's last h row once its workgroup has handed it over.
+        const long ccol = tile0 + cw + (lane & 15);
+        const bool ccol_ok = ccol < E;
+        const long c0 = (long)kWave * x.j;
+        float cv = 0.f;
+        if (x.j == 0) {
+            if (ccol_ok) cv = state[(long)x.p * E + ccol];
+        } else {
+            unsigned long long* flag = flags + (long)x.p * tl.ncb + x.cb;
+            const unsigned long long want = ((unsigned long long)gen << 32) | (unsigned)x.j;
+            if (tid == 0) {
+                int n = 0;
+                while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+                    if (++n > kScanWaitLimit) {
+                        __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+            if (ccol_ok)
+                cv = __hip_atomic_load(h + (x.row0 + c0 - 1) * E + ccol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        float hlast[kColsPerWave];
+#pragma unroll
+        for (int i = 0; i < kColsPerWave; ++i) {
+            const float hv = fmaf(A[i], readlane_f(cv, i), B[i]);
+            hlast[i] = readlane_f(hv, x.S - 1);
+            As[lane * kLd + cw + i] = hv;
+        }
+        __syncthreads();
+
+        // Row phase.  The last row of a chunk that has a successor leaves
+        // through device-coherent stores; the rest as nontemporal 16-byte stores.
+        const bool lcol_ok = tile0 + lc < E;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = lr + 16 * r;
+            if (row < x.S && lcol_ok) {
+                const long off = (x.row0 + c0 + row) * E + tile0 + lc;
+                const float* src = &As[row * kLd + lc];
+                if (!x.last && row == kWave - 1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        __hip_atomic_store(h + off + i, src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    __builtin_nontemporal_store(f32x4{src[0], src[1], src[2], src[3]},
+                                                reinterpret_cast<f32x4*>(h + off));
+                }
+            }
+        }
+        if (x.last) {
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < kColsPerWave; ++i) {
+                    const long col = tile0 + cw + i;
+                    if (col < E) state[(long)x.p * E + col] = hlast[i];
+                }
+            }
+        } else {
+            if (lr + 48 == kWave - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the wave with the last row
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(flags + (long)x.p * tl.ncb + x.cb,
+                                   ((unsigned long long)gen << 32) | (unsigned)(x.j + 1), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (nxt >= ntickets) break;
+        x = y;
+    }
+}
+
 }  // namespace
 
 template <int COLS>
@@ -210,6 +443,39 @@ hipError_t launch_cols(const float* a, const float* b, float* h, const float* h0
 hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt, long E,
                        hipStream_t st) {
     return launch_cols<kScanCols>(a, b, h, h0, hS, bt, E, st);
+}
+
+size_t scan_workspace_bytes(int P, long E) {
+    const long ncb = (E + kScanTileCols - 1) / kScanTileCols;
+    return (size_t)P * ncb * sizeof(unsigned long long) + 256;
+}
+
+hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
+                             void* workspace, hipStream_t st) {
+    if (E % 4 != 0) return launch_cols<kScanCols>(a, b, h, state, state, bt, E, st);
+    ScanTiles tl;
+    tl.ncb = (int)((E + kScanTileCols - 1) / kScanTileCols);
+    long tiles = 0;
+    for (int s = 0; s < bt.P; ++s) {
+        tl.chunk_off[s] = (int)tiles;
+        tiles += (batch_len(bt, batch_prompt(bt, s)) + kWave - 1) / kWave;
+    }
+    tl.chunk_off[bt.P] = (int)tiles;
+    if (tiles == 0) return hipSuccess;
+    static std::atomic<unsigned> generation{0};
+    const unsigned gen = generation.fetch_add(1) + 1;  // 0 is never used: a zero-filled workspace holds no flag
+    auto* ctl = static_cast<unsigned*>(workspace);  // first 256 bytes: [0] timeouts, [1] next ticket
+    auto* flags = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
+    const int ntickets = (int)(tiles * tl.ncb);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess)
+        cus = 256;
+    const int grid = std::min(ntickets, std::max(1, cus) * kScanTileBlocksPerCU);
+    hipLaunchKernelGGL(scan_ticket_reset, dim3(1), dim3(1), 0, st, ctl);
+    hipLaunchKernelGGL((scan_tile_kernel<kScanTileCols>), dim3((unsigned)grid), dim3(kScanTileCols * 4), 0, st, a, b, h,
+                       state, bt, tl, E, flags, ctl, gen, ntickets);
+    return hipGetLastError();
 }
 
 }  // namespace lrc

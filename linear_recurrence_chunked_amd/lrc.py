@@ -41,6 +41,7 @@ _SIGS = {
     "lrc_conv_prefill": [_P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _P],
     "lrc_scan_rows": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "lrc_scan_prefill": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
+    "lrc_scan_prefill_ws": [_P, _P, _P, _P, _IP, _I, _I, _I, _P, ctypes.c_size_t, _P],
     "lrc_wkv4_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "lrc_wkv4_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _P],
     "lrc_wkv_tdecay_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -57,6 +58,8 @@ for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = _S
+lib.lrc_scan_workspace_size.argtypes = [_I, _I, _I]
+lib.lrc_scan_workspace_size.restype = ctypes.c_size_t
 lib.lrc_status_string.argtypes = [_S]
 lib.lrc_status_string.restype = ctypes.c_char_p
 lib.lrc_last_error.argtypes = []
@@ -182,6 +185,37 @@ def scan_prefill(a, b, h, state, lens):
         _need(t, torch.float32, (R, D, N), n)
     _need(state, torch.float32, (P, D, N), "state")
     _check(lib.lrc_scan_prefill(_ptr(a), _ptr(b), _ptr(h), _ptr(state), arr, P, D, N, _stream(a)))
+
+
+def scan_workspace_size(P: int, D: int, N: int) -> int:
+    """Bytes of workspace scan_prefill_ws needs for P prompts of D x N state elements."""
+    return int(lib.lrc_scan_workspace_size(P, D, N))
+
+
+def scan_workspace(P: int, D: int, N: int, device) -> torch.Tensor:
+    """A zero-filled workspace for scan_prefill_ws (uint8, reusable across calls that do not overlap)."""
+    return torch.zeros(scan_workspace_size(P, D, N), dtype=torch.uint8, device=device)
+
+
+def scan_workspace_timeouts(ws: torch.Tensor) -> int:
+    """Hand-overs of scan_prefill_ws that timed out since the workspace was made (0 unless progress failed)."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def scan_prefill_ws(a, b, h, state, lens, ws):
+    """scan_prefill in its tiled form; ws from scan_workspace(P, D, N, device)."""
+    _dev(a, b, h, state, ws)
+    R, D, N = a.shape
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but a has {R} rows")
+    for t, n in ((a, "a"), (b, "b"), (h, "h")):
+        _need(t, torch.float32, (R, D, N), n)
+    _need(state, torch.float32, (P, D, N), "state")
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous 1-D uint8 tensor")
+    _check(lib.lrc_scan_prefill_ws(_ptr(a), _ptr(b), _ptr(h), _ptr(state), arr, P, D, N, _ptr(ws), ws.numel(),
+                                   _stream(a)))
 
 
 # ------------------------------------------------------------------ K2 wkv

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     for n in ["lrc_conv_rows", "lrc_conv_prefill", "lrc_scan_rows", "lrc_scan_prefill", "lrc_wkv4_rows",
               "lrc_wkv4_prefill", "lrc_gdn_chunk", "lrc_gdn_prefill", "lrc_unit_lower_inverse",
               "lrc_time_shift_rows", "lrc_time_shift_prefill", "lrc_mamba_mixer_rows", "lrc_mamba_mixer_prefill",
-              "lrc_wkv_tdecay_rows", "lrc_wkv_tdecay_prefill", "lrc_status_string", "lrc_last_error", "lrc_version"]:
+              "lrc_wkv_tdecay_rows", "lrc_wkv_tdecay_prefill", "lrc_scan_prefill_ws", "lrc_scan_workspace_size",
+              "lrc_status_string", "lrc_last_error", "lrc_version"]:
         assert n in names
 
 
@@ -84,6 +85,23 @@ def test_prefill_rejects_bad_lengths(L):
     assert _st(L, L.lib.lrc_scan_prefill(A0, A1, A2, A3, lens, 0, 4, 16, None)) == "LRC_ERR_SHAPE"
     big = (ctypes.c_int * 300)(*([1] * 300))
     assert _st(L, L.lib.lrc_wkv4_prefill(A0, A1, A2, A3, A4, A5, A6, A7, big, 300, 8, None)) == "LRC_ERR_SHAPE"
+
+
+def test_scan_tiled_workspace_size_and_rejects(L):
+    # a control block, then one 8-byte flag per (prompt, block of 128 state elements)
+    assert L.scan_workspace_size(16, 5120, 16) == 256 + 16 * 640 * 8
+    assert L.scan_workspace_size(3, 5, 3) == 256 + 3 * 8
+    assert L.scan_workspace_size(0, 4, 16) == 0
+    f = L.lib.lrc_scan_prefill_ws
+    lens = (ctypes.c_int * 3)(5, 1, 7)
+    need = L.scan_workspace_size(3, 4, 16)
+    assert _st(L, f(A0, A1, A2, A3, lens, 3, 4, 16, None, need, None)) == "LRC_ERR_NULL"
+    assert _st(L, f(A0, A1, A2, A3, lens, 3, 4, 16, A4, need - 1, None)) == "LRC_ERR_SHAPE"
+    assert _st(L, f(A0, A1, A2, A3, lens, 3, 4, 16, A4 + 4, need, None)) == "LRC_ERR_ALIGN"
+    assert _st(L, f(A0, A1, A2, A3, lens, 3, 4, 16, A2 + 64, need, None)) == "LRC_ERR_ALIAS"  # inside h
+    assert _st(L, f(A0, A1, A2, A3, lens, 3, 4, 16, A3, need, None)) == "LRC_ERR_ALIAS"  # on the state
+    bad = (ctypes.c_int * 3)(5, -1, 7)
+    assert _st(L, f(A0, A1, A2, A3, bad, 3, 4, 16, A4, need, None)) == "LRC_ERR_ROWS"
 
 
 def test_conv_rejects_bad_width_dtype_rows(L):
