@@ -60,6 +60,10 @@ constexpr int kScanTileBlocksPerCU = (160 * 1024) / (2 * kWave * (kScanTileCols 
 // 128-cycle sleep: about 0.2 s in all).
 constexpr int kScanWaitLimit = 1 << 17;
 
+// Cache policy of a device-coherent buffer access on this target (sc1).
+constexpr int kCoherent = 16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 // Tiles of the tiled form: chunk_off[s] is the first chunk of batch slot s
 // in the tiled launch (slots in batch order), chunk_off[P] the total.
 struct ScanTiles {
@@ -397,9 +401,11 @@ __global__ __launch_bounds__(COLS * 4) void scan_tile_kernel(const float* __rest
                 const long off = (x.row0 + c0 + row) * E + tile0 + lc;
                 const float* src = &As[row * kLd + lc];
                 if (!x.last && row == kWave - 1) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        __hip_atomic_store(h + off + i, src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    // one 16-byte store with the device-coherence bit (sc1, cache policy 16)
+                    const auto rs = buffer_rsrc(h + (x.row0 + c0 + row) * E + tile0, COLS * 4);
+                    const u32x4 v4 = {__float_as_uint(src[0]), __float_as_uint(src[1]), __float_as_uint(src[2]),
+                                      __float_as_uint(src[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(v4, rs, lc * 4, 0, kCoherent);
                 } else {
                     __builtin_nontemporal_store(f32x4{src[0], src[1], src[2], src[3]},
                                                 reinterpret_cast<f32x4*>(h + off));
