@@ -28,8 +28,15 @@ namespace lrc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;
 constexpr int kUnroll = 8;
+
+// Rows per tile: 32 for fp32, 64 for bf16 (measured best on the mixed prefill
+// shapes; a taller bf16 tile re-reads fewer halo rows and gives each thread a
+// longer run, while 16 or fewer rows were slower for both).
+template <typename T>
+constexpr int tile_rows() {
+    return sizeof(T) == 2 ? 64 : 32;
+}
 
 template <typename T>
 struct Io;
@@ -108,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void conv_rows_kernel(const T* __restrict
                                                             Batch bt, int C) {
     constexpr int H = K - 1;
     constexpr bool FULL = (VEC == Io<T>::VEC);
+    constexpr int kTile = tile_rows<T>();
     const int c0 = (blockIdx.x * kThreads + threadIdx.x) * VEC;
     if (c0 >= C) return;
     const int nc = min(VEC, C - c0);
@@ -195,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void conv_rows_kernel(const T* __restrict
 template <typename T, int K>
 hipError_t launch_typed(const T* x, T* y, const T* s_in, T* s_out, const float* w, const float* bias, const Batch& bt,
                         int C, hipStream_t st) {
+    constexpr int kTile = tile_rows<T>();
     int maxL = 0;
     for (int i = 0; i < bt.P; ++i) maxL = max(maxL, batch_len(bt, batch_prompt(bt, i)));
     const int tiles = max(1, min(65535, (maxL + kTile - 1) / kTile));
