@@ -29,17 +29,20 @@
 //      k_i + (n-1-i) w are independent of each other, so their maximum and
 //      the sums relative to it are plain reductions over the rows held in
 //      registers, not a chain;
-//   2. the block states meet in LDS; wave j folds the carried state and
-//      blocks 0 .. j-1, in row order, into its own start state, and the last
-//      wave folds all of them into the state after the chunk, which it hands
-//      to the next chunk through LDS;
+//   2. the block states meet in LDS; the last wave folds them, in row order,
+//      into the carried state, and writes each block's start state back to
+//      LDS as it goes (NW folds in all, not one chain per wave); it keeps the
+//      state after the chunk in registers for the next chunk;
 //   3. each wave replays its rows from its start state and writes the rows'
-//      outputs (the larger of the running maximum and the bonus u + k_t, one
-//      exp and one reciprocal per row).
+//      outputs (the larger of the running maximum and the bonus u + k_t, then
+//      the push of the row into the state: two exps and one reciprocal per
+//      row; the push exponent is the output's plus w + u).
 // A chunk's sequential work per wave is thus 64/NW rows plus at most NW folds
 // instead of 64 rows, and a prompt keeps NW waves per 64 channels busy.  The
 // next chunk's rows are loaded while the current chunk computes; the row
-// updates are branch-free selects.
+// updates are branch-free selects.  Exponents are kept in base 2 (k, w, u and
+// the maximum scaled by log2 e once, the maximum scaled back on the way out),
+// so each exponential is a bare v_exp_f32.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
@@ -55,38 +58,46 @@ namespace {
 constexpr int kWkvWaves = LRC_WKV_WAVES;
 constexpr int kWkvDepth = LRC_WKV_DEPTH;  // chunks whose rows are in flight ahead of the one computing
 
+// Exponents are held in base 2 (k, w, u and the running maximum scaled by
+// log2 e once), so that every exponential is one v_exp_f32 with no scaling.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct WkvState {
-    float aa, bb;  // num, den scaled by e^{-(m + n w)}
-    float m, n;    // current largest exponent is m + n w
+    float aa, bb;  // num, den scaled by 2^{-(m + n w)}
+    float m, n;    // current largest exponent (base 2) is m + n w
 };
 
-// One more row: decay the state by e^w, then add row (k_t, v_t).
-__device__ __forceinline__ void push_row(WkvState& s, float wc, float kt, float vt) {
-    const float n1 = s.n + 1.f;
-    const float d = fmaf(n1, wc, s.m) - kt;
-    const float e = fast_exp(-fabsf(d));
-    const bool lead = d >= 0.f;  // the decayed maximum stays in the lead
-    const float fs = lead ? 1.f : e, fb = lead ? e : 1.f;
-    s.aa = fmaf(fs, s.aa, fb * vt);
-    s.bb = fmaf(fs, s.bb, fb);
-    s.n = lead ? n1 : 0.f;
-    s.m = lead ? s.m : kt;
-}
-
-// Output of row t from the state before it and the bonus exponent u + k_t.
-__device__ __forceinline__ float out_row(const WkvState& s, float wc, float uc, float kt, float vt) {
+// Output of row t from the state before it and the bonus exponent u + k_t;
+// then, if PUSH, the state after row t (decayed by one row, row t added).  The
+// push exponent (m + (n+1) w) - k_t is the output's (m + n w) - (u + k_t)
+// plus w + u (wu).
+template <bool PUSH>
+__device__ __forceinline__ float step_row(WkvState& s, float wc, float uc, float wu, float kt, float vt) {
     const float d = fmaf(s.n, wc, s.m) - (uc + kt);
-    const float e = fast_exp(-fabsf(d));
+    const float e = exp2_(-fabsf(d));
     const float fs = d >= 0.f ? 1.f : e;
     const float fb = d >= 0.f ? e : 1.f;
-    return fmaf(fs, s.aa, fb * vt) * __builtin_amdgcn_rcpf(fmaf(fs, s.bb, fb));
+    const float o = fmaf(fs, s.aa, fb * vt) * __builtin_amdgcn_rcpf(fmaf(fs, s.bb, fb));
+    if (PUSH) {
+        const float dp = d + wu;
+        const float ep = exp2_(-fabsf(dp));
+        const bool lead = dp >= 0.f;  // the decayed maximum stays in the lead
+        const float ps = lead ? 1.f : ep, pb = lead ? ep : 1.f;
+        s.aa = fmaf(ps, s.aa, pb * vt);
+        s.bb = fmaf(ps, s.bb, pb);
+        s.n = lead ? s.n + 1.f : 0.f;
+        s.m = lead ? s.m : kt;
+    }
+    return o;
 }
 
 // s <- (s decayed by len rows) + z, where z is a block reduced from a zero state.
 __device__ __forceinline__ void absorb(WkvState& s, const float4& z, float len, float wc) {
     const float nl = s.n + len;
     const float d = fmaf(nl, wc, s.m) - fmaf(z.w, wc, z.z);
-    const float e = fast_exp(-fabsf(d));
+    const float e = exp2_(-fabsf(d));
     const bool lead = d >= 0.f;
     s.aa = fmaf(e, lead ? z.x : s.aa, lead ? s.aa : z.x);
     s.bb = fmaf(e, lead ? z.y : s.bb, lead ? s.bb : z.y);
@@ -112,7 +123,7 @@ __device__ __forceinline__ float4 reduce_block(const float (&kb)[R], const float
 #pragma unroll
     for (int i = 0; i < R; ++i)
         if (i < nb) {
-            const float e = fast_exp(ex[i] - best);
+            const float e = exp2_(ex[i] - best);
             aa = fmaf(e, vb[i], aa);
             bb = bb + e;
         }
@@ -125,8 +136,8 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
                                                       float* __restrict__ wkv, float* num, float* den, float* mx,
                                                       Batch bt, int C) {
     constexpr int R = 64 / NW;  // rows per wave and chunk
-    __shared__ float4 zs[2][NW][64];  // block states of a chunk
-    __shared__ float4 cs[2][64];      // state after a chunk, from the last wave
+    __shared__ float4 zs[NW][64];  // block states of a chunk
+    __shared__ float4 ps[NW][64];  // start state of every block, from the last wave
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = blockIdx.x * 64 + lane;
@@ -142,8 +153,8 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
     const long sidx = (long)p * C + cl;
-    const float wc = w[cl], uc = u[cl];
-    WkvState carry{num[sidx], den[sidx], mx[sidx], 0.f};
+    const float wc = w[cl] * kLog2e, uc = u[cl] * kLog2e, wu = wc + uc;
+    WkvState carry{num[sidx], den[sidx], mx[sidx] * kLog2e, 0.f};  // kept by the last wave
 
     float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R];  // ring of row buffers
     // Loads are issued unconditionally (rows past the prompt re-read its last
@@ -169,57 +180,49 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
             vb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vrs, lane_off, soff, kNontemporal));
         }
     };
-    int buf = 0;
-    auto chunk = [&](int c0, const float (&kb)[R], const float (&vb)[R]) {
+    auto chunk = [&](int c0, const float (&kb_in)[R], const float (&vb)[R]) {
         const int S = min(64, L - c0);
         const int nb = min(R, max(0, S - R * wv));  // rows of this wave's block
+        float kb[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) kb[i] = kb_in[i] * kLog2e;
         if (nb == R)
-            zs[buf][wv][lane] = reduce_block<R>(kb, vb, R, wc);  // constant row count: no per-row checks
+            zs[wv][lane] = reduce_block<R>(kb, vb, R, wc);  // constant row count: no per-row checks
         else if (nb > 0)
-            zs[buf][wv][lane] = reduce_block<R>(kb, vb, nb, wc);
+            zs[wv][lane] = reduce_block<R>(kb, vb, nb, wc);
         __syncthreads();
-        if (c0 > 0) {
-            const float4 cc = cs[buf ^ 1][lane];
-            carry = WkvState{cc.x, cc.y, cc.z, cc.w};
-        }
-        // all block states at once (slots of empty blocks hold stale values
-        // that are never folded); opaque registers, so that the folds' selects
-        // stay selects instead of conditional LDS loads
-        float4 zz[NW];
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            zz[j] = zs[buf][j][lane];
-            asm volatile("" : "+v"(zz[j].x), "+v"(zz[j].y), "+v"(zz[j].z), "+v"(zz[j].w));
-        }
-        WkvState s = carry;
-        const int jn = min(wv, (S + R - 1) / R);  // non-empty blocks before this wave's
-#pragma unroll
-        for (int j = 0; j < NW - 1; ++j)
-            if (j < jn) absorb(s, zz[j], (float)min(R, S - R * j), wc);
         if (wv == NW - 1) {
-            WkvState e = s;
-            if (nb > 0) absorb(e, zz[NW - 1], (float)nb, wc);
-            cs[buf][lane] = make_float4(e.aa, e.bb, e.m, e.n);
-            carry = e;
+            // every block's start state in row order, and the state after the chunk
+            WkvState s = carry;
+            const int nblk = (S + R - 1) / R;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                ps[j][lane] = make_float4(s.aa, s.bb, s.m, s.n);
+                float4 z = zs[j][lane];
+                asm volatile("" : "+v"(z.x), "+v"(z.y), "+v"(z.z), "+v"(z.w));
+                if (j < nblk) absorb(s, z, (float)min(R, S - R * j), wc);
+            }
+            carry = s;
         }
-        buf ^= 1;
+        __syncthreads();
+        const float4 st = ps[wv][lane];
+        WkvState s{st.x, st.y, st.z, st.w};
         // lanes past C store at an offset past the resource's end: dropped
         const auto ors = buffer_rsrc(wkv + (row0 + c0 + R * wv) * C + blockIdx.x * 64, (uint32_t)R * C * 4);
         const uint32_t st_off = valid ? lane_off : 0x80000000u;
         if (nb == R) {  // full block: straight-line code
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const float o = out_row(s, wc, uc, kb[i], vb[i]);
+                const float o = i + 1 < R ? step_row<true>(s, wc, uc, wu, kb[i], vb[i])
+                                          : step_row<false>(s, wc, uc, wu, kb[i], vb[i]);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ors, st_off, i * C * 4, kNontemporal);
-                if (i + 1 < R) push_row(s, wc, kb[i], vb[i]);
             }
         } else if (nb > 0) {
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 if (i < nb) {
-                    const float o = out_row(s, wc, uc, kb[i], vb[i]);
+                    const float o = step_row<true>(s, wc, uc, wu, kb[i], vb[i]);
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ors, st_off, i * C * 4, kNontemporal);
-                    if (i + 1 < nb) push_row(s, wc, kb[i], vb[i]);
                 }
         }
     };
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
     if (wv == NW - 1 && valid) {
         num[sidx] = carry.aa;
         den[sidx] = carry.bb;
-        mx[sidx] = fmaf(carry.n, wc, carry.m);
+        mx[sidx] = fmaf(carry.n, wc, carry.m) * kLn2;
     }
 }
 
