@@ -96,3 +96,32 @@ def test_tiled_mixed_prefill_full_size_equals_long_lived(L):
     torch.cuda.synchronize()
     assert torch.equal(h1, h2) and torch.equal(st1, st2)
     assert L.scan_workspace_timeouts(ws) == 0
+
+
+def test_tiled_two_streams_at_once(L):
+    """Two tiled scans with their own workspaces on two streams at the same time: each chain's
+    hand-overs stay within its own call, and both equal the long-lived driver bit for bit."""
+    lens_a, lens_b = [700, 3, 129, 64, 0, 1000], [1, 517, 256, 2000]
+    D, N = 256, 16
+    outs = []
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = []
+    for seed, lens in ((41, lens_a), (42, lens_b)):
+        a, b, h0 = _case(seed, lens, D, N)
+        ta, tb = (to_dev(torch.from_numpy(x).float()) for x in (a, b))
+        th0 = to_dev(torch.from_numpy(h0).float())
+        ref_h, ref_s = torch.empty_like(ta), th0.clone()
+        L.scan_prefill(ta, tb, ref_h, ref_s, lens)
+        cases.append((lens, ta, tb, th0, ref_h, ref_s, L.scan_workspace(len(lens), D, N, "cuda")))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (lens, ta, tb, th0, ref_h, ref_s, ws), st in zip(cases, (s1, s2)):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                h, s = torch.empty_like(ta), th0.clone()
+                L.scan_prefill_ws(ta, tb, h, s, lens, ws)
+            outs.append((h, s, ref_h, ref_s, ws))
+        torch.cuda.synchronize()
+    for h, s, ref_h, ref_s, ws in outs:
+        assert torch.equal(h, ref_h) and torch.equal(s, ref_s)
+        assert L.scan_workspace_timeouts(ws) == 0
