@@ -23,40 +23,35 @@
 // state of the same form, and "decay a state by n rows, then add a block" is
 // again one exp.  A workgroup owns 64 channels (one per lane, so every row's
 // loads and stores are one contiguous 256-byte run) of one prompt and walks
-// the prompt's 64-row chunks; its NW waves split each chunk into NW blocks of
-// 64/NW rows.  Per chunk:
-//   1. each wave reduces its block from a zero state: the block's exponents
-//      k_i + (n-1-i) w are independent of each other, so their maximum and
-//      the sums relative to it are plain reductions over the rows held in
-//      registers, not a chain;
-//   2. the block states meet in LDS; the last wave folds them, in row order,
-//      into the carried state, and writes each block's start state back to
-//      LDS as it goes (NW folds in all, not one chain per wave); it keeps the
-//      state after the chunk in registers for the next chunk;
-//   3. each wave replays its rows from its start state and writes the rows'
-//      outputs (the larger of the running maximum and the bonus u + k_t, then
-//      the push of the row into the state: two exps and one reciprocal per
-//      row; the push exponent is the output's plus w + u).
-// A chunk's sequential work per wave is thus 64/NW rows plus at most NW folds
-// instead of 64 rows, and a prompt keeps NW waves per 64 channels busy.  The
-// next chunk's rows are loaded while the current chunk computes; the row
-// updates are branch-free selects.  Exponents are kept in base 2 (k, w, u and
-// the maximum scaled by log2 e once, the maximum scaled back on the way out),
-// so each exponential is a bare v_exp_f32.
+// the prompt's 64-row chunks with NW row waves (blocks of 64/NW rows) and one
+// fold wave:
+//   1. in the step of chunk n, each row wave reduces its block of chunk n+1
+//      from a zero state (the block's exponents k_i + (n-1-i) w are
+//      independent of each other, so their maximum and the sums relative to
+//      it are plain reductions over registers) and signals it;
+//   2. the fold wave waits for the NW block states of chunk n, folds them in
+//      row order into the carried state, writes each block's start state to
+//      LDS as it goes, keeps the state after the chunk, and publishes;
+//   3. each row wave waits for its start state of chunk n and replays its
+//      rows (the larger of the running maximum and the bonus u + k_t, then the
+//      push of the row into the state: two exps and one reciprocal per row;
+//      the push exponent is the output's plus w + u).
+// The waves meet through LDS counters, not workgroup barriers, so the chain
+// from one chunk to the next runs through the fold alone: a row wave's
+// replay of chunk n and reduction of chunk n+2 are off it.  Block states and
+// start states are double-buffered by chunk parity; a row wave cannot reduce
+// chunk n+2 before chunk n is folded, which is what makes a count of
+// reductions per parity exact.  Rows are fetched two chunks ahead.
+// Exponents are kept in base 2 (k, w, u and the maximum scaled by log2 e,
+// the maximum scaled back on the way out), so each exponential is a bare
+// v_exp_f32.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
 namespace lrc {
 namespace {
 
-#ifndef LRC_WKV_WAVES
-#define LRC_WKV_WAVES 8
-#endif
-#ifndef LRC_WKV_DEPTH
-#define LRC_WKV_DEPTH 2
-#endif
-constexpr int kWkvWaves = LRC_WKV_WAVES;
-constexpr int kWkvDepth = LRC_WKV_DEPTH;  // chunks whose rows are in flight ahead of the one computing
+constexpr int kWkvWaves = 8;  // row waves per workgroup (blocks of 8 rows)
 
 // Exponents are held in base 2 (k, w, u and the running maximum scaled by
 // log2 e once), so that every exponential is one v_exp_f32 with no scaling.
@@ -130,43 +125,90 @@ __device__ __forceinline__ float4 reduce_block(const float (&kb)[R], const float
     return make_float4(aa, bb, zm, zn);
 }
 
-template <int NW, int DEPTH, bool FULL>
-__global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__ k, const float* __restrict__ v,
-                                                      const float* __restrict__ w, const float* __restrict__ u,
-                                                      float* __restrict__ wkv, float* num, float* den, float* mx,
-                                                      Batch bt, int C) {
-    constexpr int R = 64 / NW;  // rows per wave and chunk
-    __shared__ float4 zs[NW][64];  // block states of a chunk
-    __shared__ float4 ps[NW][64];  // start state of every block, from the last wave
+// Bounded wait on an LDS counter (no wave that one waits for needs anything
+// from the waiting wave, so the bound is never reached in practice).
+constexpr int kLdsWaitLimit = 1 << 20;
+__device__ __forceinline__ void lds_wait_at_least(int* x, int v) {
+    int n = 0;
+    while (__hip_atomic_load(x, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) {
+        if (++n > kLdsWaitLimit) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// NW row waves (a block of R = 64/NW rows each) and one fold wave.
+template <int NW, bool FULL>
+__global__ __launch_bounds__((NW + 1) * 64) void wkv4_kernel(const float* __restrict__ k, const float* __restrict__ v,
+                                                            const float* __restrict__ w, const float* __restrict__ u,
+                                                            float* __restrict__ wkv, float* num, float* den, float* mx,
+                                                            Batch bt, int C) {
+    constexpr int R = 64 / NW;        // rows per row wave and chunk
+    __shared__ float4 zs[2][NW][64];  // block states of a chunk, by chunk parity
+    __shared__ float4 ps[2][NW][64];  // start state of every block, by chunk parity
+    __shared__ int red_cnt[2];        // block reductions done, of even and of odd chunks
+    __shared__ int ps_seq;            // chunks whose start states are published
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = blockIdx.x * 64 + lane;
     const bool valid = FULL || c < C;
     const int cl = valid ? c : C - 1;  // lanes past C compute a copy of the last channel and store nothing
-    {   // the longest prompts come first in the grid; their waves get issue priority
-        const int q4 = (4 * blockIdx.y) / gridDim.y;
-        if (q4 == 0) __builtin_amdgcn_s_setprio(3);
-        else if (q4 == 1) __builtin_amdgcn_s_setprio(2);
-        else if (q4 == 2) __builtin_amdgcn_s_setprio(1);
+    if (threadIdx.x == 0) {
+        red_cnt[0] = red_cnt[1] = 0;
+        ps_seq = 0;
     }
+    __syncthreads();
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
+    if (L == 0) return;  // the state stays as it is
+    const int nc = (L + 63) / 64;
     const long sidx = (long)p * C + cl;
     const float wc = w[cl] * kLog2e, uc = u[cl] * kLog2e, wu = wc + uc;
-    WkvState carry{num[sidx], den[sidx], mx[sidx] * kLog2e, 0.f};  // kept by the last wave
 
-    float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R];  // ring of row buffers
+    if (wv == NW) {
+        // ---- fold wave: the chain from chunk to chunk.  Waits for the NW block
+        // states of chunk n, folds them in row order into the carried state,
+        // publishing each block's start state, and keeps the state after it.
+        __builtin_amdgcn_s_setprio(3);
+        WkvState s{num[sidx], den[sidx], mx[sidx] * kLog2e, 0.f};
+        for (int n = 0; n < nc; ++n) {
+            const int S = min(64, L - 64 * n), nblk = (S + R - 1) / R, b = n & 1;
+            // No row wave reduces chunk n+2 before chunk n's start states are
+            // out, so the count of this parity covers chunks up to n only.
+            lds_wait_at_least(&red_cnt[b], NW * (n / 2 + 1));
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                ps[b][j][lane] = make_float4(s.aa, s.bb, s.m, s.n);
+                float4 z = zs[b][j][lane];
+                asm volatile("" : "+v"(z.x), "+v"(z.y), "+v"(z.z), "+v"(z.w));
+                if (j < nblk) absorb(s, z, (float)min(R, S - R * j), wc);
+            }
+            if (lane == 0) __hip_atomic_store(&ps_seq, n + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (valid) {
+            num[sidx] = s.aa;
+            den[sidx] = s.bb;
+            mx[sidx] = fmaf(s.n, wc, s.m) * kLn2;
+        }
+        return;
+    }
+
+    // ---- row waves.  In the step of chunk n a row wave reduces its block of
+    // chunk n+1 (so the fold wave never waits on a replay), then waits for its
+    // start state of chunk n and replays its rows.  The longest prompts come
+    // first in the grid; their row waves get issue priority.
+    {
+        const int q4 = (4 * blockIdx.y) / gridDim.y;
+        if (q4 == 0) __builtin_amdgcn_s_setprio(2);
+        else if (q4 == 1) __builtin_amdgcn_s_setprio(1);
+    }
+    // Rows through buffer resources based at the wave's first row (uniform
+    // row offsets in the scalar offset, a fixed channel offset per lane).
     // Loads are issued unconditionally (rows past the prompt re-read its last
-    // row) so that the compiler can count them and wait only for the chunk
-    // about to be used, not for the one being prefetched.  k, v and the
-    // output are touched once: their accesses are nontemporal (streaming).
-    // R rows x C channels of a buffer resource stay below 2^31 bytes.
-    // The rows go through buffer resources based at the wave's first row: the
-    // row offsets are uniform and ride in the scalar offset, the channel
-    // offset is the same for every row, so no address is formed per load.
+    // row) so that the compiler can count them.  R rows x C channels of a
+    // resource stay below 2^31 bytes.
     const uint32_t lane_off = (uint32_t)(cl - blockIdx.x * 64) * 4;
-    const float* k0 = k + row0 * C + blockIdx.x * 64;  // the workgroup's first channel of the prompt's row 0
+    const float* k0 = k + row0 * C + blockIdx.x * 64;
     const float* v0 = v + row0 * C + blockIdx.x * 64;
     auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R]) {
         const int r0 = min(c0 + R * wv, L - 1);
@@ -180,32 +222,26 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
             vb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vrs, lane_off, soff, kNontemporal));
         }
     };
-    auto chunk = [&](int c0, const float (&kb_in)[R], const float (&vb)[R]) {
-        const int S = min(64, L - c0);
-        const int nb = min(R, max(0, S - R * wv));  // rows of this wave's block
-        float kb[R];
+    auto reduce = [&](int n, const float (&kr)[R], const float (&vb)[R]) {
+        float kb[R];  // keys in base 2
 #pragma unroll
-        for (int i = 0; i < R; ++i) kb[i] = kb_in[i] * kLog2e;
+        for (int i = 0; i < R; ++i) kb[i] = kr[i] * kLog2e;
+        const int S = min(64, L - 64 * n);
+        const int nb = min(R, max(0, S - R * wv));
         if (nb == R)
-            zs[wv][lane] = reduce_block<R>(kb, vb, R, wc);  // constant row count: no per-row checks
+            zs[n & 1][wv][lane] = reduce_block<R>(kb, vb, R, wc);  // constant row count: no per-row checks
         else if (nb > 0)
-            zs[wv][lane] = reduce_block<R>(kb, vb, nb, wc);
-        __syncthreads();
-        if (wv == NW - 1) {
-            // every block's start state in row order, and the state after the chunk
-            WkvState s = carry;
-            const int nblk = (S + R - 1) / R;
+            zs[n & 1][wv][lane] = reduce_block<R>(kb, vb, nb, wc);
+        if (lane == 0) __hip_atomic_fetch_add(&red_cnt[n & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto replay = [&](int n, const float (&kr)[R], const float (&vb)[R]) {
+        float kb[R];  // keys in base 2
 #pragma unroll
-            for (int j = 0; j < NW; ++j) {
-                ps[j][lane] = make_float4(s.aa, s.bb, s.m, s.n);
-                float4 z = zs[j][lane];
-                asm volatile("" : "+v"(z.x), "+v"(z.y), "+v"(z.z), "+v"(z.w));
-                if (j < nblk) absorb(s, z, (float)min(R, S - R * j), wc);
-            }
-            carry = s;
-        }
-        __syncthreads();
-        const float4 st = ps[wv][lane];
+        for (int i = 0; i < R; ++i) kb[i] = kr[i] * kLog2e;
+        const int c0 = 64 * n, S = min(64, L - c0);
+        const int nb = min(R, max(0, S - R * wv));
+        lds_wait_at_least(&ps_seq, n + 1);
+        const float4 st = ps[n & 1][wv][lane];
         WkvState s{st.x, st.y, st.z, st.w};
         // lanes past C store at an offset past the resource's end: dropped
         const auto ors = buffer_rsrc(wkv + (row0 + c0 + R * wv) * C + blockIdx.x * 64, (uint32_t)R * C * 4);
@@ -227,24 +263,23 @@ __global__ __launch_bounds__(NW * 64) void wkv4_kernel(const float* __restrict__
         }
     };
 
-    if (L > 0) {
-#pragma unroll
-        for (int s = 0; s < DEPTH; ++s) fetch(64 * s, kb_[s], vb_[s]);
-    }
-    for (int c0 = 0; c0 < L; c0 += 64 * (DEPTH + 1)) {
-#pragma unroll
-        for (int s = 0; s <= DEPTH; ++s) {
-            const int cc = c0 + 64 * s;
-            if (cc >= L) break;
-            fetch(cc + 64 * DEPTH, kb_[(s + DEPTH) % (DEPTH + 1)], vb_[(s + DEPTH) % (DEPTH + 1)]);
-            chunk(cc, kb_[s], vb_[s]);
-        }
-    }
-    // the last wave holds the state after the prompt (or the incoming one)
-    if (wv == NW - 1 && valid) {
-        num[sidx] = carry.aa;
-        den[sidx] = carry.bb;
-        mx[sidx] = fmaf(carry.n, wc, carry.m) * kLn2;
+    // A ring of three row buffers: chunk n (replayed), n+1 (reduced), n+2 (in flight).
+    float kb0[R], vb0[R], kb1[R], vb1[R], kb2[R], vb2[R];
+    fetch(0, kb0, vb0);
+    fetch(64, kb1, vb1);
+    reduce(0, kb0, vb0);
+    for (int n = 0; n < nc; n += 3) {
+        fetch(64 * (n + 2), kb2, vb2);
+        if (n + 1 < nc) reduce(n + 1, kb1, vb1);
+        replay(n, kb0, vb0);
+        if (n + 1 >= nc) break;
+        fetch(64 * (n + 3), kb0, vb0);
+        if (n + 2 < nc) reduce(n + 2, kb2, vb2);
+        replay(n + 1, kb1, vb1);
+        if (n + 2 >= nc) break;
+        fetch(64 * (n + 4), kb1, vb1);
+        if (n + 3 < nc) reduce(n + 3, kb0, vb0);
+        replay(n + 2, kb2, vb2);
     }
 }
 
@@ -254,11 +289,11 @@ hipError_t launch_wkv4(const float* k, const float* v, const float* w, const flo
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st) {
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)bt.P);
     if (C % 64 == 0)
-        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, kWkvDepth, true>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
-                           den, mx, bt, C);
+        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, true>), grid, dim3((kWkvWaves + 1) * 64), 0, st, k, v, w, u, wkv,
+                           num, den, mx, bt, C);
     else
-        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, kWkvDepth, false>), grid, dim3(kWkvWaves * 64), 0, st, k, v, w, u, wkv, num,
-                           den, mx, bt, C);
+        hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, false>), grid, dim3((kWkvWaves + 1) * 64), 0, st, k, v, w, u, wkv,
+                           num, den, mx, bt, C);
     return hipGetLastError();
 }
 
