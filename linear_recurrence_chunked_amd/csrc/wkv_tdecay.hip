@@ -20,21 +20,25 @@
 // rounded to FP32 for the exp.
 //
 // Mapping on CDNA4: as for the RWKV-4 kernel.  A workgroup owns 64 channels
-// (one per lane) of one prompt and walks its 64-row chunks; its NW waves split
-// a chunk into NW blocks.  Each wave reduces its block from a zero state to
+// (one per lane) of one prompt and walks its 64-row chunks with NW row waves,
+// which split a chunk into NW blocks, and one fold wave.  In the step of
+// chunk n each row wave reduces its block of chunk n+1 from a zero state to
 // (sums, largest exponent relative to the block's end, total decay of the
-// block); the block states meet in LDS, each wave folds the carried state and
-// the blocks before its own into its start state, the last wave hands the
-// state after the chunk to the next one, and each wave replays its rows.  The
-// next chunk's k, v and w are loaded while the current one computes.
+// block) and signals it, then waits for its start state of chunk n and
+// replays its rows.  The fold wave waits for a chunk's block states, folds
+// them in row order into the carried state, writing each block's start state
+// to LDS, and publishes.  The waves meet through LDS counters, not workgroup
+// barriers, so the chain from chunk to chunk runs through the fold alone.
+// Block and start states are double-buffered by chunk parity; a row wave
+// cannot reduce chunk n+2 before chunk n is folded, which makes a count of
+// reductions per parity exact.  k, v and w are fetched two chunks ahead.
 #include "lrc_device.h"
 #include "lrc_internal.h"
 
 namespace lrc {
 namespace {
 
-constexpr int kTdWaves = 8;
-constexpr int kTdDepth = 2;  // chunks whose rows are in flight ahead of the one computing
+constexpr int kTdWaves = 8;  // row waves per workgroup (blocks of 8 rows)
 
 struct TdState {
     float aa, bb;  // num, den scaled by e^{-m}
@@ -111,46 +115,104 @@ __device__ __forceinline__ TdBlock reduce_block(const float (&kb)[R], const floa
     return TdBlock{aa, bb, best, tail};
 }
 
-template <int NW, int DEPTH, bool FULL>
-__global__ __launch_bounds__(NW * 64) void wkv_tdecay_kernel(const float* __restrict__ k, const float* __restrict__ v,
-                                                            const float* __restrict__ w, const float* __restrict__ u,
-                                                            float* __restrict__ wkv, float* num, float* den, float* mx,
-                                                            Batch bt, int C) {
-    constexpr int R = 64 / NW;  // rows per wave and chunk
-    __shared__ float2 zs[2][NW][64];   // block sums of a chunk
+// Bounded wait on an LDS counter (no wave that one waits for needs anything
+// from the waiting wave, so the bound is never reached in practice).
+constexpr int kLdsWaitLimit = 1 << 20;
+__device__ __forceinline__ void lds_wait_at_least(int* x, int v) {
+    int n = 0;
+    while (__hip_atomic_load(x, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) {
+        if (++n > kLdsWaitLimit) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// NW row waves (a block of R = 64/NW rows each) and one fold wave.
+template <int NW, bool FULL>
+__global__ __launch_bounds__((NW + 1) * 64) void wkv_tdecay_kernel(const float* __restrict__ k,
+                                                                  const float* __restrict__ v,
+                                                                  const float* __restrict__ w,
+                                                                  const float* __restrict__ u,
+                                                                  float* __restrict__ wkv, float* num, float* den,
+                                                                  float* mx, Batch bt, int C) {
+    constexpr int R = 64 / NW;         // rows per row wave and chunk
+    __shared__ float2 zs[2][NW][64];   // block sums of a chunk, by chunk parity
     __shared__ double2 zx[2][NW][64];  // block (largest exponent, decay)
-    __shared__ float2 cs[2][64];       // state after a chunk, from the last wave
-    __shared__ double cm[2][64];
+    __shared__ float2 ps[2][NW][64];   // start state of every block, by chunk parity
+    __shared__ double pm[2][NW][64];
+    __shared__ int red_cnt[2];         // block reductions done, of even and of odd chunks
+    __shared__ int ps_seq;             // chunks whose start states are published
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = blockIdx.x * 64 + lane;
     const bool valid = FULL || c < C;
     const int cl = valid ? c : C - 1;  // lanes past C compute a copy of the last channel and store nothing
-    {   // the longest prompts come first in the grid; their waves get issue priority
-        const int q4 = (4 * blockIdx.y) / gridDim.y;
-        if (q4 == 0) __builtin_amdgcn_s_setprio(3);
-        else if (q4 == 1) __builtin_amdgcn_s_setprio(2);
-        else if (q4 == 2) __builtin_amdgcn_s_setprio(1);
+    if (threadIdx.x == 0) {
+        red_cnt[0] = red_cnt[1] = 0;
+        ps_seq = 0;
     }
+    __syncthreads();
     const int p = batch_prompt(bt, blockIdx.y);
     const long row0 = batch_row0(bt, p);
     const int L = batch_len(bt, p);
+    if (L == 0) return;  // the state stays as it is
+    const int nc = (L + 63) / 64;
     const long sidx = (long)p * C + cl;
     const float uc = u[cl];
-    TdState carry{num[sidx], den[sidx], (double)mx[sidx]};
+
+    if (wv == NW) {
+        // ---- fold wave: the chain from chunk to chunk.  Waits for the NW block
+        // states of chunk n, folds them in row order into the carried state,
+        // publishing each block's start state, and keeps the state after it.
+        __builtin_amdgcn_s_setprio(3);
+        TdState s{num[sidx], den[sidx], (double)mx[sidx]};
+        for (int n = 0; n < nc; ++n) {
+            const int S = min(64, L - 64 * n), nblk = (S + R - 1) / R, b = n & 1;
+            // No row wave reduces chunk n+2 before chunk n's start states are
+            // out, so the count of this parity covers chunks up to n only.
+            lds_wait_at_least(&red_cnt[b], NW * (n / 2 + 1));
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                ps[b][j][lane] = make_float2(s.aa, s.bb);
+                pm[b][j][lane] = s.m;
+                if (j < nblk) {
+                    const float2 a = zs[b][j][lane];
+                    const double2 x = zx[b][j][lane];
+                    absorb(s, TdBlock{a.x, a.y, x.x, x.y});
+                }
+            }
+            if (lane == 0) __hip_atomic_store(&ps_seq, n + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // the sums are rescaled to the FP32 maximum that is stored with them
+        if (valid) {
+            const float mf = (float)s.m;
+            const float f = s.m > -1e30 ? fast_exp((float)(s.m - (double)mf)) : 1.f;
+            num[sidx] = s.aa * f;
+            den[sidx] = s.bb * f;
+            mx[sidx] = mf;
+        }
+        return;
+    }
+
+    // ---- row waves.  In the step of chunk n a row wave reduces its block of
+    // chunk n+1, then waits for its start state of chunk n and replays its
+    // rows.  The longest prompts come first in the grid; their row waves get
+    // issue priority.
+    {
+        const int q4 = (4 * blockIdx.y) / gridDim.y;
+        if (q4 == 0) __builtin_amdgcn_s_setprio(2);
+        else if (q4 == 1) __builtin_amdgcn_s_setprio(1);
+    }
     // Rows go through buffer resources based at the workgroup's first channel
     // and the wave's first row: row offsets are uniform (scalar offset), the
     // channel offset is the same for every row, so no address is formed per
-    // access.  R rows x C channels of a resource stay below 2^31 bytes.
+    // access.  R rows x C channels of a resource stay below 2^31 bytes.  Loads
+    // are issued unconditionally (rows past the prompt re-read its last row),
+    // so that only the chunk about to be used is waited for; k, v, w and the
+    // output are touched once, so their accesses are nontemporal.
     const uint32_t lane_off = (uint32_t)(cl - blockIdx.x * 64) * 4;
     const float* k0 = k + row0 * C + blockIdx.x * 64;
     const float* v0 = v + row0 * C + blockIdx.x * 64;
     const float* w0 = w + row0 * C + blockIdx.x * 64;
-
-    float kb_[DEPTH + 1][R], vb_[DEPTH + 1][R], wb_[DEPTH + 1][R];  // ring of row buffers
-    // Loads are issued unconditionally (rows past the prompt re-read its last
-    // row), so that only the chunk about to be used is waited for; k, v, w and
-    // the output are touched once, so their accesses are nontemporal.
     auto fetch = [&](int c0, float (&kb)[R], float (&vb)[R], float (&wb)[R]) {
         const int r0 = min(c0 + R * wv, L - 1);
         const auto krs = buffer_rsrc(k0 + (long)r0 * C, (uint32_t)R * C * 4);
@@ -165,41 +227,22 @@ __global__ __launch_bounds__(NW * 64) void wkv_tdecay_kernel(const float* __rest
             wb[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wrs, lane_off, soff, kNontemporal));
         }
     };
-    int buf = 0;
-    auto chunk = [&](int c0, const float (&kb)[R], const float (&vb)[R], const float (&wb)[R]) {
-        const int S = min(64, L - c0);
-        const int nb = min(R, max(0, S - R * wv));  // rows of this wave's block
+    auto reduce = [&](int n, const float (&kb)[R], const float (&vb)[R], const float (&wb)[R]) {
+        const int S = min(64, L - 64 * n);
+        const int nb = min(R, max(0, S - R * wv));
         if (nb > 0) {
             const TdBlock z = nb == R ? reduce_block<R>(kb, vb, wb, R) : reduce_block<R>(kb, vb, wb, nb);
-            zs[buf][wv][lane] = make_float2(z.aa, z.bb);
-            zx[buf][wv][lane] = make_double2(z.zm, z.zd);
+            zs[n & 1][wv][lane] = make_float2(z.aa, z.bb);
+            zx[n & 1][wv][lane] = make_double2(z.zm, z.zd);
         }
-        __syncthreads();
-        if (c0 > 0) {
-            const float2 s2 = cs[buf ^ 1][lane];
-            carry = TdState{s2.x, s2.y, cm[buf ^ 1][lane]};
-        }
-        TdState s = carry;
-        const int jn = min(wv, (S + R - 1) / R);  // non-empty blocks before this wave's
-#pragma unroll
-        for (int j = 0; j < NW - 1; ++j)
-            if (j < jn) {
-                const float2 a = zs[buf][j][lane];
-                const double2 x = zx[buf][j][lane];
-                absorb(s, TdBlock{a.x, a.y, x.x, x.y});
-            }
-        if (wv == NW - 1) {
-            TdState e = s;
-            if (nb > 0) {
-                const float2 a = zs[buf][NW - 1][lane];
-                const double2 x = zx[buf][NW - 1][lane];
-                absorb(e, TdBlock{a.x, a.y, x.x, x.y});
-            }
-            cs[buf][lane] = make_float2(e.aa, e.bb);
-            cm[buf][lane] = e.m;
-            carry = e;
-        }
-        buf ^= 1;
+        if (lane == 0) __hip_atomic_fetch_add(&red_cnt[n & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto replay = [&](int n, const float (&kb)[R], const float (&vb)[R], const float (&wb)[R]) {
+        const int c0 = 64 * n, S = min(64, L - c0);
+        const int nb = min(R, max(0, S - R * wv));
+        lds_wait_at_least(&ps_seq, n + 1);
+        const float2 st = ps[n & 1][wv][lane];
+        TdState s{st.x, st.y, pm[n & 1][wv][lane]};
         // lanes past C store at an offset past the resource's end: dropped
         const auto ors = buffer_rsrc(wkv + (row0 + c0 + R * wv) * C + blockIdx.x * 64, (uint32_t)R * C * 4);
         const uint32_t st_off = valid ? lane_off : 0x80000000u;
@@ -212,28 +255,23 @@ __global__ __launch_bounds__(NW * 64) void wkv_tdecay_kernel(const float* __rest
             }
     };
 
-    if (L > 0) {
-#pragma unroll
-        for (int s = 0; s < DEPTH; ++s) fetch(64 * s, kb_[s], vb_[s], wb_[s]);
-    }
-    for (int c0 = 0; c0 < L; c0 += 64 * (DEPTH + 1)) {
-#pragma unroll
-        for (int s = 0; s <= DEPTH; ++s) {
-            const int cc = c0 + 64 * s;
-            if (cc >= L) break;
-            const int nx = (s + DEPTH) % (DEPTH + 1);
-            fetch(cc + 64 * DEPTH, kb_[nx], vb_[nx], wb_[nx]);
-            chunk(cc, kb_[s], vb_[s], wb_[s]);
-        }
-    }
-    // the last wave holds the state after the prompt (or the incoming one);
-    // the sums are rescaled to the FP32 maximum that is stored with them
-    if (wv == NW - 1 && valid) {
-        const float mf = (float)carry.m;
-        const float f = carry.m > -1e30 ? fast_exp((float)(carry.m - (double)mf)) : 1.f;
-        num[sidx] = carry.aa * f;
-        den[sidx] = carry.bb * f;
-        mx[sidx] = mf;
+    // A ring of three row buffers: chunk n (replayed), n+1 (reduced), n+2 (in flight).
+    float kb0[R], vb0[R], wb0[R], kb1[R], vb1[R], wb1[R], kb2[R], vb2[R], wb2[R];
+    fetch(0, kb0, vb0, wb0);
+    fetch(64, kb1, vb1, wb1);
+    reduce(0, kb0, vb0, wb0);
+    for (int n = 0; n < nc; n += 3) {
+        fetch(64 * (n + 2), kb2, vb2, wb2);
+        if (n + 1 < nc) reduce(n + 1, kb1, vb1, wb1);
+        replay(n, kb0, vb0, wb0);
+        if (n + 1 >= nc) break;
+        fetch(64 * (n + 3), kb0, vb0, wb0);
+        if (n + 2 < nc) reduce(n + 2, kb2, vb2, wb2);
+        replay(n + 1, kb1, vb1, wb1);
+        if (n + 2 >= nc) break;
+        fetch(64 * (n + 4), kb1, vb1, wb1);
+        if (n + 3 < nc) reduce(n + 3, kb0, vb0, wb0);
+        replay(n + 2, kb2, vb2, wb2);
     }
 }
 
@@ -243,10 +281,10 @@ hipError_t launch_wkv_tdecay(const float* k, const float* v, const float* w, con
                              float* den, float* mx, const Batch& bt, int C, hipStream_t st) {
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)bt.P);
     if (C % 64 == 0)
-        hipLaunchKernelGGL((wkv_tdecay_kernel<kTdWaves, kTdDepth, true>), grid, dim3(kTdWaves * 64), 0, st, k, v, w,
-                           u, wkv, num, den, mx, bt, C);
+        hipLaunchKernelGGL((wkv_tdecay_kernel<kTdWaves, true>), grid, dim3((kTdWaves + 1) * 64), 0, st, k, v, w, u,
+                           wkv, num, den, mx, bt, C);
     else
-        hipLaunchKernelGGL((wkv_tdecay_kernel<kTdWaves, kTdDepth, false>), grid, dim3(kTdWaves * 64), 0, st, k, v, w,
+        hipLaunchKernelGGL((wkv_tdecay_kernel<kTdWaves, false>), grid, dim3((kTdWaves + 1) * 64), 0, st, k, v, w,
                            u, wkv, num, den, mx, bt, C);
     return hipGetLastError();
 }
