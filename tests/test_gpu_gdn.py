@@ -174,16 +174,16 @@ def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv):
         r += n
 
 
-@pytest.mark.parametrize("dk,dv", [(32, 32), (128, 128)])
-def test_gdn_bf16_lanes(L, orc, dk, dv):
-    """16 value-head pairs of 16 key heads over 16 ragged prompts: more workgroups than compute
-    units, so the prompts run as lanes, several per workgroup row, with chunks of different
-    prompts back to back in one pipeline and the state swapped at each prompt boundary."""
-    Hk, Hv = 16, 32
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(32, 32, 16, 32), (128, 128, 16, 32), (32, 64, 12, 24), (64, 32, 4, 64)])
+def test_gdn_bf16_lanes(L, orc, dk, dv, Hk, Hv):
+    """Value heads over 16 ragged prompts with more workgroups than compute units, so the prompts
+    run as lanes (256 CUs: 8 lanes of 32 heads, 10 of 24, 4 of 64), several per workgroup row, with
+    chunks of different prompts back to back in one pipeline and the state swapped at each prompt
+    boundary."""
     lens = [300, 0, 64, 65, 1, 257, 130, 190, 17, 128, 45, 99, 200, 33, 70, 150]
     R, P = sum(lens), len(lens)
     assert P * Hv > torch.cuda.get_device_properties(0).multi_processor_count
-    rng = np.random.default_rng(910 + dk)
+    rng = np.random.default_rng(910 + dk + dv + Hv)
     q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
     k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
     v = rng.standard_normal((R, Hv, dv))
