@@ -316,8 +316,7 @@ lrc_status lrc_scan_prefill_ws(const float* a, const float* b, float* h, float* 
     REQUIRE(!overlap(workspace, need, a, tb) && !overlap(workspace, need, b, tb) && !overlap(workspace, need, h, tb) &&
                 !overlap(workspace, need, state, sb),
             LRC_ERR_ALIAS, "workspace overlaps a tensor");
-    REQUIRE((uint64_t)(rows / 64 + P) * (uint64_t)((E + 255) / 256) < (1ull << 31), LRC_ERR_SHAPE,
-            "too many tiles for one launch");
+    REQUIRE(lrc::scan_tiled_tiles_bound(rows, P, E) < (1l << 31), LRC_ERR_SHAPE, "too many tiles for one launch");
     auto st = static_cast<hipStream_t>(stream);
     return check_launch(lrc::launch_scan_tiled(a, b, h, state, bt, E, workspace, st), st, "scan prefill (tiled)");
 }

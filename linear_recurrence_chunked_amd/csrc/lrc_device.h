@@ -60,4 +60,17 @@ constexpr int kNontemporal = 2;  // cache-policy argument of the buffer builtins
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Bounded wait until an LDS counter reaches v (acquire, workgroup scope).  For
+// waits on another wave of the same workgroup that needs nothing from the
+// waiting one, so the bound (about 2^20 polls) is never reached in practice;
+// past it the wave goes on rather than hang.
+constexpr int kLdsWaitLimit = 1 << 20;
+__device__ __forceinline__ void lds_wait_at_least(int* x, int v) {
+    int n = 0;
+    while (__hip_atomic_load(x, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) {
+        if (++n > kLdsWaitLimit) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 }  // namespace lrc

@@ -38,6 +38,7 @@ hipError_t launch_conv(const void* x, void* y, const void* state_in, void* state
 hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0, float* hS, const Batch& bt,
                        long E, hipStream_t st);
 size_t scan_workspace_bytes(int P, long E);
+long scan_tiled_tiles_bound(long rows, int P, long E);  // at least the tiled scan's tile count
 hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
                              void* workspace, hipStream_t st);
 hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,

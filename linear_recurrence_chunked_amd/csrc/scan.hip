@@ -451,6 +451,10 @@ hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0
     return launch_cols<kScanCols>(a, b, h, h0, hS, bt, E, st);
 }
 
+long scan_tiled_tiles_bound(long rows, int P, long E) {
+    return (rows / kWave + P) * ((E + kScanTileCols - 1) / kScanTileCols);
+}
+
 size_t scan_workspace_bytes(int P, long E) {
     const long ncb = (E + kScanTileCols - 1) / kScanTileCols;
     return (size_t)P * ncb * sizeof(unsigned long long) + 256;

@@ -115,17 +115,6 @@ __device__ __forceinline__ TdBlock reduce_block(const float (&kb)[R], const floa
     return TdBlock{aa, bb, best, tail};
 }
 
-// Bounded wait on an LDS counter (no wave that one waits for needs anything
-// from the waiting wave, so the bound is never reached in practice).
-constexpr int kLdsWaitLimit = 1 << 20;
-__device__ __forceinline__ void lds_wait_at_least(int* x, int v) {
-    int n = 0;
-    while (__hip_atomic_load(x, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) {
-        if (++n > kLdsWaitLimit) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // NW row waves (a block of R = 64/NW rows each) and one fold wave.
 template <int NW, bool FULL>
 __global__ __launch_bounds__((NW + 1) * 64) void wkv_tdecay_kernel(const float* __restrict__ k,
