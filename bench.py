@@ -464,6 +464,8 @@ def main():
         if "flops" in work[k]:
             d["TFLOPs"] = work[k]["flops"] / (ms * 1e-3) / 1e12
             d["mfma_bf16_frac"] = d["TFLOPs"] / MFMA_BF16_PEAK_TFS
+        if k == "scan":  # carry hand-overs of the tiled driver that timed out over the whole run (expected 0)
+            d["handover_timeouts"] = lrc.scan_workspace_timeouts(W["scan_ws"])
         kern[k] = d
     nxt = measure_next_rows(lrc, dev, W["lens"]) if not args.only else None
     if nxt and "scan" in per_k:
