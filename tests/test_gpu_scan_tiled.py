@@ -125,3 +125,28 @@ def test_tiled_two_streams_at_once(L):
     for h, s, ref_h, ref_s, ws in outs:
         assert torch.equal(h, ref_h) and torch.equal(s, ref_s)
         assert L.scan_workspace_timeouts(ws) == 0
+
+
+def test_tiled_random_shapes_equal_long_lived(L):
+    """Seeded random batches (1-64 prompts of 0-700 rows, some exactly on chunk boundaries; 4-2048 state
+    elements, multiples of 4, so the tiled form runs): bit for bit the long-lived driver, no timeouts."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        P = int(rng.integers(1, 65))
+        lens = [int(x) for x in rng.integers(0, 701, size=P)]
+        for i in rng.choice(P, size=min(P, 3), replace=False):
+            lens[i] = int(rng.choice([0, 1, 63, 64, 65, 128]))
+        E = 4 * int(rng.integers(1, 513))
+        D = E // 4 if E % 16 else E // 16
+        N = E // D
+        a, b, h0 = _case(3000 + case, lens, D, N)
+        ta, tb = (to_dev(torch.from_numpy(x).float()) for x in (a, b))
+        th0 = to_dev(torch.from_numpy(h0).float())
+        h1, s1 = torch.empty_like(ta), th0.clone()
+        L.scan_prefill(ta, tb, h1, s1, lens)
+        ws = L.scan_workspace(P, D, N, "cuda")
+        h2, s2 = torch.empty_like(ta), th0.clone()
+        L.scan_prefill_ws(ta, tb, h2, s2, lens, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(h1, h2) and torch.equal(s1, s2), (case, P, E)
+        assert L.scan_workspace_timeouts(ws) == 0, (case, P, E)

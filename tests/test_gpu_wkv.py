@@ -117,3 +117,34 @@ def test_wkv_extreme_keys_and_decays_stay_finite(L, orc):
     assert torch.isfinite(out).all()
     assert rel_err(f64(out[0]), ref) < TOL_F32
     _check_state(num[0], den[0], mx[0], rn, rd, rm)
+
+
+def test_wkv4_random_batches_against_oracle(L, orc):
+    """Seeded random batches for the fold-wave pipeline: 1-24 prompts of 0-400 rows (some on chunk
+    boundaries), 1-200 channels, keys with +-30 spikes; every prompt against the float64 oracle from
+    a random finite incoming state."""
+    from linear_recurrence_chunked_amd import inputs
+
+    rng = np.random.default_rng(77)
+    for case in range(16):
+        P = int(rng.integers(1, 25))
+        lens = [int(x) for x in rng.integers(0, 401, size=P)]
+        lens[int(rng.integers(0, P))] = int(rng.choice([0, 1, 64, 65, 128]))
+        if sum(lens) == 0:
+            lens[0] = 5
+        C = int(rng.integers(1, 201))
+        d = inputs.rwkv_169m(rows=sum(lens), channels=C, seed=500 + case)
+        k, v, w, u = (to_dev(d[n]) for n in ("k", "v", "w", "u"))
+        num0 = rng.uniform(-2, 2, (P, C)); den0 = rng.uniform(0.5, 3, (P, C)); mx0 = rng.uniform(-5, 5, (P, C))
+        num, den, mx = (to_dev(torch.from_numpy(x).float()) for x in (num0, den0, mx0))
+        out = torch.empty_like(k)
+        L.wkv4_prefill(k, v, w, u, out, num, den, mx, lens)
+        torch.cuda.synchronize()
+        off = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+        for p in range(P):
+            sl = slice(off[p], off[p + 1])
+            st0 = [f64(torch.from_numpy(x[p]).float()) for x in (num0, den0, mx0)]
+            ro, rn, rd, rm = orc.wkv4(f64(d["k"][sl]), f64(d["v"][sl]), f64(d["w"]), f64(d["u"]), *st0)
+            if lens[p]:
+                assert rel_err(f64(out[sl]), ro) < TOL_F32, (case, p)
+            assert rel_err(f64(num[p] / den[p]), rn / rd) < TOL_F32, (case, p)
