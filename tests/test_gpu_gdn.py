@@ -246,3 +246,41 @@ def test_inverse_full_chunk_production_precision(L, orc, n, nkeys):
     for b in range(8):
         assert rel_err(got[b], ref[b]) < TOL_F32
     assert np.all(np.triu(got, 1) == 0) and np.all(np.diagonal(got, axis1=1, axis2=2) == 1)
+
+
+def test_gdn_bf16_random_lane_plans(L, orc):
+    """Seeded random batches with more (prompt, head) workgroups than compute units, so each one runs
+    a different lane plan: 9-40 prompts of 0-300 rows, 32 or 64 value heads over 16 key heads,
+    dk = dv = 32.  Every prompt and head against the float64 oracle."""
+    rng = np.random.default_rng(4242)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for case in range(6):
+        Hk, Hv, dk, dv = 16, int(rng.choice([32, 64])), 32, 32
+        P = int(rng.integers(cus // Hv + 1, 41))
+        lens = [int(x) for x in rng.integers(0, 301, size=P)]
+        lens[int(rng.integers(0, P))] = int(rng.choice([0, 64, 65]))
+        if sum(lens) == 0:
+            lens[0] = 7
+        R = sum(lens)
+        q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((R, Hv, dv))
+        beta = 1 / (1 + np.exp(-rng.standard_normal((R, Hv))))
+        g = -np.logaddexp(0, rng.standard_normal((R, Hv))) * 0.5
+        S0 = rng.normal(0, 0.1, (P, Hv, dk, dv))
+        t = {n: torch.from_numpy(a).float() for n, a in dict(beta=beta, g=g, S0=S0).items()}
+        for n, a in dict(q=q, k=k, v=v).items():
+            t[n] = torch.from_numpy(a).to(torch.bfloat16)
+        dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+        o = torch.full((R, Hv, dv), float("nan"), device="cuda")
+        L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+        torch.cuda.synchronize()
+        r = 0
+        for p, n in enumerate(lens):
+            sl = slice(r, r + n)
+            ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
+                                   f64(t["g"][sl]), f64(t["S0"][p]))
+            if n:
+                assert rel_err(f64(o[sl]), ref_o) < TOL_BF16, (case, p)
+            assert rel_err(f64(dS[p]), ref_s) < TOL_BF16, (case, p)
+            r += n
