@@ -473,7 +473,10 @@ hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* st
     tl.chunk_off[bt.P] = (int)tiles;
     if (tiles == 0) return hipSuccess;
     static std::atomic<unsigned> generation{0};
-    const unsigned gen = generation.fetch_add(1) + 1;  // 0 is never used: a zero-filled workspace holds no flag
+    unsigned gen;  // never 0 (also after wrapping): a zero-filled workspace holds no flag
+    do {
+        gen = generation.fetch_add(1) + 1;
+    } while (gen == 0);
     auto* ctl = static_cast<unsigned*>(workspace);  // first 256 bytes: [0] timeouts, [1] next ticket
     auto* flags = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + 256);
     const int ntickets = (int)(tiles * tl.ncb);
