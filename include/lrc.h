@@ -68,7 +68,9 @@ typedef enum {
     LRC_ERR_ALIAS = 7   /* an output overlaps an input it may not alias */
 } lrc_status;
 
-typedef enum { LRC_F32 = 0, LRC_BF16 = 1 } lrc_dtype;
+/* Element type of the inputs.  LRC_BF16_SPLIT (K3 only) takes bf16 inputs like
+   LRC_BF16 and changes how FP32 intermediates reach the bf16 matrix cores. */
+typedef enum { LRC_F32 = 0, LRC_BF16 = 1, LRC_BF16_SPLIT = 2 } lrc_dtype;
 
 /* ------------------------------------------------------------------------
  * K0  Depthwise causal short conv over rows  [mamba], [qwen]
@@ -191,8 +193,13 @@ lrc_status lrc_wkv4_prefill(const float* k, const float* v, const float* w, cons
  *  S_in        [B, Hv, dk, dv] float
  *  S_out       [B, Hv, dk, dv] float; may alias S_in
  *  dk, dv in {32, 64, 128}; Hk >= 1; Hv a multiple of Hk.
- *  dtype F32: FP32 arithmetic throughout.  dtype BF16: bf16 q/k/v, FP32
- *  state, decays, inverse and accumulation.
+ *  dtype F32: FP32 arithmetic throughout.  dtype BF16: bf16 q/k/v; the
+ *  state, decays, inverse and every accumulation are FP32, and an FP32
+ *  operand of a matrix product (S_0, T, the right-hand side, P, U) is
+ *  rounded to bf16 once.  dtype BF16_SPLIT: the same inputs, with each such
+ *  operand entered as a pair hi = bf16(x), lo = bf16(x - hi), about 16
+ *  mantissa bits, for about 1.45x the time.  Other calls reject BF16_SPLIT
+ *  with LRC_ERR_DTYPE.
  * ---------------------------------------------------------------------- */
 lrc_status lrc_gdn_chunk(const void* q, const void* k, const void* v, const float* beta,
                          const float* g, float* o, const float* S_in, float* S_out, int B, int S,

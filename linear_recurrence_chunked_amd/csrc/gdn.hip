@@ -338,7 +338,8 @@ __global__ __launch_bounds__(kThreads) void tri_inverse_kernel(const float* __re
 hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                       const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv, lrc_dtype dt,
                       hipStream_t st) {
-    if (dt == LRC_BF16) return launch_gdn_bf16_mfma(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+    if (dt == LRC_BF16 || dt == LRC_BF16_SPLIT)
+        return launch_gdn_bf16_mfma(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, dt == LRC_BF16_SPLIT, st);
     return dispatch_dk<float>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
 }
 

@@ -25,14 +25,14 @@
 //    end after the chunk's rows, so rows past it need no test.
 //  * 4 prep waves, which in step n prepare chunk n+1, the part that does not
 //    depend on the state: the inverse (diagonal tiles in A, level 16 in B,
-//    level 32 in C and D, each tile of T split to hi/lo bf16 once final) and
+//    level 32 in C and D, each tile of T rounded to bf16 once final) and
 //    the masked decayed Q K^T (D); they stage chunk n+2 into LDS (C) and form
 //    the rest of its masked K K^T (E), and keep the rows of chunk n+3 in
 //    flight.
 // LDS holds K and Q of two chunks (by chunk parity), the per-row gamma,
 // Gamma, beta and state-update decay of three, where the rows of four are
 // and which prompt they belong to, and one copy of A -> T (FP32),
-// T and P (hi/lo bf16) and K^T: each is written in a segment where no wave
+// T and P (bf16) and K^T: each is written in a segment where no wave
 // reads the copy it replaces.  About 147 KiB, one workgroup per CU.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
@@ -44,12 +44,15 @@
 // two 4-element runs of its row from LDS.  The masked products are computed
 // transposed (keys as rows), so each lane holds 4 consecutive keys of one
 // query and writes them as one packed store.
-// FP32 operands enter as a hi + lo pair of bf16 (hi = bf16(x),
-// lo = bf16(x - hi)), about 16 mantissa bits:
-//   K K^T, Q K^T        bf16 x bf16 (exact products)            1 pass
-//   K S_0, Q S_0        bf16 x (S_0 hi, lo)                     2 passes
-//   K^T (d U)           bf16 x (decayed U hi, lo)               2 passes
-//   T RHS, P U          (hi, lo) x (hi, lo) without lo x lo     3 passes
+// Accumulation is FP32 throughout.  An FP32 operand (S_0, the right-hand
+// side, T, P, decayed U) is rounded to bf16 once on its way into the matrix
+// cores.  With SPLIT it enters as a pair hi = bf16(x), lo = bf16(x - hi),
+// about 16 mantissa bits, at the cost of more passes:
+//                                                    passes    with SPLIT
+//   K K^T, Q K^T        bf16 x bf16 (exact)            1          1
+//   K S_0, Q S_0        bf16 x S_0                     1          2
+//   K^T (d U)           bf16 x decayed U               1          2
+//   T RHS, P U          FP32 x FP32                    1          3 (lo x lo dropped)
 // Decay factors: on the diagonal 16x16 tiles e^{gamma_i - gamma_j} is formed
 // per element; below them it is the product e^{gamma_i - gamma_c}
 // e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
@@ -93,15 +96,24 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
     const float rb = b - __uint_as_float(hi & 0xffff0000u);
     lo = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(ra), static_cast<__bf16>(rb)});
 }
-// B fragment from two accumulator tiles (rows 16t.. and 16t+16..): hi and lo parts.
+__device__ __forceinline__ uint32_t pack_pair(float a, float b) {
+    return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+}
+// B fragment from two accumulator tiles (rows 16t.. and 16t+16..): the bf16
+// values, and with SPLIT also the lo parts.
+template <bool SPLIT>
 __device__ __forceinline__ void acc_frag(const floatx4& t0, const floatx4& t1, bf16x8& hi, bf16x8& lo) {
     uint4 h, l;
-    split_pair(t0[0], t0[1], h.x, l.x);
-    split_pair(t0[2], t0[3], h.y, l.y);
-    split_pair(t1[0], t1[1], h.z, l.z);
-    split_pair(t1[2], t1[3], h.w, l.w);
+    if constexpr (SPLIT) {
+        split_pair(t0[0], t0[1], h.x, l.x);
+        split_pair(t0[2], t0[3], h.y, l.y);
+        split_pair(t1[0], t1[1], h.z, l.z);
+        split_pair(t1[2], t1[3], h.w, l.w);
+        lo = __builtin_bit_cast(bf16x8, l);
+    } else {
+        h = uint4{pack_pair(t0[0], t0[1]), pack_pair(t0[2], t0[3]), pack_pair(t1[0], t1[1]), pack_pair(t1[2], t1[3])};
+    }
     hi = __builtin_bit_cast(bf16x8, h);
-    lo = __builtin_bit_cast(bf16x8, l);
 }
 __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
@@ -128,16 +140,17 @@ __device__ __forceinline__ void read_ahead() {
     __builtin_amdgcn_sched_group_barrier(0x008, M * AHEAD, 0);
 }
 
-template <int DK>
+template <int DK, bool SPLIT>
 struct PipeSmem {
     static constexpr int LDK = DK + 8;
+    static constexpr int LO = SPLIT ? 64 * L64 : 8;  // the lo copies are used with SPLIT only
     __bf16 K[2][64 * LDK];  // chunk rows, by parity of the chunk index
     __bf16 Q[2][64 * LDK];
     __bf16 KT[DK * L64];    // K^T of the chunk whose state update comes next
-    __bf16 T_hi[64 * L64];  // (I + A)^-1 as hi/lo bf16
-    __bf16 T_lo[64 * L64];
+    __bf16 T_hi[64 * L64];  // (I + A)^-1 in bf16 (with SPLIT: hi and lo parts)
+    __bf16 T_lo[LO];
     __bf16 P_hi[64 * L64];  // masked decayed Q K^T
-    __bf16 P_lo[64 * L64];
+    __bf16 P_lo[LO];
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
     float gam[3][64];       // per-row values, by chunk index mod 3
@@ -146,7 +159,13 @@ struct PipeSmem {
     float decS[3][64];      // e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
     alignas(16) int meta[4][4];  // by chunk index mod 4: its first row, its rows, its prompt
 };
-static_assert(offsetof(PipeSmem<128>, meta) % 16 == 0 && offsetof(PipeSmem<32>, meta) % 16 == 0,
+template <bool SPLIT>
+constexpr bool meta_aligned() {
+    using Big = PipeSmem<128, SPLIT>;
+    using Small = PipeSmem<32, SPLIT>;
+    return offsetof(Big, meta) % 16 == 0 && offsetof(Small, meta) % 16 == 0;
+}
+static_assert(meta_aligned<true>() && meta_aligned<false>(),
               "a chunk's record is written as one 16-byte store");
 
 // Which prompts a workgroup row runs.  With n == 0, row y runs the prompt in
@@ -214,22 +233,23 @@ __device__ __forceinline__ floatx4 tile_decay(const float* gam, int ti, int tj, 
     return dec;
 }
 
-// One 16x16 tile of the FP32 matrix into the hi/lo bf16 copies.
+// One 16x16 tile of the FP32 matrix into its bf16 copy (with SPLIT: hi and lo copies).
+template <bool SPLIT>
 __device__ __forceinline__ void split_tile(const float* M, __bf16* hi, __bf16* lo, int ti, int tj, int lane) {
     const int r = 16 * ti + (lane >> 2), c = 16 * tj + 4 * (lane & 3);
     const floatx4 x = *reinterpret_cast<const floatx4*>(&M[r * kTriLd + c]);
     bf16x4 h, l;
     split4(x, h, l);
     *reinterpret_cast<bf16x4*>(&hi[r * L64 + c]) = h;
-    *reinterpret_cast<bf16x4*>(&lo[r * L64 + c]) = l;
+    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&lo[r * L64 + c]) = l;
 }
 
 // Masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M: tile
 // pairs first, first + stride, ... (NP of them; pairs past the last one are
 // computed but not stored).
-template <int DK, int NP>
-__device__ __forceinline__ void masked_kk(PipeSmem<DK>& sm, int b, int rbuf, int first, int stride) {
-    constexpr int LDK = PipeSmem<DK>::LDK;
+template <int DK, int NP, class Sm>
+__device__ __forceinline__ void masked_kk(Sm& sm, int b, int rbuf, int first, int stride) {
+    constexpr int LDK = Sm::LDK;
     constexpr int KS = DK / 32;
     int tid_c = threadIdx.x;
     asm volatile("" : "+v"(tid_c));
@@ -263,7 +283,7 @@ __device__ __forceinline__ void masked_kk(PipeSmem<DK>& sm, int b, int rbuf, int
 }
 
 // Grid (value heads, prompts); NS = dv / 32 state waves, then kPrep prep waves.
-template <int DK, int NS>
+template <int DK, int NS, bool SPLIT>
 __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const uint16_t* __restrict__ q,
                                                                         const uint16_t* __restrict__ k,
                                                                         const uint16_t* __restrict__ v,
@@ -273,10 +293,11 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                                                                         float* S_out, Batch bt, GdnLanes lanes,
                                                                         int Hk, int Hv, int dv) {
     static_assert(CG == 2, "a lane's column pair is one even and one odd column");
-    using Sm = PipeSmem<DK>;
+    using Sm = PipeSmem<DK, SPLIT>;
     constexpr int LDK = Sm::LDK;
     constexpr int KS = DK / 32;             // k-steps over dk
     constexpr int RT = DK / 16;             // state row tiles
+    constexpr int PS = SPLIT ? 2 : 1;       // passes of a product with one FP32 operand
     constexpr int PK = 64 * DK / 8;         // 16-byte pieces of a K (or Q) chunk
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 for (int s = 0; s < KS; ++s) {
                     bf16x8 bh[CG], bl[CG];
 #pragma unroll
-                    for (int c = 0; c < CG; ++c) acc_frag(sacc[c][2 * s], sacc[c][2 * s + 1], bh[c], bl[c]);
+                    for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(sacc[c][2 * s], sacc[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const bf16x8 ak = frag_perm(&sm.K[cb][(16 * t + lr) * LDK + 32 * s], lg);
@@ -385,13 +406,13 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             ks0[c][t] = mfma(ak, bh[c], ks0[c][t]);
-                            ks0[c][t] = mfma(ak, bl[c], ks0[c][t]);
+                            if constexpr (SPLIT) ks0[c][t] = mfma(ak, bl[c], ks0[c][t]);
                             qs0[c][t] = mfma(aq, bh[c], qs0[c][t]);
-                            qs0[c][t] = mfma(aq, bl[c], qs0[c][t]);
+                            if constexpr (SPLIT) qs0[c][t] = mfma(aq, bl[c], qs0[c][t]);
                         }
                     }
                 }
-                read_ahead<4 * KS, 2, 4 * CG, 2>();
+                read_ahead<4 * KS, 2, 2 * PS * CG, 2>();
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const floatx4 b4 = *reinterpret_cast<const floatx4*>(&sm.beta[rb][16 * t + lq]);
@@ -419,20 +440,23 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 for (int s = 0; s < 2; ++s) {
                     bf16x8 bh[CG], bl[CG];
 #pragma unroll
-                    for (int c = 0; c < CG; ++c) acc_frag(ks0[c][2 * s], ks0[c][2 * s + 1], bh[c], bl[c]);
+                    for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(ks0[c][2 * s], ks0[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
                         const bf16x8 ah = frag_perm(&sm.T_hi[(16 * t + lr) * L64 + 32 * s], lg);
-                        const bf16x8 al = frag_perm(&sm.T_lo[(16 * t + lr) * L64 + 32 * s], lg);
+                        bf16x8 al;
+                        if constexpr (SPLIT) al = frag_perm(&sm.T_lo[(16 * t + lr) * L64 + 32 * s], lg);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             u[c][t] = mfma(ah, bh[c], u[c][t]);
-                            u[c][t] = mfma(ah, bl[c], u[c][t]);
-                            u[c][t] = mfma(al, bh[c], u[c][t]);
+                            if constexpr (SPLIT) {
+                                u[c][t] = mfma(ah, bl[c], u[c][t]);
+                                u[c][t] = mfma(al, bh[c], u[c][t]);
+                            }
                         }
                     }
                 }
-                read_ahead<6, 2, 3 * CG, 2>();
+                read_ahead<6, SPLIT ? 2 : 1, (SPLIT ? 3 : 1) * CG, 2>();
             }
             __syncthreads();
 
@@ -447,20 +471,23 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 for (int s = 0; s < 2; ++s) {
                     bf16x8 bh[CG], bl[CG];
 #pragma unroll
-                    for (int c = 0; c < CG; ++c) acc_frag(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
+                    for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
                         const bf16x8 ah = frag_perm(&sm.P_hi[(16 * t + lr) * L64 + 32 * s], lg);
-                        const bf16x8 al = frag_perm(&sm.P_lo[(16 * t + lr) * L64 + 32 * s], lg);
+                        bf16x8 al;
+                        if constexpr (SPLIT) al = frag_perm(&sm.P_lo[(16 * t + lr) * L64 + 32 * s], lg);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             pu[c][t] = mfma(ah, bh[c], pu[c][t]);
-                            pu[c][t] = mfma(ah, bl[c], pu[c][t]);
-                            pu[c][t] = mfma(al, bh[c], pu[c][t]);
+                            if constexpr (SPLIT) {
+                                pu[c][t] = mfma(ah, bl[c], pu[c][t]);
+                                pu[c][t] = mfma(al, bh[c], pu[c][t]);
+                            }
                         }
                     }
                 }
-                read_ahead<6, 2, 3 * CG, 2>();
+                read_ahead<6, SPLIT ? 2 : 1, (SPLIT ? 3 : 1) * CG, 2>();
                 // Through a buffer resource that ends after the chunk's Sn rows: the
                 // stores of rows past it are dropped, with no per-row test.
                 Sn = meta(n, 1);
@@ -498,18 +525,18 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 for (int s = 0; s < 2; ++s) {
                     bf16x8 bh[CG], bl[CG];
 #pragma unroll
-                    for (int c = 0; c < CG; ++c) acc_frag(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
+                    for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int tr = 0; tr < RT; ++tr) {
                         const bf16x8 a = frag_perm(&sm.KT[(16 * tr + lr) * L64 + 32 * s], lg);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             sacc[c][tr] = mfma(a, bh[c], sacc[c][tr]);
-                            sacc[c][tr] = mfma(a, bl[c], sacc[c][tr]);
+                            if constexpr (SPLIT) sacc[c][tr] = mfma(a, bl[c], sacc[c][tr]);
                         }
                     }
                 }
-                read_ahead<2 * RT, 2, 2 * CG, 2>();
+                read_ahead<2 * RT, SPLIT ? 2 : 1, PS * CG, 2>();
             }
             if (do_next) {
                 // Through a buffer resource that ends after the chunk's S rows: rows
@@ -627,7 +654,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 sm.decS[rbuf][lane] = lane < S ? fast_exp(fminf(gS - x, 0.f)) : 0.f;
             }
         };
-        // masked decayed Q K^T of the chunk in buffers (b, rbuf) -> P as hi/lo, transposed (keys as rows)
+        // masked decayed Q K^T of the chunk in buffers (b, rbuf) -> P in bf16 (with SPLIT also its lo parts), transposed (keys as rows)
         auto masked_qk = [&](int b, int rbuf) {
             int tid_c = tid;
             asm volatile("" : "+v"(tid_c));
@@ -656,14 +683,16 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     bf16x4 ph, pl;
                     split4(pv4, ph, pl);
                     *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj + lq]) = ph;
-                    *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj + lq]) = pl;
+                    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj + lq]) = pl;
                 }
         };
 
         // Tiles above the diagonal stay zero for the whole prompt.
         for (int e = pt; e < 64 * kTriLd; e += PT) sm.M[e] = 0.f;
-        for (int e = pt; e < 64 * L64; e += PT)
-            sm.T_hi[e] = sm.T_lo[e] = sm.P_hi[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
+        for (int e = pt; e < 64 * L64; e += PT) {
+            sm.T_hi[e] = sm.P_hi[e] = static_cast<__bf16>(0.f);
+            if constexpr (SPLIT) sm.T_lo[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
+        }
         if (nc > 0) {
             fetch(0);
             stage(0, 0);
@@ -685,13 +714,13 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (do_next) tri::lvl16<kPrep>(sm.M, pw);
             __syncthreads();
 
-            // ---- C: level 32 (first half); the tiles of T that are final go to hi/lo;
+            // ---- C: level 32 (first half); the tiles of T that are final go to bf16;
             //      chunk n+2 into the buffers chunk n used, chunk n+3 in flight
             if (do_next) {
                 tri::lvl32a<kPrep>(sm.M, sm.scratch, pw);
-                split_tile(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
-                if (pw == 0) split_tile(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
-                if (pw == 1) split_tile(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
+                split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
+                if (pw == 0) split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
+                if (pw == 1) split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
             }
             if (do_stage) {
                 stage(n & 1, (n + 5) % 3);
@@ -703,12 +732,12 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (do_next) {
                 tri::lvl32b<kPrep>(sm.M, sm.scratch, pw);
                 tri::wave_sync();
-                split_tile(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
+                split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
                 masked_qk(nb, nrb);
             }
             __syncthreads();
 
-            // ---- E: A of chunk n+2 into M (T of chunk n+1 is in hi/lo now)
+            // ---- E: A of chunk n+2 into M (T of chunk n+1 is in bf16 now)
             if (do_stage) masked_kk<DK, 2>(sm, n & 1, (n + 5) % 3, pw, kPrep);  // tile pairs 0 .. 7
             __syncthreads();
         }
@@ -859,11 +888,11 @@ void lanes_for(const Batch& bt, int Hv, Batch& run, GdnLanes& lanes) {
     memo.lanes = lanes;
 }
 
-template <int DK, int NS>
+template <int DK, int NS, bool SPLIT>
 hipError_t launch_pipe(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                        const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dv, hipStream_t st) {
-    auto kern = gdn_pipe_kernel<DK, NS>;
-    const size_t smem = sizeof(PipeSmem<DK>);
+    auto kern = gdn_pipe_kernel<DK, NS, SPLIT>;
+    const size_t smem = sizeof(PipeSmem<DK, SPLIT>);
     // Opt in to more than 64 KiB of LDS once per process (a thread-safe static).
     static const hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -878,14 +907,26 @@ hipError_t launch_pipe(const void* q, const void* k, const void* v, const float*
     return hipGetLastError();
 }
 
-template <int NS>
+template <int NS, bool SPLIT>
 hipError_t launch_dk(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                      const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
                      hipStream_t st) {
     switch (dk) {
-        case 32: return launch_pipe<32, NS>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-        case 64: return launch_pipe<64, NS>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
-        case 128: return launch_pipe<128, NS>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 32: return launch_pipe<32, NS, SPLIT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 64: return launch_pipe<64, NS, SPLIT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+        case 128: return launch_pipe<128, NS, SPLIT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dv, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool SPLIT>
+hipError_t launch_dv(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
+                     const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk, int dv,
+                     hipStream_t st) {
+    switch (dv) {
+        case 32: return launch_dk<1, SPLIT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+        case 64: return launch_dk<2, SPLIT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
+        case 128: return launch_dk<4, SPLIT>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
     }
     return hipErrorInvalidValue;
 }
@@ -894,11 +935,9 @@ hipError_t launch_dk(const void* q, const void* k, const void* v, const float* b
 
 hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, const float* beta, const float* g,
                                 float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
-                                int dv, hipStream_t st) {
-    if (dv == 32) return launch_dk<1>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
-    if (dv == 64) return launch_dk<2>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
-    if (dv == 128) return launch_dk<4>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
-    return hipErrorInvalidValue;
+                                int dv, bool split, hipStream_t st) {
+    return split ? launch_dv<true>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st)
+                 : launch_dv<false>(q, k, v, beta, g, o, S_in, S_out, bt, Hk, Hv, dk, dv, st);
 }
 
 }  // namespace lrc

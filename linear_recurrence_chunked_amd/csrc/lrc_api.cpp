@@ -31,7 +31,7 @@ constexpr uint64_t kMaxElems = 1ull << 46;  // sanity bound on any tensor's elem
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t esize(lrc_dtype dt) { return dt == LRC_BF16 ? 2 : 4; }
+size_t esize(lrc_dtype dt) { return dt == LRC_BF16 || dt == LRC_BF16_SPLIT ? 2 : 4; }
 
 bool overlap(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
     if (!a || !b || abytes == 0 || bbytes == 0) return false;
@@ -181,7 +181,7 @@ lrc_status gdn_common(const void* q, const void* k, const void* v, const float* 
     REQUIRE_PTR_IF(q, rows > 0); REQUIRE_PTR_IF(k, rows > 0); REQUIRE_PTR_IF(v, rows > 0);
     REQUIRE_PTR_IF(beta, rows > 0); REQUIRE_PTR_IF(g, rows > 0); REQUIRE_PTR_IF(o, rows > 0);
     REQUIRE_PTR_IF(S_in, P > 0); REQUIRE_PTR_IF(S_out, P > 0);
-    REQUIRE(dt == LRC_F32 || dt == LRC_BF16, LRC_ERR_DTYPE, "unsupported dtype %d", (int)dt);
+    REQUIRE(dt == LRC_F32 || dt == LRC_BF16 || dt == LRC_BF16_SPLIT, LRC_ERR_DTYPE, "unsupported dtype %d", (int)dt);
     REQUIRE(Hk >= 1 && Hv >= 1 && Hv % Hk == 0, LRC_ERR_SHAPE, "value heads %d must be a positive multiple of key heads %d", Hv, Hk);
     REQUIRE(Hv <= 65535, LRC_ERR_SHAPE, "value heads %d > 65535", Hv);
     REQUIRE(dk == 32 || dk == 64 || dk == 128, LRC_ERR_SHAPE, "dk %d not in {32, 64, 128}", dk);

@@ -28,7 +28,7 @@ MAX_ROWS = 64
 MAX_PROMPTS = 256
 MAX_CONV_K = 8
 MAX_MIX = 8
-F32, BF16 = 0, 1
+F32, BF16, BF16_SPLIT = 0, 1, 2  # lrc_dtype
 
 STATUS = {0: "LRC_OK", 1: "LRC_ERR_NULL", 2: "LRC_ERR_ROWS", 3: "LRC_ERR_SHAPE", 4: "LRC_ERR_DTYPE",
           5: "LRC_ERR_ALIGN", 6: "LRC_ERR_LAUNCH", 7: "LRC_ERR_ALIAS"}
@@ -114,6 +114,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return BF16
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _gdn_dtype_code(q: torch.Tensor, split: bool) -> int:
+    code = _dtype_code(q)
+    if not split:
+        return code
+    if code != BF16:
+        raise ValueError("split applies to bf16 inputs only")
+    return BF16_SPLIT
 
 
 def _need(t: torch.Tensor, dtype, shape, name: str) -> None:
@@ -281,9 +290,10 @@ def wkv_tdecay_prefill(k, v, w, u, wkv, num, den, mx, lens):
 
 
 # ------------------------------------------------------------------ K3 gdn
-def gdn_chunk(q, k, v, beta, g, o, S_in, S_out):
+def gdn_chunk(q, k, v, beta, g, o, S_in, S_out, split=False):
     """q, k [B, S, Hk, dk]; v [B, S, Hv, dv] (f32 or bf16); beta, g [B, S, Hv] f32;
-    o [B, S, Hv, dv] f32; S_in, S_out [B, Hv, dk, dv] f32 (may be the same tensor)."""
+    o [B, S, Hv, dv] f32; S_in, S_out [B, Hv, dk, dv] f32 (may be the same tensor).
+    split (bf16 only): FP32 operands of the matrix products as hi + lo bf16 pairs."""
     _dev(q, k, v, beta, g, o, S_in, S_out)
     B, S, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
@@ -295,12 +305,12 @@ def gdn_chunk(q, k, v, beta, g, o, S_in, S_out):
     _need(S_in, torch.float32, (B, Hv, dk, dv), "S_in")
     _need(S_out, torch.float32, (B, Hv, dk, dv), "S_out")
     _check(lib.lrc_gdn_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o), _ptr(S_in), _ptr(S_out),
-                             B, S, Hk, Hv, dk, dv, _dtype_code(q), _stream(q)))
+                             B, S, Hk, Hv, dk, dv, _gdn_dtype_code(q, split), _stream(q)))
 
 
-def gdn_prefill(q, k, v, beta, g, o, state, lens):
+def gdn_prefill(q, k, v, beta, g, o, state, lens, split=False):
     """q, k [R, Hk, dk]; v [R, Hv, dv]; beta, g [R, Hv]; o [R, Hv, dv] packed rows;
-    state [P, Hv, dk, dv] f32 updated in place."""
+    state [P, Hv, dk, dv] f32 updated in place.  split as in gdn_chunk."""
     _dev(q, k, v, beta, g, o, state)
     R, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
@@ -314,7 +324,7 @@ def gdn_prefill(q, k, v, beta, g, o, state, lens):
     _need(o, torch.float32, (R, Hv, dv), "o")
     _need(state, torch.float32, (P, Hv, dk, dv), "state")
     _check(lib.lrc_gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o), _ptr(state), arr, P,
-                               Hk, Hv, dk, dv, _dtype_code(q), _stream(q)))
+                               Hk, Hv, dk, dv, _gdn_dtype_code(q, split), _stream(q)))
 
 
 def unit_lower_inverse(A, T):

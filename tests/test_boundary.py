@@ -109,6 +109,7 @@ def test_conv_rejects_bad_width_dtype_rows(L):
     assert _st(L, f(A0, A1, A2, A3, A4, None, 1, 8, 16, 0, 0, None)) == "LRC_ERR_SHAPE"
     assert _st(L, f(A0, A1, A2, A3, A4, None, 1, 8, 16, 9, 0, None)) == "LRC_ERR_SHAPE"
     assert _st(L, f(A0, A1, A2, A3, A4, None, 1, 8, 16, 4, 7, None)) == "LRC_ERR_DTYPE"
+    assert _st(L, f(A0, A1, A2, A3, A4, None, 1, 8, 16, 4, L.BF16_SPLIT, None)) == "LRC_ERR_DTYPE"  # K3 only
     assert _st(L, f(A0, A1, A2, A3, A4, None, 1, 65, 16, 4, 0, None)) == "LRC_ERR_ROWS"
     assert _st(L, f(A0, A0, A2, A3, A4, None, 1, 8, 16, 4, 0, None)) == "LRC_ERR_ALIAS"
     assert _st(L, f(A0, A1, None, A3, A4, None, 1, 8, 16, 4, 0, None)) == "LRC_ERR_NULL"
@@ -142,6 +143,7 @@ def test_gdn_rejects(L):
     assert _st(L, f(*ok_args, 1, 8, 2, 4, 48, 64, 1, None)) == "LRC_ERR_SHAPE"   # dk
     assert _st(L, f(*ok_args, 1, 8, 2, 4, 64, 256, 1, None)) == "LRC_ERR_SHAPE"  # dv
     assert _st(L, f(*ok_args, 1, 8, 2, 4, 64, 64, 5, None)) == "LRC_ERR_DTYPE"
+    assert _st(L, f(*ok_args, 1, 8, 2, 4, 64, 256, L.BF16_SPLIT, None)) == "LRC_ERR_SHAPE"  # split is a K3 dtype
     bad = list(ok_args)
     bad[5] = A0  # o aliases q
     assert _st(L, f(*bad, 1, 8, 2, 4, 64, 64, 1, None)) == "LRC_ERR_ALIAS"

@@ -2,7 +2,8 @@
 against the float64 oracle.
 
 Workloads: small (8 heads, dk = dv = 64, 75 rows as 64 + 11) in fp32 (tol
-1e-4) and bf16 (tol 2e-2); the stress case of nearly parallel keys
+1e-4) and bf16 (tol 2e-2; the split bf16 form, whose FP32 operands enter the
+matrix cores as hi + lo pairs, to 1e-4); the stress case of nearly parallel keys
 (cosine > 0.999) with beta = 0.99, for 16, 32 and 64 such keys; the 9B-like
 shape (32 value heads on 16 key heads, 128 x 128, 2048 rows as 32 x 64 chunks,
 bf16, decays from -1e-3 to -8 per row); ragged batches.  The inverse is
@@ -27,7 +28,7 @@ def L():
     return lrc
 
 
-def _run_chunked(L, d, splits):
+def _run_chunked(L, d, splits, split=False):
     q, k, v, beta, g, S0 = (to_dev(d[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
     R, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
@@ -36,19 +37,19 @@ def _run_chunked(L, d, splits):
     for r, n in chunks(R, splits):
         oc = torch.empty((1, n, Hv, dv), device=q.device)
         L.gdn_chunk(q[r:r + n][None].contiguous(), k[r:r + n][None].contiguous(), v[r:r + n][None].contiguous(),
-                    beta[r:r + n][None].contiguous(), g[r:r + n][None].contiguous(), oc, st, st)
+                    beta[r:r + n][None].contiguous(), g[r:r + n][None].contiguous(), oc, st, st, split=split)
         o[r:r + n] = oc[0]
     torch.cuda.synchronize()
     return o, st[0]
 
 
-def _run_prefill(L, d):
+def _run_prefill(L, d, split=False):
     q, k, v, beta, g, S0 = (to_dev(d[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
     R = q.shape[0]
     Hv, dv = v.shape[1], v.shape[2]
     o = torch.empty((R, Hv, dv), device=q.device)
     st = S0.clone().unsqueeze(0)
-    L.gdn_prefill(q, k, v, beta, g, o, st, [R])
+    L.gdn_prefill(q, k, v, beta, g, o, st, [R], split=split)
     torch.cuda.synchronize()
     return o, st[0]
 
@@ -284,3 +285,42 @@ def test_gdn_bf16_random_lane_plans(L, orc):
                 assert rel_err(f64(o[sl]), ref_o) < TOL_BF16, (case, p)
             assert rel_err(f64(dS[p]), ref_s) < TOL_BF16, (case, p)
             r += n
+
+
+TOL_SPLIT = 1e-4  # hi + lo bf16 pairs carry about 16 mantissa bits
+
+
+def _split_case(name):
+    from linear_recurrence_chunked_amd import inputs
+
+    if name == "small":
+        return inputs.gdn_small(dtype=torch.bfloat16)
+    if name == "parallel64":
+        return inputs.gdn_small(dtype=torch.bfloat16, parallel_keys=64, parallel_start=0, beta_const=0.99)
+    return inputs.gdn_9b()
+
+
+@pytest.mark.parametrize("case", ["small", "parallel64", "9b"])
+def test_gdn_bf16_split_precision(L, orc, case):
+    """The split form against the oracle at 1e-4, and the default single
+    rounding on the same inputs within the bf16 tolerance."""
+    d = _split_case(case)
+    ref_o, ref_s = _oracle(orc, d)
+    o, s = _run_prefill(L, d, split=True)
+    assert rel_err(f64(o), ref_o) < TOL_SPLIT
+    assert rel_err(f64(s), ref_s) < TOL_SPLIT
+    o1, s1 = _run_prefill(L, d)
+    assert rel_err(f64(o1), ref_o) < TOL_BF16
+    assert rel_err(f64(s1), ref_s) < TOL_BF16
+
+
+def test_gdn_bf16_split_chunked_and_rejects_f32(L, orc):
+    from linear_recurrence_chunked_amd import inputs
+
+    d = inputs.gdn_small(dtype=torch.bfloat16)
+    ref_o, ref_s = _oracle(orc, d)
+    o, s = _run_chunked(L, d, [7, 4, 64], split=True)
+    assert rel_err(f64(o), ref_o) < TOL_SPLIT
+    assert rel_err(f64(s), ref_s) < TOL_SPLIT
+    with pytest.raises(ValueError):
+        _run_prefill(L, inputs.gdn_small(dtype=torch.float32), split=True)
