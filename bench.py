@@ -313,6 +313,22 @@ ALU_LANE_SLOTS = 256 * 4 * 16 * 2.4e9
 MIXER_SLOTS_PER_STEP = 8
 
 
+def time_launch(fn, stream, reps=10):
+    """Average ms of fn() over reps launches on stream, after two untimed ones."""
+    import torch
+
+    for _ in range(2):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def measure_next_rows(lrc, dev, lens, reps=10):
     """Time the rows beyond the step's hot path -- the RWKV-4 time shift (three mixed inputs at
     the RWKV width), the fused Mamba mixer rows (Mamba width) and the WKV with a token-dependent
@@ -467,6 +483,11 @@ def main():
         if k == "scan":  # carry hand-overs of the tiled driver that timed out over the whole run (expected 0)
             d["handover_timeouts"] = lrc.scan_workspace_timeouts(W["scan_ws"])
         kern[k] = d
+    if "gdn" in kern:  # the same launch with FP32 operands as hi + lo bf16 pairs (LRC_BF16_SPLIT), not in `value`
+        ms = time_launch(lambda: lrc.gdn_prefill(W["q"], W["gk"], W["gv"], W["beta"], W["g"], W["o"], W["S"],
+                                                 W["lens"], split=True), stream)
+        tf = work["gdn"]["flops"] / (ms * 1e-3) / 1e12
+        kern["gdn"]["split_form"] = {"ms": round(ms, 4), "TFLOPs": tf, "mfma_bf16_frac": tf / MFMA_BF16_PEAK_TFS}
     nxt = measure_next_rows(lrc, dev, W["lens"]) if not args.only else None
     if nxt and "scan" in per_k:
         nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
