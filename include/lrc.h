@@ -218,9 +218,9 @@ lrc_status lrc_gdn_prefill(const void* q, const void* k, const void* v, const fl
 lrc_status lrc_unit_lower_inverse(const float* A, float* T, int batch, int n, void* stream);
 
 /* ------------------------------------------------------------------------
- * RWKV-4 time shift ([rwkv]: each mixed input blends row t with row t-1,
- * row 0 with the incoming shift state; the next shift state is the chunk's
- * last row).  For each of M mixing vectors mu_j:
+ * RWKV-4 time shift ([rwkv]: every mixed input combines each row with the
+ * previous one, and the first row with the carried shift state; the chunk's
+ * last row becomes the next shift state).  For each of M mixing vectors mu_j:
  *   out[j][t][c] = mu_j[c] x[t][c] + (1 - mu_j[c]) x[t-1][c],  x[-1] = state_in
  *   state_out    = x[S-1]  (state_in if S = 0)
  * One pass over x writes all M mixed inputs.
@@ -264,7 +264,7 @@ lrc_status lrc_mamba_mixer_prefill(const float* x, const float* dt, const float*
 
 /* ------------------------------------------------------------------------
  * WKV with a token-dependent decay.  [rwkv], Notes For Future Readers, says
- * that RWKV versions whose decay depends on the token need another chunk
+ * that RWKV generations with a per-token decay call for a different chunk
  * form, and gives none; this is the reading that the RWKV-4 recurrence above
  * takes a decay w_t per row and channel in place of w:
  *   A_t = e^{w_t} A_{t-1} + e^{k_t} v_t,  B_t = e^{w_t} B_{t-1} + e^{k_t},

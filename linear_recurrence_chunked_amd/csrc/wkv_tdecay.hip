@@ -1,8 +1,8 @@
 // WKV with a token-dependent decay, FP32 sums with FP64 exponents, on gfx950.
 //
 // Source: "perf(rwkv): prefill text prompts in multi-token chunks", Notes For
-// Future Readers -- RWKV versions whose decay depends on the token need
-// another chunk form than the RWKV-4 one.  The pages give no formula for those
+// Future Readers -- RWKV generations with a per-token decay call for a
+// different chunk form from the RWKV-4 one.  The pages give no formula for those
 // versions; this kernel computes the RWKV-4 recurrence with the channel decay
 // w replaced by a decay w_t of each row:
 //   A_t = e^{w_t} A_{t-1} + e^{k_t} v_t,   B_t = e^{w_t} B_{t-1} + e^{k_t},

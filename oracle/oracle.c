@@ -151,7 +151,7 @@ void oracle_wkv4(const double* k, const double* v, const double* w, const double
 
 /*
  * WKV with a token-dependent decay ("perf(rwkv): ...", Notes For Future
- * Readers: RWKV versions whose decay depends on the token need another chunk
+ * Readers: RWKV generations with a per-token decay call for a different chunk
  * form).  The pages give no formula for those versions; the reading here is
  * the RWKV-4 step above with the channel decay w replaced by a decay w_t of
  * the row (w_t < 0), applied where the state moves past row t:

@@ -2,8 +2,8 @@
 mixer rows -- against the float64 oracle.
 
 Time shift: "perf(rwkv): prefill text prompts in multi-token chunks",
-Implementation (row t blends with row t - 1, row 0 with the incoming shift
-state).  Mixer rows: "perf(mamba): prefill text prompts in multi-token
+Implementation (each row mixed with the row before it, the first row with
+the carried shift state).  Mixer rows: "perf(mamba): prefill text prompts in multi-token
 chunks", Implementation (the scan between forming a, b and reading h out),
 read as a = exp(dt A), b = dt B x, y = C.h + D x.
 

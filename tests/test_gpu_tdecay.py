@@ -1,8 +1,8 @@
 """GPU parity of the WKV with a token-dependent decay against the float64 oracle.
 
 Reading ("perf(rwkv): prefill text prompts in multi-token chunks", Notes For
-Future Readers: versions whose decay depends on the token need another chunk
-form): the RWKV-4 recurrence with a decay w_t per row and channel.
+Future Readers: RWKV generations with a per-token decay call for a different
+chunk form): the RWKV-4 recurrence with a decay w_t per row and channel.
 Workloads: the 169M-like RWKV-4 recipe with w_t = -exp(U(-6, 2)) drawn per
 row and channel, 128 rows from a 32-row warm-up state run by the oracle; the
 mixed prefill lengths at the RWKV-4 width of 2560 channels from fresh states;

@@ -1,8 +1,8 @@
 """Pins for the oracle's RWKV-4 time shift and its fused Mamba mixer rows.
 
 Time shift -- "perf(rwkv): prefill text prompts in multi-token chunks",
-Implementation: row t blends with row t - 1, row 0 with the incoming shift
-state; the next state is the last row.  Pins: the two one-hot mixes reproduce
+Implementation: each row is mixed with the row before it, the first row with
+the carried shift state; the next state is the last row.  Pins: the two one-hot mixes reproduce
 the rows and the shifted rows exactly, a mix is the same affine combination
 of those two, chunk splits carry the state exactly, an empty chunk keeps it.
 

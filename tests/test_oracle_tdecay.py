@@ -1,7 +1,7 @@
 """Pins for the oracle's WKV with a token-dependent decay.
 
 "perf(rwkv): prefill text prompts in multi-token chunks", Notes For Future
-Readers: RWKV versions whose decay depends on the token need another chunk
+Readers: RWKV generations with a per-token decay call for a different chunk
 form.  The pages print no formula for those versions; the oracle reads the
 decay of the RWKV-4 step as a decay w_t of the row,
     A_t = e^{w_t} A_{t-1} + e^{k_t} v_t,   B_t = e^{w_t} B_{t-1} + e^{k_t},
