@@ -19,6 +19,8 @@ from helpers import TOL_BF16, TOL_F32, rel_err
 
 pytestmark = pytest.mark.gpu
 
+TOL_SPLIT = 1e-4  # hi + lo bf16 pairs carry about 16 mantissa bits
+
 
 @pytest.fixture(scope="module")
 def L():
@@ -142,12 +144,16 @@ def test_gdn_ragged_batch(L, orc, dk, dv, Hk, Hv):
         r += n
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("dk,dv,Hk,Hv", [(32, 32, 8, 16), (64, 32, 16, 64), (32, 64, 12, 24), (32, 32, 4, 4),
-                                         (64, 128, 2, 32), (32, 32, 8, 128)])
-def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv):
+                                         (64, 128, 2, 32), (32, 32, 8, 128), (32, 128, 1, 2), (64, 64, 2, 4),
+                                         (128, 32, 2, 4), (128, 64, 4, 8)])
+def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv, split):
     """The bf16 matrix-core path over ragged prompts with value-head groups of 1, 2, 4 and 16.
     Groups whose value heads fill whole multiples of 8 groups are placed so that siblings share
-    an XCD; the others keep the plain order: both must give every head its own key head."""
+    an XCD; the others keep the plain order: both must give every head its own key head.  Every
+    (dk, dv) build of the kernel runs in both forms (single rounding, and split at 1e-4)."""
+    tol = TOL_SPLIT if split else TOL_BF16
     rng = np.random.default_rng(900 + dk + dv + Hk + Hv)
     lens = [1, 64, 0, 65, 130, 7]
     R, P = sum(lens), len(lens)
@@ -162,7 +168,7 @@ def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv):
         t[n] = torch.from_numpy(a).to(torch.bfloat16)
     dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
     o = torch.full((R, Hv, dv), float("nan"), device="cuda")
-    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens, split=split)
     torch.cuda.synchronize()
     r = 0
     for p, n in enumerate(lens):
@@ -170,17 +176,19 @@ def test_gdn_bf16_head_layouts(L, orc, dk, dv, Hk, Hv):
         ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
                                f64(t["g"][sl]), f64(t["S0"][p]))
         if n:
-            assert rel_err(f64(o[sl]), ref_o) < TOL_BF16
-        assert rel_err(f64(dS[p]), ref_s) < TOL_BF16
+            assert rel_err(f64(o[sl]), ref_o) < tol
+        assert rel_err(f64(dS[p]), ref_s) < tol
         r += n
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("dk,dv,Hk,Hv", [(32, 32, 16, 32), (128, 128, 16, 32), (32, 64, 12, 24), (64, 32, 4, 64)])
-def test_gdn_bf16_lanes(L, orc, dk, dv, Hk, Hv):
+def test_gdn_bf16_lanes(L, orc, dk, dv, Hk, Hv, split):
     """Value heads over 16 ragged prompts with more workgroups than compute units, so the prompts
     run as lanes (256 CUs: 8 lanes of 32 heads, 10 of 24, 4 of 64), several per workgroup row, with
     chunks of different prompts back to back in one pipeline and the state swapped at each prompt
     boundary."""
+    tol = TOL_SPLIT if split else TOL_BF16
     lens = [300, 0, 64, 65, 1, 257, 130, 190, 17, 128, 45, 99, 200, 33, 70, 150]
     R, P = sum(lens), len(lens)
     assert P * Hv > torch.cuda.get_device_properties(0).multi_processor_count
@@ -196,11 +204,11 @@ def test_gdn_bf16_lanes(L, orc, dk, dv, Hk, Hv):
         t[n] = torch.from_numpy(a).to(torch.bfloat16)
     dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
     o = torch.full((R, Hv, dv), float("nan"), device="cuda")
-    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens, split=split)
     torch.cuda.synchronize()
     first = (o.clone(), dS.clone())
     dS.copy_(to_dev(t["S0"]))
-    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)  # same lengths again: the kept plan
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens, split=split)  # same lengths again: the kept plan
     torch.cuda.synchronize()
     assert torch.equal(first[0], o) and torch.equal(first[1], dS)
     r = 0
@@ -209,8 +217,8 @@ def test_gdn_bf16_lanes(L, orc, dk, dv, Hk, Hv):
         ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
                                f64(t["g"][sl]), f64(t["S0"][p]))
         if n:
-            assert rel_err(f64(o[sl]), ref_o) < TOL_BF16
-        assert rel_err(f64(dS[p]), ref_s) < TOL_BF16
+            assert rel_err(f64(o[sl]), ref_o) < tol
+        assert rel_err(f64(dS[p]), ref_s) < tol
         r += n
 
 
@@ -286,8 +294,6 @@ def test_gdn_bf16_random_lane_plans(L, orc):
             assert rel_err(f64(dS[p]), ref_s) < TOL_BF16, (case, p)
             r += n
 
-
-TOL_SPLIT = 1e-4  # hi + lo bf16 pairs carry about 16 mantissa bits
 
 
 def _split_case(name):
