@@ -12,9 +12,10 @@
 // formed element by element from differences of gamma (never as ratios of
 // Gamma, which under- and overflow at large decays).
 //
-// This file holds the FP32-input path (bf16 inputs run on the matrix cores,
-// in gdn_mfma.hip): every contraction is an FP32 FMA loop over tiles staged
-// in LDS.  A workgroup owns one value head and a DVT-wide slice
+// This file holds the FP32-input path (bf16 inputs run on the bf16 matrix
+// cores, in gdn_mfma.hip): every contraction is a product of 16x16 tiles
+// staged in LDS, on the FP32 matrix cores (v_mfma_f32_16x16x4f32) with FP32
+// accumulation.  A workgroup owns one value head and a DVT-wide slice
 // of dv for one prompt, keeps that slice of the state resident in LDS while
 // it walks the prompt's chunks, and writes the state back once at the end.
 #include "lrc_device.h"
@@ -24,7 +25,8 @@
 namespace lrc {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // the standalone inverse
+constexpr int kChunkThreads = 1024;  // the chunk kernel: four waves per SIMD
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
@@ -32,6 +34,13 @@ template <>
 __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+// Lower-triangular 16x16 tile pair pr = 0 .. 9 (row tile ti, column tile tj)
+// of a 64x64 matrix, row by row: (0,0), (1,0), (1,1), (2,0), ...
+__device__ __forceinline__ void tile_pair(int pr, int& ti, int& tj) {
+    ti = (pr >= 1) + (pr >= 3) + (pr >= 6);
+    tj = pr - ti * (ti + 1) / 2;
+}
 
 // Inclusive prefix sum over the 64 lanes of one wave.
 __device__ __forceinline__ float wave_inclusive_sum(float x) {
@@ -57,10 +66,11 @@ struct GdnSmem {
     float scratch[kTriScratch];
     float gam[64];
     float beta[64];
+    alignas(16) float decS[64];  // e^{min(gamma_S - gamma_r, 0)}
 };
 
 template <typename TIN, int DK, int DVT>
-__global__ __launch_bounds__(kThreads) void gdn_f32_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
+__global__ __launch_bounds__(kChunkThreads) void gdn_f32_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
                                                           const TIN* __restrict__ v, const float* __restrict__ beta,
                                                           const float* __restrict__ g, float* __restrict__ o,
                                                           const float* S_in, float* S_out, Batch bt, int Hk, int Hv,
@@ -81,21 +91,29 @@ __global__ __launch_bounds__(kThreads) void gdn_f32_kernel(const TIN* __restrict
 
     // State slice S[:, vt*DVT : (vt+1)*DVT] of (prompt p, head h).
     const long sbase = ((long)p * Hv + h) * DK * dv + vt * DVT;
-    for (int e = tid; e < DK * DVT; e += kThreads) {
+    for (int e = tid; e < DK * DVT; e += kChunkThreads) {
         const int r = e / DVT, c = e % DVT;
         sm.S[r * LDV + c] = S_in[sbase + (long)r * dv + c];
     }
 
-    // Thread tiles: rows 4*ti .. 4*ti+3 of a 64-row operand, CPT columns.
-    const int ti = tid >> 4, tj = tid & 15;
-    constexpr int CPT = DVT / 16;   // columns of a [64 x DVT] output per thread
-    constexpr int RPS = DK / 16;    // state rows per thread
+    // Products run as 16x16 tiles on the FP32 matrix cores, dealt to the waves.
+    constexpr int kWaves = kChunkThreads / 64;
+    constexpr int NCT = DVT / 16;                      // column tiles of a [64 x DVT] operand
+    constexpr int NT = 4 * NCT, NS = (DK / 16) * NCT;  // [64 x DVT] tiles, state tiles
+    constexpr int TPW = (NT + kWaves - 1) / kWaves;    // per wave, the last ones maybe idle
+    constexpr int SPW = (NS + kWaves - 1) / kWaves;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int lr, lg;
+    tri::lanes(lr, lg);
+    const tri_f4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // Tiles above the diagonal of A (then T) and P stay zero for the whole prompt.
+    for (int e = tid; e < 64 * kTriLd; e += kChunkThreads) sm.M[e] = sm.P[e] = 0.f;
 
     for (int c0 = 0; c0 < L; c0 += 64) {
         const int S = min(64, L - c0);
         __syncthreads();  // previous chunk finished with every tile
         // ---- stage the chunk: K, Q [64 x DK], V slice [64 x DVT], beta, g
-        for (int e = tid; e < 64 * DK; e += kThreads) {
+        for (int e = tid; e < 64 * DK; e += kChunkThreads) {
             const int r = e / DK, d = e % DK;
             float kv = 0.f, qv = 0.f;
             if (r < S) {
@@ -106,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void gdn_f32_kernel(const TIN* __restrict
             sm.K[r * LDK + d] = kv;
             sm.Q[r * LDK + d] = qv;
         }
-        for (int e = tid; e < 64 * DVT; e += kThreads) {
+        for (int e = tid; e < 64 * DVT; e += kChunkThreads) {
             const int r = e / DVT, c = e % DVT;
             sm.U[r * LDV + c] = r < S ? to_f32(v[((row0 + c0 + r) * Hv + h) * (long)dv + vt * DVT + c]) : 0.f;
         }
@@ -114,167 +132,135 @@ __global__ __launch_bounds__(kThreads) void gdn_f32_kernel(const TIN* __restrict
             const bool ok = tid < S;
             const float gv = ok ? g[(row0 + c0 + tid) * Hv + h] : 0.f;
             sm.beta[tid] = ok ? beta[(row0 + c0 + tid) * Hv + h] : 0.f;
-            sm.gam[tid] = wave_inclusive_sum(gv);
+            const float x = wave_inclusive_sum(gv);
+            sm.gam[tid] = x;
+            sm.decS[tid] = fast_exp(fminf(__shfl(x, S - 1, 64) - x, 0.f));  // 1 past the chunk
         }
         __syncthreads();
 
-        // ---- A (strictly lower) and P (lower with diagonal) from K K^T and Q K^T
-        {
-            float kk[4][4] = {}, qk[4][4] = {};
-            if (tj <= ti) {
-                for (int d = 0; d < DK; d += 4) {
-                    float4 ki[4], qi[4], kj[4];
+        // ---- A (strictly lower) and P (lower with diagonal) from K K^T and Q K^T:
+        //      the 10 lower 16x16 tiles of each, over the waves
+        for (int x = w; x < 20; x += kWaves) {
+            const bool isq = x >= 10;
+            int ti, tj;
+            tile_pair(isq ? x - 10 : x, ti, tj);
+            const float* X = (isq ? sm.Q : sm.K) + 16 * ti * LDK;
+            const float* Y = sm.K + 16 * tj * LDK;
+            tri_f4 acc = zero4;
+#pragma unroll 4
+            for (int kc = 0; kc < DK; kc += 16)
+                acc = tri::mm(acc, tri::ld_row(X + kc, LDK, lr, lg), tri::ld_row(Y + kc, LDK, lr, lg));
+            const int j = 16 * tj + lr;
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        ki[a] = *reinterpret_cast<const float4*>(&sm.K[(4 * ti + a) * LDK + d]);
-                        qi[a] = *reinterpret_cast<const float4*>(&sm.Q[(4 * ti + a) * LDK + d]);
-                        kj[a] = *reinterpret_cast<const float4*>(&sm.K[(4 * tj + a) * LDK + d]);
-                    }
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            kk[a][b] = fmaf(ki[a].x, kj[b].x, kk[a][b]);
-                            kk[a][b] = fmaf(ki[a].y, kj[b].y, kk[a][b]);
-                            kk[a][b] = fmaf(ki[a].z, kj[b].z, kk[a][b]);
-                            kk[a][b] = fmaf(ki[a].w, kj[b].w, kk[a][b]);
-                            qk[a][b] = fmaf(qi[a].x, kj[b].x, qk[a][b]);
-                            qk[a][b] = fmaf(qi[a].y, kj[b].y, qk[a][b]);
-                            qk[a][b] = fmaf(qi[a].z, kj[b].z, qk[a][b]);
-                            qk[a][b] = fmaf(qi[a].w, kj[b].w, qk[a][b]);
-                        }
-                }
+            for (int r = 0; r < 4; ++r) {  // acc[r] is row 16 ti + 4 g + r, column j
+                const int i = 16 * ti + 4 * lg + r;
+                const float dec = i >= j ? fast_exp(sm.gam[i] - sm.gam[j]) : 0.f;
+                if (isq)
+                    sm.P[i * kTriLd + j] = dec * acc[r];
+                else
+                    sm.M[i * kTriLd + j] = i > j ? sm.beta[i] * dec * acc[r] : 0.f;
             }
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int i = 4 * ti + a, j = 4 * tj + b;
-                    const float dec = i >= j ? fast_exp(sm.gam[i] - sm.gam[j]) : 0.f;
-                    sm.M[i * kTriLd + j] = i > j ? sm.beta[i] * dec * kk[a][b] : 0.f;
-                    sm.P[i * kTriLd + j] = i >= j ? dec * qk[a][b] : 0.f;
-                }
         }
         // ---- T = (I + A)^-1 (barriers inside)
-        tri_inverse64<kThreads / 64>(sm.M, sm.scratch);
+        tri_inverse64<kChunkThreads / 64>(sm.M, sm.scratch);
 
-        // ---- RHS = diag(beta) V - diag(beta Gamma) K S_0, in registers
-        float rhs[4][CPT];
-        {
-            float ks[4][CPT] = {};
-            for (int d = 0; d < DK; ++d) {
-                float sv[CPT];
+        // ---- RHS = diag(beta) V - diag(beta Gamma) K S_0 by [16 x 16] tiles, in registers
+        tri_f4 rhs[TPW];
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) sv[c] = sm.S[d * LDV + tj * CPT + c];
+        for (int y = 0; y < TPW; ++y) {
+            const int x = w + kWaves * y, ti = x / NCT, tc = x % NCT;
+            if (x >= NT) continue;
+            tri_f4 acc = zero4;
+#pragma unroll 4
+            for (int kc = 0; kc < DK; kc += 16)
+                acc = tri::mm(acc, tri::ld_row(sm.K + 16 * ti * LDK + kc, LDK, lr, lg),
+                              tri::ld_acc(sm.S + kc * LDV + 16 * tc, LDV, lr, lg));
+            const int c = 16 * tc + lr;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float kv = sm.K[(4 * ti + a) * LDK + d];
-#pragma unroll
-                    for (int c = 0; c < CPT; ++c) ks[a][c] = fmaf(kv, sv[c], ks[a][c]);
-                }
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int i = 4 * ti + a;
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lg + r;
                 const float bi = sm.beta[i];
-                const float bg = bi * fast_exp(sm.gam[i]);
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) rhs[a][c] = bi * sm.U[i * LDV + tj * CPT + c] - bg * ks[a][c];
+                rhs[y][r] = bi * sm.U[i * LDV + c] - bi * fast_exp(sm.gam[i]) * acc[r];
             }
         }
         __syncthreads();  // every read of V is done
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) sm.U[(4 * ti + a) * LDV + tj * CPT + c] = rhs[a][c];
+        for (int y = 0; y < TPW; ++y) {
+            const int x = w + kWaves * y, ti = x / NCT, tc = x % NCT;
+            if (x >= NT) continue;
+            tri::st_acc(sm.U + 16 * ti * LDV + 16 * tc, LDV, lr, lg, rhs[y]);
+        }
         __syncthreads();
-        // ---- U = T RHS (T lower triangular with unit diagonal)
+        // ---- U = T RHS (T lower triangular: tiles up to the diagonal)
         {
-            float u[4][CPT] = {};
-            for (int m = 0; m < 4 * ti + 4; ++m) {
-                float rv[CPT];
+            tri_f4 u[TPW];
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) rv[c] = sm.U[m * LDV + tj * CPT + c];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float t = sm.M[(4 * ti + a) * kTriLd + m];
-#pragma unroll
-                    for (int c = 0; c < CPT; ++c) u[a][c] = fmaf(t, rv[c], u[a][c]);
-                }
+            for (int y = 0; y < TPW; ++y) {
+                const int x = w + kWaves * y, ti = x / NCT, tc = x % NCT;
+                if (x >= NT) continue;
+                tri_f4 acc = zero4;
+                for (int tk = 0; tk <= ti; ++tk)
+                    acc = tri::mm(acc, tri::ld_row(sm.M + 16 * ti * kTriLd + 16 * tk, kTriLd, lr, lg),
+                                  tri::ld_acc(sm.U + 16 * tk * LDV + 16 * tc, LDV, lr, lg));
+                u[y] = acc;
             }
             __syncthreads();  // every read of RHS is done
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) sm.U[(4 * ti + a) * LDV + tj * CPT + c] = u[a][c];
+            for (int y = 0; y < TPW; ++y) {
+                const int x = w + kWaves * y, ti = x / NCT, tc = x % NCT;
+                if (x >= NT) continue;
+                tri::st_acc(sm.U + 16 * ti * LDV + 16 * tc, LDV, lr, lg, u[y]);
+            }
         }
         __syncthreads();
         // ---- O = diag(Gamma) Q S_0 + P U
-        {
-            float qs[4][CPT] = {}, pu[4][CPT] = {};
-            for (int d = 0; d < DK; ++d) {
-                float sv[CPT];
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) sv[c] = sm.S[d * LDV + tj * CPT + c];
+        for (int y = 0; y < TPW; ++y) {
+            const int x = w + kWaves * y, ti = x / NCT, tc = x % NCT;
+            if (x >= NT) continue;
+            tri_f4 qs = zero4, pu = zero4;
+#pragma unroll 4
+            for (int kc = 0; kc < DK; kc += 16)
+                qs = tri::mm(qs, tri::ld_row(sm.Q + 16 * ti * LDK + kc, LDK, lr, lg),
+                             tri::ld_acc(sm.S + kc * LDV + 16 * tc, LDV, lr, lg));
+            for (int tk = 0; tk <= ti; ++tk)
+                pu = tri::mm(pu, tri::ld_row(sm.P + 16 * ti * kTriLd + 16 * tk, kTriLd, lr, lg),
+                             tri::ld_acc(sm.U + 16 * tk * LDV + 16 * tc, LDV, lr, lg));
+            const int c = vt * DVT + 16 * tc + lr;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float qv = sm.Q[(4 * ti + a) * LDK + d];
-#pragma unroll
-                    for (int c = 0; c < CPT; ++c) qs[a][c] = fmaf(qv, sv[c], qs[a][c]);
-                }
-            }
-            for (int m = 0; m < 4 * ti + 4; ++m) {
-                float uv[CPT];
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) uv[c] = sm.U[m * LDV + tj * CPT + c];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float pv = sm.P[(4 * ti + a) * kTriLd + m];
-#pragma unroll
-                    for (int c = 0; c < CPT; ++c) pu[a][c] = fmaf(pv, uv[c], pu[a][c]);
-                }
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int i = 4 * ti + a;
-                if (i < S) {
-                    const float G = fast_exp(sm.gam[i]);
-                    float* orow = o + ((row0 + c0 + i) * Hv + h) * (long)dv + vt * DVT + tj * CPT;
-#pragma unroll
-                    for (int c = 0; c < CPT; ++c) orow[c] = fmaf(G, qs[a][c], pu[a][c]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ti + 4 * lg + r;
+                if (i < S) o[((row0 + c0 + i) * Hv + h) * (long)dv + c] = fmaf(fast_exp(sm.gam[i]), qs[r], pu[r]);
             }
         }
-        // ---- S_S = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U
+        // ---- S_S = e^{gamma_S} S_0 + (K * e^{min(gamma_S - gamma, 0)})^T U; rows past the chunk
+        //      add nothing (their K and U rows are zero)
         {
-            const float gS = sm.gam[S - 1];
-            const float GS = fast_exp(gS);
-            float acc[RPS][CPT];
+            const float GS = fast_exp(sm.gam[S - 1]);
+            tri_f4 acc[SPW];
 #pragma unroll
-            for (int r = 0; r < RPS; ++r)
+            for (int y = 0; y < SPW; ++y) {
+                const int x = w + kWaves * y, td = x / NCT, tc = x % NCT;
+                if (x >= NS) continue;
+                acc[y] = GS * tri::ld_acc(sm.S + 16 * td * LDV + 16 * tc, LDV, lr, lg);
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) acc[r][c] = GS * sm.S[(ti * RPS + r) * LDV + tj * CPT + c];
-            for (int m = 0; m < S; ++m) {
-                const float dec = fast_exp(fminf(gS - sm.gam[m], 0.f));
-                float uv[CPT];
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) uv[c] = sm.U[m * LDV + tj * CPT + c];
-#pragma unroll
-                for (int r = 0; r < RPS; ++r) {
-                    const float kd = sm.K[m * LDK + ti * RPS + r] * dec;
-#pragma unroll
-                    for (int c = 0; c < CPT; ++c) acc[r][c] = fmaf(kd, uv[c], acc[r][c]);
+                for (int mc = 0; mc < 64; mc += 16) {
+                    const tri_f4 d4 = *reinterpret_cast<const tri_f4*>(&sm.decS[mc + 4 * lg]);
+                    acc[y] = tri::mm(acc[y], d4 * tri::ld_acc(sm.K + mc * LDK + 16 * td, LDK, lr, lg),
+                                     tri::ld_acc(sm.U + mc * LDV + 16 * tc, LDV, lr, lg));
                 }
             }
             __syncthreads();  // every read of S_0 is done
 #pragma unroll
-            for (int r = 0; r < RPS; ++r)
-#pragma unroll
-                for (int c = 0; c < CPT; ++c) sm.S[(ti * RPS + r) * LDV + tj * CPT + c] = acc[r][c];
+            for (int y = 0; y < SPW; ++y) {
+                const int x = w + kWaves * y, td = x / NCT, tc = x % NCT;
+                if (x >= NS) continue;
+                tri::st_acc(sm.S + 16 * td * LDV + 16 * tc, LDV, lr, lg, acc[y]);
+            }
         }
     }
     __syncthreads();
-    for (int e = tid; e < DK * DVT; e += kThreads) {
+    for (int e = tid; e < DK * DVT; e += kChunkThreads) {
         const int r = e / DVT, c = e % DVT;
         S_out[sbase + (long)r * dv + c] = sm.S[r * LDV + c];
     }
@@ -290,7 +276,7 @@ hipError_t launch_f32_path(const void* q, const void* k, const void* v, const fl
                                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (configured != hipSuccess) return configured;
     const dim3 grid((unsigned)(Hv * (dv / DVT)), (unsigned)bt.P);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, st, static_cast<const TIN*>(q), static_cast<const TIN*>(k),
+    hipLaunchKernelGGL(kern, grid, dim3(kChunkThreads), smem, st, static_cast<const TIN*>(q), static_cast<const TIN*>(k),
                        static_cast<const TIN*>(v), beta, g, o, S_in, S_out, bt, Hk, Hv, dv);
     return hipGetLastError();
 }
