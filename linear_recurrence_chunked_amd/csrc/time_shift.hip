@@ -23,7 +23,7 @@ namespace lrc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;
+constexpr int kTile = 16;
 constexpr int kUnroll = 8;
 
 template <int VEC>
