@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_FP32_PEAK_TFS = 157.3  # MI355X dense fp32 MFMA, TFLOP/s
 FP32_VEC_PEAK_TFS = 157.3    # MI355X fp32 vector, TFLOP/s
 
 
@@ -488,6 +489,14 @@ def main():
                                                  W["lens"], split=True), stream)
         tf = work["gdn"]["flops"] / (ms * 1e-3) / 1e12
         kern["gdn"]["split_form"] = {"ms": round(ms, 4), "TFLOPs": tf, "mfma_bf16_frac": tf / MFMA_BF16_PEAK_TFS}
+        # the same rows with FP32 q, k, v (the FP32-input path, on the FP32 matrix cores), not in `value`
+        q32, k32, v32 = (W[n].float() for n in ("q", "gk", "gv"))
+        ms = time_launch(lambda: lrc.gdn_prefill(q32, k32, v32, W["beta"], W["g"], W["o"], W["S"], W["lens"]),
+                         stream, reps=5)
+        tf = work["gdn"]["flops"] / (ms * 1e-3) / 1e12
+        kern["gdn"]["fp32_inputs"] = {"ms": round(ms, 4), "TFLOPs": tf,
+                                      "mfma_fp32_frac": tf / MFMA_FP32_PEAK_TFS}
+        del q32, k32, v32
     nxt = measure_next_rows(lrc, dev, W["lens"]) if not args.only else None
     if nxt and "scan" in per_k:
         nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
