@@ -22,7 +22,7 @@
 //   * B and C of a 64-row chunk are staged in LDS by the workgroup (the next
 //     chunk's rows load into registers while the current chunk computes);
 //     every lane of a part reads the same LDS address (a broadcast).
-//   * x and dt move through a register ring of two 16-row groups, loaded one
+//   * x and dt move through a register ring of two 4-row groups, loaded one
 //     group ahead; loads past the prompt re-read its last row and those rows
 //     are never computed, so the state stops at the prompt's last row.
 #include "lrc_device.h"
@@ -37,7 +37,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanes = LRC_MIXER_LANES;  // lanes per channel when d_state allows (2 or 4)
 constexpr int kChunk = 64;             // rows of B and C staged per chunk
-constexpr int kGroup = 16;             // rows of x and dt per register group
+constexpr int kGroup = 4;              // rows of x and dt per register group
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Sum over the LPD lanes (1, 2 or 4 consecutive lanes of a quad) that share a channel.
