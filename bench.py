@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle work")
     ap.add_argument("--only", default="", help="comma list of kernels to run (profiling aid)")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="time only the step's own launches: no split-form or FP32-input DeltaNet legs, "
+                         "no rows beyond the step (profiling aid)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 4 GiB device copy (for scaling HBM counters) and exit")
     return ap.parse_args()
@@ -484,7 +487,7 @@ def main():
         if k == "scan":  # carry hand-overs of the tiled driver that timed out over the whole run (expected 0)
             d["handover_timeouts"] = lrc.scan_workspace_timeouts(W["scan_ws"])
         kern[k] = d
-    if "gdn" in kern:  # the same launch with FP32 operands as hi + lo bf16 pairs (LRC_BF16_SPLIT), not in `value`
+    if "gdn" in kern and not args.no_extra_legs:  # the same launch with FP32 operands as hi + lo bf16 pairs (LRC_BF16_SPLIT), not in `value`
         ms = time_launch(lambda: lrc.gdn_prefill(W["q"], W["gk"], W["gv"], W["beta"], W["g"], W["o"], W["S"],
                                                  W["lens"], split=True), stream)
         tf = work["gdn"]["flops"] / (ms * 1e-3) / 1e12
@@ -497,7 +500,7 @@ def main():
         kern["gdn"]["fp32_inputs"] = {"ms": round(ms, 4), "TFLOPs": tf,
                                       "mfma_fp32_frac": tf / MFMA_FP32_PEAK_TFS}
         del q32, k32, v32
-    nxt = measure_next_rows(lrc, dev, W["lens"]) if not args.only else None
+    nxt = measure_next_rows(lrc, dev, W["lens"]) if not (args.only or args.no_extra_legs) else None
     if nxt and "scan" in per_k:
         nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
     dom = max(kernels, key=lambda k: per_k[k])

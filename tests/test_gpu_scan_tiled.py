@@ -2,7 +2,7 @@
 
 Reading ("perf(mamba): prefill text prompts in multi-token chunks",
 Implementation): every 64-row chunk is the doubling scan with the carried state
-applied last.  The tiled driver runs each (chunk, block of 256 state elements)
+applied last.  The tiled driver runs each (chunk, block of 128 state elements)
 in its own workgroup and takes the carry from the previous chunk's last h row;
 its chunk arithmetic and carry values are those of the long-lived driver
 (lrc_scan_prefill), so the two must agree bit for bit, and both must be within
