@@ -56,11 +56,13 @@
 // Decay factors: on the diagonal 16x16 tiles e^{gamma_i - gamma_j} is formed
 // per element; below them it is the product e^{gamma_i - gamma_c}
 // e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
-// The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) runs in
-// FP32 on the FP32 matrix cores.
+// The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) keeps T in
+// FP32; its tile products run as hi/lo bf16 pairs on the bf16 matrix cores,
+// or, with SPLIT, on the FP32 matrix cores.
 #include <algorithm>
 #include <cstddef>
 #include <cstring>
+#include <type_traits>
 
 #include "lrc_device.h"
 #include "lrc_internal.h"
@@ -687,6 +689,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 }
         };
 
+        // The inverse's tile products: FP32 matrix cores in the split form, whose
+        // T enters the state products with about 16 bits; otherwise hi/lo bf16
+        // pairs (about 2^-17 per product), since T is rounded to bf16 once anyway.
+        using InvMM = typename std::conditional<SPLIT, tri::MmF32, tri::MmBf16Split>::type;
         // Tiles above the diagonal stay zero for the whole prompt.
         for (int e = pt; e < 64 * kTriLd; e += PT) sm.M[e] = 0.f;
         for (int e = pt; e < 64 * L64; e += PT) {
@@ -707,17 +713,17 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             const int nb = (n + 1) & 1, nrb = (n + 4) % 3;  // buffers of chunk n+1
 
             // ---- A: diagonal tiles of the inverse of chunk n+1
-            if (do_next) tri::diag<kPrep>(sm.M, sm.scratch, pw);
+            if (do_next) tri::diag<kPrep, InvMM>(sm.M, sm.scratch, pw);
             __syncthreads();
 
             // ---- B: level 16
-            if (do_next) tri::lvl16<kPrep>(sm.M, pw);
+            if (do_next) tri::lvl16<kPrep, InvMM>(sm.M, pw);
             __syncthreads();
 
             // ---- C: level 32 (first half); the tiles of T that are final go to bf16;
             //      chunk n+2 into the buffers chunk n used, chunk n+3 in flight
             if (do_next) {
-                tri::lvl32a<kPrep>(sm.M, sm.scratch, pw);
+                tri::lvl32a<kPrep, InvMM>(sm.M, sm.scratch, pw);
                 split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
                 if (pw == 0) split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
                 if (pw == 1) split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
@@ -730,7 +736,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
 
             // ---- D: level 32 (second half) and its tile of T; P of chunk n+1
             if (do_next) {
-                tri::lvl32b<kPrep>(sm.M, sm.scratch, pw);
+                tri::lvl32b<kPrep, InvMM>(sm.M, sm.scratch, pw);
                 tri::wave_sync();
                 split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
                 masked_qk(nb, nrb);

@@ -27,6 +27,15 @@
 // X[l%16][4g .. 4g+3] (g = l/16) and, for Y, the accumulator-layout column
 // slice Y[4g .. 4g+3][l%16]; the four 16x16x4 steps pair k = 4g + kk on both
 // sides, so Y can be a previous product's accumulator as it is.
+//
+// Two ways to form a tile product, chosen by the caller:
+//  * MmF32: four v_mfma_f32_16x16x4f32, FP32 operands (32 cycles each).
+//  * MmBf16Split: each FP32 operand is split as hi = bf16(x), lo = bf16(x - hi)
+//    and the product is hi.hi + lo.hi + hi.lo on the bf16 matrix cores, two
+//    v_mfma_f32_16x16x32_bf16 (16 cycles each): the lane's 8 k-slots carry
+//    (hi, lo) of X against (hi, hi) of Y, then (hi, lo) against (lo, 0).  The
+//    dropped lo.lo term and the roundings leave about 2^-17 of each product's
+//    operands, against 2^-24 for MmF32, at a quarter of the matrix-core time.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,13 +49,39 @@ typedef float tri_f4 __attribute__((ext_vector_type(4)));
 
 namespace tri {
 
-__device__ __forceinline__ tri_f4 mm(tri_f4 z, tri_f4 xrow, tri_f4 yc) {
-    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[0], yc[0], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[1], yc[1], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[2], yc[2], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[3], yc[3], z, 0, 0, 0);
-    return z;
-}
+typedef __bf16 tri_bf8 __attribute__((ext_vector_type(8)));
+
+struct MmF32 {
+    static __device__ __forceinline__ tri_f4 mm(tri_f4 z, tri_f4 xrow, tri_f4 yc) {
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[0], yc[0], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[1], yc[1], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[2], yc[2], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[3], yc[3], z, 0, 0, 0);
+        return z;
+    }
+};
+
+struct MmBf16Split {
+    static __device__ __forceinline__ tri_f4 mm(tri_f4 z, tri_f4 xrow, tri_f4 yc) {
+        tri_bf8 a, b1, b2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const __bf16 xh = static_cast<__bf16>(xrow[r]);
+            const __bf16 yh = static_cast<__bf16>(yc[r]);
+            a[r] = xh;
+            a[4 + r] = static_cast<__bf16>(xrow[r] - static_cast<float>(xh));
+            b1[r] = yh;
+            b1[4 + r] = yh;
+            b2[r] = static_cast<__bf16>(yc[r] - static_cast<float>(yh));
+            b2[4 + r] = static_cast<__bf16>(0.f);
+        }
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, z, 0, 0, 0);
+        return z;
+    }
+};
+
+__device__ __forceinline__ tri_f4 mm(tri_f4 z, tri_f4 xrow, tri_f4 yc) { return MmF32::mm(z, xrow, yc); }
 // Row segment X[lr][4g .. 4g+3] of a row-major tile.
 __device__ __forceinline__ tri_f4 ld_row(const float* t, int ld, int lr, int g) {
     return *reinterpret_cast<const tri_f4*>(t + lr * ld + 4 * g);
@@ -89,7 +124,7 @@ __device__ __forceinline__ void lanes(int& lr, int& g) {
     g = lane >> 4;
 }
 
-template <int NW>
+template <int NW, class MM = MmF32>
 __device__ inline void diag(float* M, float* /*scratch*/, int w) {
     constexpr int ld = kTriLd;
     int lr, g;
@@ -110,14 +145,14 @@ __device__ inline void diag(float* M, float* /*scratch*/, int w) {
             nacc[k] = in_acc ? nacc[k] : 0.f;
         }
         // Every product that is needed again as a row operand is also formed
-        // in row layout, as the transposed product: mm(Y_acc, X_row) is
+        // in row layout, as the transposed product: MM::mm(Y_acc, X_row) is
         // (X Y)^T in accumulator layout, i.e. X Y in row layout.  That trades
         // the LDS round trips of a layout change for three more products.
-        const tri_f4 n2 = mm(zero, nrow, nacc);     // N^2
-        const tri_f4 n2r = mm(zero, nacc, nrow);    // N^2, row layout
-        const tri_f4 nn2 = mm(zero, nrow, n2);      // N N^2
-        const tri_f4 nn2r = mm(zero, n2, nrow);     // N N^2, row layout
-        const tri_f4 n4 = mm(zero, n2r, n2);        // N^4
+        const tri_f4 n2 = MM::mm(zero, nrow, nacc);     // N^2
+        const tri_f4 n2r = MM::mm(zero, nacc, nrow);    // N^2, row layout
+        const tri_f4 nn2 = MM::mm(zero, nrow, n2);      // N N^2
+        const tri_f4 nn2r = MM::mm(zero, n2, nrow);     // N N^2, row layout
+        const tri_f4 n4 = MM::mm(zero, n2r, n2);        // N^4
         tri_f4 x, xr;                               // (I - N)(I + N^2), both layouts
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -125,16 +160,16 @@ __device__ inline void diag(float* M, float* /*scratch*/, int w) {
             x[k] = id - nacc[k] + n2[k] - nn2[k];
             xr[k] = id - nrow[k] + n2r[k] - nn2r[k];
         }
-        const tri_f4 d = x + mm(zero, xr, n4);     // D = X (I + N^4)
-        const tri_f4 dr = xr + mm(zero, n4, xr);   // D, row layout
-        const tri_f4 y = mm(zero, lorow, d);       // L D
-        const tri_f4 z = mm(zero, dr, y);          // D L D
+        const tri_f4 d = x + MM::mm(zero, xr, n4);     // D = X (I + N^4)
+        const tri_f4 dr = xr + MM::mm(zero, n4, xr);   // D, row layout
+        const tri_f4 y = MM::mm(zero, lorow, d);       // L D
+        const tri_f4 z = MM::mm(zero, dr, y);          // D L D
         st_acc(Mt, ld, lr, g, d - z);
     }
 }
 
 // level 16: blocks b = 0, 1 (rows 32b+16 .., columns 32b ..)
-template <int NW>
+template <int NW, class MM = MmF32>
 __device__ inline void lvl16(float* M, int w) {
     constexpr int ld = kTriLd;
     int lr, g;
@@ -142,14 +177,14 @@ __device__ inline void lvl16(float* M, int w) {
     const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int b = w; b < 2; b += NW) {
         float* L21 = M + (32 * b + 16) * ld + 32 * b;
-        const tri_f4 y = mm(zero, ld_row(L21, ld, lr, g), ld_acc(M + 32 * b * ld + 32 * b, ld, lr, g));
-        const tri_f4 z = mm(zero, ld_row(M + (32 * b + 16) * ld + 32 * b + 16, ld, lr, g), y);
+        const tri_f4 y = MM::mm(zero, ld_row(L21, ld, lr, g), ld_acc(M + 32 * b * ld + 32 * b, ld, lr, g));
+        const tri_f4 z = MM::mm(zero, ld_row(M + (32 * b + 16) * ld + 32 * b + 16, ld, lr, g), y);
         st_acc(L21, ld, lr, g, -z);
     }
 }
 
 // level 32, first half: Y = L21 T11 by 16x16 output tiles (ta, tb), into scratch (32 x 36)
-template <int NW>
+template <int NW, class MM = MmF32>
 __device__ inline void lvl32a(float* M, float* scratch, int w) {
     constexpr int ld = kTriLd;
     int lr, g;
@@ -159,14 +194,14 @@ __device__ inline void lvl32a(float* M, float* scratch, int w) {
         const int ta = q >> 1, tb = q & 1;
         tri_f4 acc = zero;
         for (int c = tb; c < 2; ++c)  // T11 is block lower triangular
-            acc = mm(acc, ld_row(M + (32 + 16 * ta) * ld + 16 * c, ld, lr, g),
+            acc = MM::mm(acc, ld_row(M + (32 + 16 * ta) * ld + 16 * c, ld, lr, g),
                      ld_acc(M + 16 * c * ld + 16 * tb, ld, lr, g));
         st_acc(scratch + 16 * ta * 36 + 16 * tb, 36, lr, g, acc);
     }
 }
 
 // level 32, second half: T21 = -T22 Y
-template <int NW>
+template <int NW, class MM = MmF32>
 __device__ inline void lvl32b(float* M, const float* scratch, int w) {
     constexpr int ld = kTriLd;
     int lr, g;
@@ -176,7 +211,7 @@ __device__ inline void lvl32b(float* M, const float* scratch, int w) {
         const int ta = q >> 1, tb = q & 1;
         tri_f4 acc = zero;
         for (int c = 0; c <= ta; ++c)  // T22 is block lower triangular
-            acc = mm(acc, ld_row(M + (32 + 16 * ta) * ld + 32 + 16 * c, ld, lr, g),
+            acc = MM::mm(acc, ld_row(M + (32 + 16 * ta) * ld + 32 + 16 * c, ld, lr, g),
                      ld_acc(scratch + 16 * c * 36 + 16 * tb, 36, lr, g));
         st_acc(M + (32 + 16 * ta) * ld + 16 * tb, ld, lr, g, -acc);
     }

@@ -330,3 +330,75 @@ def test_gdn_bf16_split_chunked_and_rejects_f32(L, orc):
     assert rel_err(f64(s), ref_s) < TOL_SPLIT
     with pytest.raises(ValueError):
         _run_prefill(L, inputs.gdn_small(dtype=torch.float32), split=True)
+
+
+# ---------------------------------------------------------------- FP32 inputs at the timed shape
+def test_gdn_fp32_9b_shape_full(L, orc):
+    """The FP32-input path at the 9B-like shape (32 value heads on 16 key heads, dk = dv = 128,
+    2048 rows = 32 chunks of 64) against the oracle at 1e-4, every head, and the head whose decay is
+    -8 on every row (gamma reaches -512 inside a chunk) on its own."""
+    from linear_recurrence_chunked_amd import inputs
+
+    d = inputs.gdn_9b(dtype=torch.float32)
+    ref_o, ref_s = _oracle(orc, d)
+    o, s = _run_prefill(L, d)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    assert rel_err(f64(o), ref_o) < TOL_F32
+    assert rel_err(f64(s), ref_s) < TOL_F32
+    for h in (0, 31):
+        assert rel_err(f64(o[:, h]), ref_o[:, h]) < TOL_F32, h
+        assert rel_err(f64(s[h]), ref_s[h]) < TOL_F32, h
+
+
+def test_gdn_fp32_lane_lengths_128(L, orc):
+    """The FP32-input path at dk = dv = 128 over the 16-prompt ragged length mix of the lane tests
+    (32 value heads on 16 key heads, decays of the 9B-like recipe), every prompt against the oracle."""
+    from linear_recurrence_chunked_amd import inputs
+
+    lens = [300, 0, 64, 65, 1, 257, 130, 190, 17, 128, 45, 99, 200, 33, 70, 150]
+    R, P, Hk, Hv, dk, dv = sum(lens), len(lens), 16, 32, 128, 128
+    rng = np.random.default_rng(930)
+    q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((R, Hv, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((R, Hv))))
+    g = inputs.gdn_decays(rng, R, Hv)
+    S0 = rng.normal(0, 0.1, (P, Hv, dk, dv))
+    t = {n: torch.from_numpy(a).float() for n, a in dict(q=q, k=k, v=v, beta=beta, g=g, S0=S0).items()}
+    dq, dk_, dv_, db, dg, dS = (to_dev(t[n]) for n in ("q", "k", "v", "beta", "g", "S0"))
+    o = torch.full((R, Hv, dv), float("nan"), device="cuda")
+    L.gdn_prefill(dq, dk_, dv_, db, dg, o, dS, lens)
+    torch.cuda.synchronize()
+    r = 0
+    for p, n in enumerate(lens):
+        sl = slice(r, r + n)
+        ref_o, ref_s = orc.gdn(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]), f64(t["beta"][sl]),
+                               f64(t["g"][sl]), f64(t["S0"][p]))
+        if n:
+            assert rel_err(f64(o[sl]), ref_o) < TOL_F32, p
+        assert rel_err(f64(dS[p]), ref_s) < TOL_F32, p
+        r += n
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)])
+def test_gdn_long_prompt_59_chunks(L, orc, dtype, tol):
+    """One prompt of 3 742 rows (59 chunks, the longest of the mixed prefill) at dk = dv = 128 on two
+    value heads of one key head, one with the mildest (-1e-3) and one with the strongest (-8) decay of
+    the range on every row: the error of the chunk chain over tens of chunks."""
+    rng = np.random.default_rng(931)
+    R, Hk, Hv, dk, dv = 3742, 1, 2, 128, 128
+    q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((R, Hv, dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((R, Hv))))
+    g = np.stack([np.full(R, -1e-3), np.full(R, -8.0)], axis=1)
+    S0 = rng.normal(0, 0.1, (Hv, dk, dv))
+    t = {n: torch.from_numpy(a).float() for n, a in dict(beta=beta, g=g, S0=S0).items()}
+    for n, a in dict(q=q, k=k, v=v).items():
+        t[n] = torch.from_numpy(a).to(dtype)
+    ref_o, ref_s = orc.gdn(*(f64(t[n]) for n in ("q", "k", "v", "beta", "g", "S0")))
+    o, s = _run_prefill(L, t)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    for h in range(Hv):
+        assert rel_err(f64(o[:, h]), ref_o[:, h]) < tol, h
+        assert rel_err(f64(s[h]), ref_s[h]) < tol, h
