@@ -449,6 +449,7 @@ def main():
     torch.cuda.synchronize()
     kernels = [k for k in KERNELS if not args.only or k in args.only.split(",")]
 
+    lrc.wait_timeouts(reset=True)  # bounded in-workgroup waits of the WKV kernels that ran out (expected 0)
     fresh = None if args.no_cpu_baseline else fresh_outputs_sample(lrc, W)
     reset_states(W)
     for _ in range(args.warmup):
@@ -486,6 +487,8 @@ def main():
             d["mfma_bf16_frac"] = d["TFLOPs"] / MFMA_BF16_PEAK_TFS
         if k == "scan":  # carry hand-overs of the tiled driver that timed out over the whole run (expected 0)
             d["handover_timeouts"] = lrc.scan_workspace_timeouts(W["scan_ws"])
+        if k == "wkv4":  # bounded waits between its waves that ran out over the whole run (expected 0)
+            d["lds_wait_timeouts"] = lrc.wait_timeouts()
         kern[k] = d
     if "gdn" in kern and not args.no_extra_legs:  # the same launch with FP32 operands as hi + lo bf16 pairs (LRC_BF16_SPLIT), not in `value`
         ms = time_launch(lambda: lrc.gdn_prefill(W["q"], W["gk"], W["gv"], W["beta"], W["g"], W["o"], W["S"],
@@ -501,6 +504,8 @@ def main():
                                       "mfma_fp32_frac": tf / MFMA_FP32_PEAK_TFS}
         del q32, k32, v32
     nxt = measure_next_rows(lrc, dev, W["lens"]) if not (args.only or args.no_extra_legs) else None
+    if nxt:  # the token-dependent decay's waits, counted with those of the step's WKV
+        nxt["wkv_tdecay"]["lds_wait_timeouts"] = lrc.wait_timeouts()
     if nxt and "scan" in per_k:
         nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
     dom = max(kernels, key=lambda k: per_k[k])

@@ -284,6 +284,17 @@ lrc_status lrc_wkv_tdecay_prefill(const float* k, const float* v, const float* w
                                   float* num, float* den, float* mx, const int* lens_host, int P, int C,
                                   void* stream);
 
+/* ------------------------------------------------------------------------
+ * Diagnostics.  The WKV kernels (K2 and the token-dependent decay) pass each
+ * chunk between the waves of a workgroup through counters in LDS, and a wave
+ * waits for another with a bounded poll (about 2^20 polls).  A wait that runs
+ * out goes on rather than hang and is counted on the device; the count stays
+ * 0 unless a launch could not make progress, and outputs of a launch that
+ * counted one are not to be trusted.  This call synchronizes `stream`, writes
+ * the current GPU's count to *count_host (host memory), and with reset != 0
+ * sets it back to 0. */
+lrc_status lrc_wait_timeouts(unsigned* count_host, int reset, void* stream);
+
 /* ------------------------------------------------------------------------ */
 const char* lrc_status_string(lrc_status s);
 /* Detail of the last error on the calling thread ("" if none). */

@@ -6,9 +6,32 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 
 #include "lrc_internal.h"
+
+namespace lrc {
+namespace {
+// Bounded LDS waits that gave up (see lds_wait_at_least), one counter per GPU.
+__device__ unsigned g_wait_timeouts = 0;
+}  // namespace
+
+unsigned* wait_timeouts_counter() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static unsigned* ptr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_wait_timeouts)) != hipSuccess) return nullptr;
+        ptr[dev] = static_cast<unsigned*>(p);
+    }
+    return ptr[dev];
+}
+}  // namespace lrc
 
 namespace {
 
@@ -319,6 +342,21 @@ lrc_status lrc_scan_prefill_ws(const float* a, const float* b, float* h, float* 
     REQUIRE(lrc::scan_tiled_tiles_bound(rows, P, E) < (1l << 31), LRC_ERR_SHAPE, "too many tiles for one launch");
     auto st = static_cast<hipStream_t>(stream);
     return check_launch(lrc::launch_scan_tiled(a, b, h, state, bt, E, workspace, st), st, "scan prefill (tiled)");
+}
+
+lrc_status lrc_wait_timeouts(unsigned* count_host, int reset, void* stream) {
+    REQUIRE_PTR(count_host);
+    auto st = static_cast<hipStream_t>(stream);
+    unsigned* c = lrc::wait_timeouts_counter();
+    if (!c) return fail(LRC_ERR_LAUNCH, "wait-timeout counter: no device address");
+    hipError_t e = hipMemcpyAsync(count_host, c, sizeof(unsigned), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess && reset) {
+        static const unsigned zero = 0;
+        e = hipMemcpyAsync(c, &zero, sizeof(unsigned), hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+    }
+    return check_launch(e, st, "wait-timeout counter");
 }
 
 lrc_status lrc_wkv4_rows(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,

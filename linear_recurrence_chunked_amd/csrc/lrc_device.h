@@ -63,12 +63,17 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 // Bounded wait until an LDS counter reaches v (acquire, workgroup scope).  For
 // waits on another wave of the same workgroup that needs nothing from the
 // waiting one, so the bound (about 2^20 polls) is never reached in practice;
-// past it the wave goes on rather than hang.
+// past it the wave goes on rather than hang, and its lane 0 adds one to
+// *timeouts (a device counter the host reads back; its results are then
+// not to be trusted).
 constexpr int kLdsWaitLimit = 1 << 20;
-__device__ __forceinline__ void lds_wait_at_least(int* x, int v) {
+__device__ __forceinline__ void lds_wait_at_least(int* x, int v, unsigned* timeouts) {
     int n = 0;
     while (__hip_atomic_load(x, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < v) {
-        if (++n > kLdsWaitLimit) break;
+        if (++n > kLdsWaitLimit) {
+            if (lane_id() == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
 }

@@ -31,6 +31,10 @@ __host__ __device__ inline int batch_len(const Batch& b, int p) {
     return b.uniform >= 0 ? b.uniform : b.row_off[p + 1] - b.row_off[p];
 }
 
+// Device counter (one per GPU, in the library) of bounded LDS waits that gave
+// up; the WKV kernels add to it.  nullptr if its address cannot be had.
+unsigned* wait_timeouts_counter();
+
 // Kernel launchers (one per op), defined next to their kernels.  They
 // assume validated arguments and return the launch status.
 hipError_t launch_conv(const void* x, void* y, const void* state_in, void* state_out, const float* w,
@@ -40,8 +44,7 @@ hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0
 size_t scan_workspace_bytes(int P, long E);
 long scan_tiled_tiles_bound(long rows, int P, long E);  // at least the tiled scan's tile count
 hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
-                             void* workspace, hipStream_t st);
-hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
+                             void* workspace, hipStream_t st);hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st);
 hipError_t launch_wkv_tdecay(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                              float* den, float* mx, const Batch& bt, int C, hipStream_t st);

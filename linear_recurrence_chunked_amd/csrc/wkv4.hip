@@ -130,7 +130,7 @@ template <int NW, bool FULL>
 __global__ __launch_bounds__((NW + 1) * 64) void wkv4_kernel(const float* __restrict__ k, const float* __restrict__ v,
                                                             const float* __restrict__ w, const float* __restrict__ u,
                                                             float* __restrict__ wkv, float* num, float* den, float* mx,
-                                                            Batch bt, int C) {
+                                                            Batch bt, int C, unsigned* timeouts) {
     constexpr int R = 64 / NW;        // rows per row wave and chunk
     __shared__ float4 zs[2][NW][64];  // block states of a chunk, by chunk parity
     __shared__ float4 ps[2][NW][64];  // start state of every block, by chunk parity
@@ -164,7 +164,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv4_kernel(const float* __rest
             const int S = min(64, L - 64 * n), nblk = (S + R - 1) / R, b = n & 1;
             // No row wave reduces chunk n+2 before chunk n's start states are
             // out, so the count of this parity covers chunks up to n only.
-            lds_wait_at_least(&red_cnt[b], NW * (n / 2 + 1));
+            lds_wait_at_least(&red_cnt[b], NW * (n / 2 + 1), timeouts);
 #pragma unroll
             for (int j = 0; j < NW; ++j) {
                 ps[b][j][lane] = make_float4(s.aa, s.bb, s.m, s.n);
@@ -229,7 +229,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv4_kernel(const float* __rest
         for (int i = 0; i < R; ++i) kb[i] = kr[i] * kLog2e;
         const int c0 = 64 * n, S = min(64, L - c0);
         const int nb = min(R, max(0, S - R * wv));
-        lds_wait_at_least(&ps_seq, n + 1);
+        lds_wait_at_least(&ps_seq, n + 1, timeouts);
         const float4 st = ps[n & 1][wv][lane];
         WkvState s{st.x, st.y, st.z, st.w};
         // lanes past C store at an offset past the resource's end: dropped
@@ -276,13 +276,15 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv4_kernel(const float* __rest
 
 hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st) {
+    unsigned* timeouts = wait_timeouts_counter();
+    if (!timeouts) return hipErrorInvalidSymbol;
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)bt.P);
     if (C % 64 == 0)
         hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, true>), grid, dim3((kWkvWaves + 1) * 64), 0, st, k, v, w, u, wkv,
-                           num, den, mx, bt, C);
+                           num, den, mx, bt, C, timeouts);
     else
         hipLaunchKernelGGL((wkv4_kernel<kWkvWaves, false>), grid, dim3((kWkvWaves + 1) * 64), 0, st, k, v, w, u, wkv,
-                           num, den, mx, bt, C);
+                           num, den, mx, bt, C, timeouts);
     return hipGetLastError();
 }
 

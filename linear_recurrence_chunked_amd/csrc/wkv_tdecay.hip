@@ -122,7 +122,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv_tdecay_kernel(const float* 
                                                                   const float* __restrict__ w,
                                                                   const float* __restrict__ u,
                                                                   float* __restrict__ wkv, float* num, float* den,
-                                                                  float* mx, Batch bt, int C) {
+                                                                  float* mx, Batch bt, int C, unsigned* timeouts) {
     constexpr int R = 64 / NW;         // rows per row wave and chunk
     __shared__ float2 zs[2][NW][64];   // block sums of a chunk, by chunk parity
     __shared__ double2 zx[2][NW][64];  // block (largest exponent, decay)
@@ -158,7 +158,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv_tdecay_kernel(const float* 
             const int S = min(64, L - 64 * n), nblk = (S + R - 1) / R, b = n & 1;
             // No row wave reduces chunk n+2 before chunk n's start states are
             // out, so the count of this parity covers chunks up to n only.
-            lds_wait_at_least(&red_cnt[b], NW * (n / 2 + 1));
+            lds_wait_at_least(&red_cnt[b], NW * (n / 2 + 1), timeouts);
 #pragma unroll
             for (int j = 0; j < NW; ++j) {
                 ps[b][j][lane] = make_float2(s.aa, s.bb);
@@ -229,7 +229,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv_tdecay_kernel(const float* 
     auto replay = [&](int n, const float (&kb)[R], const float (&vb)[R], const float (&wb)[R]) {
         const int c0 = 64 * n, S = min(64, L - c0);
         const int nb = min(R, max(0, S - R * wv));
-        lds_wait_at_least(&ps_seq, n + 1);
+        lds_wait_at_least(&ps_seq, n + 1, timeouts);
         const float2 st = ps[n & 1][wv][lane];
         TdState s{st.x, st.y, pm[n & 1][wv][lane]};
         // lanes past C store at an offset past the resource's end: dropped
@@ -268,13 +268,15 @@ __global__ __launch_bounds__((NW + 1) * 64) void wkv_tdecay_kernel(const float* 
 
 hipError_t launch_wkv_tdecay(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                              float* den, float* mx, const Batch& bt, int C, hipStream_t st) {
+    unsigned* timeouts = wait_timeouts_counter();
+    if (!timeouts) return hipErrorInvalidSymbol;
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)bt.P);
     if (C % 64 == 0)
         hipLaunchKernelGGL((wkv_tdecay_kernel<kTdWaves, true>), grid, dim3((kTdWaves + 1) * 64), 0, st, k, v, w, u,
-                           wkv, num, den, mx, bt, C);
+                           wkv, num, den, mx, bt, C, timeouts);
     else
         hipLaunchKernelGGL((wkv_tdecay_kernel<kTdWaves, false>), grid, dim3((kTdWaves + 1) * 64), 0, st, k, v, w,
-                           u, wkv, num, den, mx, bt, C);
+                           u, wkv, num, den, mx, bt, C, timeouts);
     return hipGetLastError();
 }
 

@@ -58,6 +58,8 @@ for _name, _args in _SIGS.items():
     _fn = getattr(lib, _name)
     _fn.argtypes = _args
     _fn.restype = _S
+lib.lrc_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint), _I, _P]
+lib.lrc_wait_timeouts.restype = _S
 lib.lrc_scan_workspace_size.argtypes = [_I, _I, _I]
 lib.lrc_scan_workspace_size.restype = ctypes.c_size_t
 lib.lrc_status_string.argtypes = [_S]
@@ -225,6 +227,14 @@ def scan_prefill_ws(a, b, h, state, lens, ws):
         raise ValueError("ws must be a contiguous 1-D uint8 tensor")
     _check(lib.lrc_scan_prefill_ws(_ptr(a), _ptr(b), _ptr(h), _ptr(state), arr, P, D, N, _ptr(ws), ws.numel(),
                                    _stream(a)))
+
+
+def wait_timeouts(reset: bool = False) -> int:
+    """Bounded in-workgroup waits of the WKV kernels that gave up on the current GPU (0 unless a launch
+    could not make progress).  Synchronizes the current stream; with reset, sets the count back to 0."""
+    n = ctypes.c_uint(0)
+    _check(lib.lrc_wait_timeouts(ctypes.byref(n), int(reset), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    return int(n.value)
 
 
 # ------------------------------------------------------------------ K2 wkv

@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
               "lrc_wkv4_prefill", "lrc_gdn_chunk", "lrc_gdn_prefill", "lrc_unit_lower_inverse",
               "lrc_time_shift_rows", "lrc_time_shift_prefill", "lrc_mamba_mixer_rows", "lrc_mamba_mixer_prefill",
               "lrc_wkv_tdecay_rows", "lrc_wkv_tdecay_prefill", "lrc_scan_prefill_ws", "lrc_scan_workspace_size",
+              "lrc_wait_timeouts",
               "lrc_status_string", "lrc_last_error", "lrc_version"]:
         assert n in names
 
