@@ -16,7 +16,9 @@
  *    unless an argument says it may alias.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *    asynchronous on that stream, allocates no memory and keeps no state
- *    between calls.  Calls on distinct buffers are thread-safe.
+ *    between calls (lrc_scan_prefill_static alone uses a fixed device array
+ *    of the library, described there).  Calls on distinct buffers are
+ *    thread-safe.
  *  - All arguments are validated on the host before anything is enqueued,
  *    without any HIP call.  On a validation error nothing is launched, no
  *    buffer is written, and lrc_last_error() (thread-local) explains it.
@@ -144,6 +146,20 @@ size_t lrc_scan_workspace_size(int P, int D, int N);
 lrc_status lrc_scan_prefill_ws(const float* a, const float* b, float* h, float* state,
                                const int* lens_host, int P, int D, int N,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* K1 driver, tiled form, allocating nothing: for callers that cannot
+ * allocate device memory or pass a workspace (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments and
+ * the same result, bit for bit, as lrc_scan_prefill_ws, whose workspace is
+ * replaced here by a fixed device array inside the library: 2 MiB per GPU,
+ * held from the first call on that GPU until the process ends, zero-filled
+ * by that first call on `stream`.  It bounds P * ceil(D * N / 128) to
+ * 262 112 (LRC_ERR_SHAPE beyond, before anything is launched).  Every call on
+ * one GPU uses the same array: calls that may run at the same time on one GPU
+ * (on streams with no ordering between them) race and must not be made.  The
+ * call makes no hipMalloc or hipFree and no allocating library call. */
+lrc_status lrc_scan_prefill_static(const float* a, const float* b, float* h, float* state,
+                                   const int* lens_host, int P, int D, int N, void* stream);
 
 /* ------------------------------------------------------------------------
  * K2  RWKV-4 WKV over rows  [rwkv]

@@ -344,6 +344,24 @@ lrc_status lrc_scan_prefill_ws(const float* a, const float* b, float* h, float* 
     return check_launch(lrc::launch_scan_tiled(a, b, h, state, bt, E, workspace, st), st, "scan prefill (tiled)");
 }
 
+lrc_status lrc_scan_prefill_static(const float* a, const float* b, float* h, float* state, const int* lens_host,
+                                   int P, int D, int N, void* stream) {
+    thread_local lrc::Batch bt;
+    long rows = 0;
+    lrc_status s = packed_batch(lens_host, P, bt, rows);
+    if (s != LRC_OK) return s;
+    if ((s = scan_common(a, b, h, state, state, rows, P, D, N)) != LRC_OK) return s;
+    const long E = (long)D * N;
+    const size_t need = lrc::scan_workspace_bytes(P, E);
+    REQUIRE(need <= lrc::kScanStaticScratchBytes, LRC_ERR_SHAPE,
+            "%d prompts of %ld state elements need %zu bytes of scratch, more than the fixed %zu (at most %zu "
+            "prompt x 128-element blocks)",
+            P, E, need, lrc::kScanStaticScratchBytes, (lrc::kScanStaticScratchBytes - 256) / 8);
+    REQUIRE(lrc::scan_tiled_tiles_bound(rows, P, E) < (1l << 31), LRC_ERR_SHAPE, "too many tiles for one launch");
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_scan_tiled_static(a, b, h, state, bt, E, st), st, "scan prefill (fixed scratch)");
+}
+
 lrc_status lrc_wait_timeouts(unsigned* count_host, int reset, void* stream) {
     REQUIRE_PTR(count_host);
     auto st = static_cast<hipStream_t>(stream);

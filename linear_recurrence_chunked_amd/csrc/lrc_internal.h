@@ -44,7 +44,13 @@ hipError_t launch_scan(const float* a, const float* b, float* h, const float* h0
 size_t scan_workspace_bytes(int P, long E);
 long scan_tiled_tiles_bound(long rows, int P, long E);  // at least the tiled scan's tile count
 hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
-                             void* workspace, hipStream_t st);hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
+                             void* workspace, hipStream_t st);
+// The tiled driver with its control block and flags in a fixed device array
+// of kScanStaticScratchBytes (one per GPU) instead of a caller's workspace.
+constexpr size_t kScanStaticScratchBytes = size_t(2) << 20;
+hipError_t launch_scan_tiled_static(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
+                                    hipStream_t st);
+hipError_t launch_wkv4(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                        float* den, float* mx, const Batch& bt, int C, hipStream_t st);
 hipError_t launch_wkv_tdecay(const float* k, const float* v, const float* w, const float* u, float* wkv, float* num,
                              float* den, float* mx, const Batch& bt, int C, hipStream_t st);

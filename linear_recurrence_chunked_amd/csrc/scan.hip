@@ -30,6 +30,7 @@
 //  The row loads and stores are nontemporal: every byte is used once.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "lrc_device.h"
 #include "lrc_internal.h"
@@ -489,6 +490,53 @@ hipError_t launch_scan_tiled(const float* a, const float* b, float* h, float* st
     hipLaunchKernelGGL((scan_tile_kernel<kScanTileCols>), dim3((unsigned)grid), dim3(kScanTileCols * 4), 0, st, a, b, h,
                        state, bt, tl, E, flags, ctl, gen, ntickets);
     return hipGetLastError();
+}
+
+
+// ------------------------------------------------------- fixed device scratch
+// The tiled driver's control block and completion flags in a file-scope
+// device array instead of a caller's workspace, for callers that cannot
+// allocate.  Each GPU holds its own copy until the process ends; its address
+// comes from hipGetSymbolAddress, once per device, with that device current
+// (the array's name in host code is not a device address).  The first call
+// on a device zero-fills it with a kernel on the caller's stream.  Every call
+// on one GPU shares it, so calls that may run at the same time on one GPU
+// race; the ticket counter is reset by every launch and the flags carry the
+// call's generation, so nothing else needs clearing between calls.
+namespace {
+static __device__ __align__(256) unsigned char scan_scratch[kScanStaticScratchBytes];
+
+__global__ void scan_scratch_clear(uint4* p, long n16) {
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n16; i += (long)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t launch_scan_tiled_static(const float* a, const float* b, float* h, float* state, const Batch& bt, long E,
+                                    hipStream_t st) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        p = ptr[dev];
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scan_scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            hipLaunchKernelGGL(scan_scratch_clear, dim3(64), dim3(256), 0, st, static_cast<uint4*>(p),
+                               (long)(kScanStaticScratchBytes / 16));
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            ptr[dev] = p;
+        }
+    }
+    return launch_scan_tiled(a, b, h, state, bt, E, p, st);
 }
 
 }  // namespace lrc

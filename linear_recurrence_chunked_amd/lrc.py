@@ -42,6 +42,7 @@ _SIGS = {
     "lrc_scan_rows": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "lrc_scan_prefill": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
     "lrc_scan_prefill_ws": [_P, _P, _P, _P, _IP, _I, _I, _I, _P, ctypes.c_size_t, _P],
+    "lrc_scan_prefill_static": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
     "lrc_wkv4_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
     "lrc_wkv4_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _P],
     "lrc_wkv_tdecay_rows": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P],
@@ -227,6 +228,20 @@ def scan_prefill_ws(a, b, h, state, lens, ws):
         raise ValueError("ws must be a contiguous 1-D uint8 tensor")
     _check(lib.lrc_scan_prefill_ws(_ptr(a), _ptr(b), _ptr(h), _ptr(state), arr, P, D, N, _ptr(ws), ws.numel(),
                                    _stream(a)))
+
+
+def scan_prefill_static(a, b, h, state, lens):
+    """scan_prefill_ws without a workspace: the library's fixed 2 MiB device scratch (one per GPU)
+    holds the tiled driver's flags.  Calls that overlap on one GPU race."""
+    _dev(a, b, h, state)
+    R, D, N = a.shape
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but a has {R} rows")
+    for t, n in ((a, "a"), (b, "b"), (h, "h")):
+        _need(t, torch.float32, (R, D, N), n)
+    _need(state, torch.float32, (P, D, N), "state")
+    _check(lib.lrc_scan_prefill_static(_ptr(a), _ptr(b), _ptr(h), _ptr(state), arr, P, D, N, _stream(a)))
 
 
 def wait_timeouts(reset: bool = False) -> int:

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
               "lrc_wkv4_prefill", "lrc_gdn_chunk", "lrc_gdn_prefill", "lrc_unit_lower_inverse",
               "lrc_time_shift_rows", "lrc_time_shift_prefill", "lrc_mamba_mixer_rows", "lrc_mamba_mixer_prefill",
               "lrc_wkv_tdecay_rows", "lrc_wkv_tdecay_prefill", "lrc_scan_prefill_ws", "lrc_scan_workspace_size",
-              "lrc_wait_timeouts",
+              "lrc_scan_prefill_static", "lrc_wait_timeouts",
               "lrc_status_string", "lrc_last_error", "lrc_version"]:
         assert n in names
 
@@ -103,6 +103,23 @@ def test_scan_tiled_workspace_size_and_rejects(L):
     assert _st(L, f(A0, A1, A2, A3, lens, 3, 4, 16, A3, need, None)) == "LRC_ERR_ALIAS"  # on the state
     bad = (ctypes.c_int * 3)(5, -1, 7)
     assert _st(L, f(A0, A1, A2, A3, bad, 3, 4, 16, A4, need, None)) == "LRC_ERR_ROWS"
+
+
+def test_scan_static_rejects_beyond_its_scratch(L):
+    """The allocation-free tiled scan keeps its flags in a fixed 2 MiB array: a 256-byte control block
+    and one 8-byte flag per (prompt, block of 128 state elements), so at most 262 112 such pairs."""
+    f = L.lib.lrc_scan_prefill_static
+    lens = (ctypes.c_int * 256)(*([3] * 256))
+    far = [0x1000000000 * (i + 1) for i in range(4)]  # 64 GiB apart: the tensors below never overlap
+    # 256 prompts x 1024 blocks (D * N = 131 072) need 256 + 8 * 262 144 bytes: one block too many per prompt
+    assert _st(L, f(*far, lens, 256, 8192, 16, None)) == "LRC_ERR_SHAPE"
+    assert "scratch" in L.lib.lrc_last_error().decode()
+    bad = (ctypes.c_int * 3)(5, -1, 7)
+    assert _st(L, f(A0, A1, A2, A3, bad, 3, 4, 16, None)) == "LRC_ERR_ROWS"
+    lens3 = (ctypes.c_int * 3)(5, 1, 7)
+    assert _st(L, f(None, A1, A2, A3, lens3, 3, 4, 16, None)) == "LRC_ERR_NULL"
+    assert _st(L, f(A0, A1, A0, A3, lens3, 3, 4, 16, None)) == "LRC_ERR_ALIAS"
+    assert _st(L, f(MIS, A1, A2, A3, lens3, 3, 4, 16, None)) == "LRC_ERR_ALIGN"
 
 
 def test_conv_rejects_bad_width_dtype_rows(L):
