@@ -227,6 +227,30 @@ lrc_status lrc_gdn_prefill(const void* q, const void* k, const void* v, const fl
                            const float* g, float* o, float* state, const int* lens_host, int P,
                            int Hk, int Hv, int dk, int dv, lrc_dtype dt, void* stream);
 
+/* K3 driver, chunk-parallel form [qwen], for launches with few prompts.
+ * With T = (I + A)^-1 the chunk's U regroups as U = U' - W S_0, where
+ * U' = T diag(beta) V and W = T diag(beta Gamma) K need no state.  A first
+ * kernel forms A, T, W, U', the masked decayed Q K^T and the per-row decays of
+ * every (chunk, value head) at once, into `workspace`; a second walks each
+ * prompt's chunks and runs only the products with the state (W S_0, Q S_0,
+ * the outputs and the state update).  Same arguments and results as
+ * lrc_gdn_prefill (within the bf16 tolerance; the association differs), for
+ * LRC_BF16 inputs only (LRC_ERR_DTYPE otherwise).  lrc_gdn_prefill is the
+ * faster choice when prompts x value heads fill the GPU's compute units;
+ * this form when they do not (one long prompt, say).
+ *  workspace   device memory of at least lrc_gdn_workspace_bytes(P, R, Hk,
+ *              Hv, dk, dv, dt) bytes for R = sum of lens, 16-byte aligned,
+ *              owned by the caller, no initial contents needed; it must not
+ *              overlap a tensor, and calls that may run at the same time must
+ *              not share it.  (72.5 KiB per 64-row chunk and value head at
+ *              dk = dv = 128.)
+ * lrc_gdn_workspace_bytes returns 0 for arguments the call rejects. */
+size_t lrc_gdn_workspace_bytes(int P, long total_rows, int Hk, int Hv, int dk, int dv, lrc_dtype dt);
+lrc_status lrc_gdn_prefill_ws(const void* q, const void* k, const void* v, const float* beta,
+                              const float* g, float* o, float* state, const int* lens_host, int P,
+                              int Hk, int Hv, int dk, int dv, lrc_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* The triangular inverse of K3 on its own, at the precision K3 uses (FP32):
    T = (I + strictly_lower(A))^-1 for `batch` matrices of n x n, n <= 64,
    padded to 64 rows with identity.  A, T [batch, n, n] float; T must not

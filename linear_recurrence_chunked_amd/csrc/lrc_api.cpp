@@ -448,6 +448,41 @@ lrc_status lrc_gdn_prefill(const void* q, const void* k, const void* v, const fl
                         "gdn prefill");
 }
 
+size_t lrc_gdn_workspace_bytes(int P, long total_rows, int Hk, int Hv, int dk, int dv, lrc_dtype dt) {
+    if (P < 1 || total_rows < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || dt != LRC_BF16) return 0;
+    if ((dk != 32 && dk != 64 && dk != 128) || (dv != 32 && dv != 64 && dv != 128)) return 0;
+    return (size_t)(total_rows / 64 + P) * Hv * lrc::gdn_cp_block_bytes(dk, dv);
+}
+
+lrc_status lrc_gdn_prefill_ws(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                              float* o, float* state, const int* lens_host, int P, int Hk, int Hv, int dk, int dv,
+                              lrc_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    thread_local lrc::Batch bt;
+    long rows = 0;
+    lrc_status s = packed_batch(lens_host, P, bt, rows);
+    if (s != LRC_OK) return s;
+    if ((s = gdn_common(q, k, v, beta, g, o, state, state, rows, P, Hk, Hv, dk, dv, dt)) != LRC_OK) return s;
+    REQUIRE(dt == LRC_BF16, LRC_ERR_DTYPE, "the chunk-parallel form takes bf16 inputs (LRC_BF16) only");
+    long chunks = 0;
+    for (int p = 0; p < P; ++p) chunks += (lens_host[p] + 63) / 64;
+    REQUIRE(chunks < (1l << 31), LRC_ERR_SHAPE, "too many chunks for one launch");
+    const size_t need = (size_t)chunks * Hv * lrc::gdn_cp_block_bytes(dk, dv);
+    REQUIRE_PTR_IF(workspace, need > 0);
+    REQUIRE_ALIGN(workspace);
+    REQUIRE(workspace_bytes >= need, LRC_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const uint64_t es = esize(dt);
+    const uint64_t qb = (uint64_t)rows * Hk * dk * es, vb = (uint64_t)rows * Hv * dv * es;
+    const uint64_t gb = (uint64_t)rows * Hv * 4, ob = (uint64_t)rows * Hv * dv * 4;
+    const uint64_t sb = (uint64_t)P * Hv * dk * dv * 4;
+    const void* ts[7] = {q, k, v, beta, g, o, state};
+    const uint64_t tb[7] = {qb, qb, vb, gb, gb, ob, sb};
+    for (int i = 0; i < 7; ++i) REQUIRE(!overlap(workspace, need, ts[i], tb[i]), LRC_ERR_ALIAS, "workspace overlaps a tensor");
+    if (need == 0) return ok();
+    auto st = static_cast<hipStream_t>(stream);
+    return check_launch(lrc::launch_gdn_chunk_parallel(q, k, v, beta, g, o, state, bt, Hk, Hv, dk, dv, workspace, st),
+                        st, "gdn prefill (chunk-parallel)");
+}
+
 lrc_status lrc_unit_lower_inverse(const float* A, float* T, int batch, int n, void* stream) {
     REQUIRE_PTR(A); REQUIRE_PTR(T);
     REQUIRE(batch >= 0 && batch <= (1 << 30), LRC_ERR_SHAPE, "batch %d outside [0, 2^30]", batch);

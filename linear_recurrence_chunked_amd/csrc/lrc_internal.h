@@ -60,6 +60,12 @@ hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* 
 hipError_t launch_gdn_bf16_mfma(const void* q, const void* k, const void* v, const float* beta, const float* g,
                                 float* o, const float* S_in, float* S_out, const Batch& bt, int Hk, int Hv, int dk,
                                 int dv, bool split, hipStream_t st);
+// The chunk-parallel bf16 form: one workspace block of gdn_cp_block_bytes per
+// (chunk, value head); state [P, Hv, dk, dv] updated in place.
+size_t gdn_cp_block_bytes(int dk, int dv);
+hipError_t launch_gdn_chunk_parallel(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                                     float* o, float* state, const Batch& bt, int Hk, int Hv, int dk, int dv,
+                                     void* ws, hipStream_t st);
 hipError_t launch_unit_lower_inverse(const float* A, float* T, int batch, int n, hipStream_t st);
 // `plane` is the element stride between mixed inputs in `out` (rows x C).
 hipError_t launch_time_shift(const float* x, float* out, const float* state_in, float* state_out, const float* mix,

@@ -49,6 +49,7 @@ _SIGS = {
     "lrc_wkv_tdecay_prefill": [_P, _P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _P],
     "lrc_gdn_chunk": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P],
     "lrc_gdn_prefill": [_P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _I, _I, _P],
+    "lrc_gdn_prefill_ws": [_P, _P, _P, _P, _P, _P, _P, _IP, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P],
     "lrc_unit_lower_inverse": [_P, _P, _I, _I, _P],
     "lrc_time_shift_rows": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "lrc_time_shift_prefill": [_P, _P, _P, _P, _IP, _I, _I, _I, _P],
@@ -61,6 +62,8 @@ for _name, _args in _SIGS.items():
     _fn.restype = _S
 lib.lrc_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint), _I, _P]
 lib.lrc_wait_timeouts.restype = _S
+lib.lrc_gdn_workspace_bytes.argtypes = [_I, ctypes.c_long, _I, _I, _I, _I, _I]
+lib.lrc_gdn_workspace_bytes.restype = ctypes.c_size_t
 lib.lrc_scan_workspace_size.argtypes = [_I, _I, _I]
 lib.lrc_scan_workspace_size.restype = ctypes.c_size_t
 lib.lrc_status_string.argtypes = [_S]
@@ -350,6 +353,39 @@ def gdn_prefill(q, k, v, beta, g, o, state, lens, split=False):
     _need(state, torch.float32, (P, Hv, dk, dv), "state")
     _check(lib.lrc_gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o), _ptr(state), arr, P,
                                Hk, Hv, dk, dv, _gdn_dtype_code(q, split), _stream(q)))
+
+
+def gdn_workspace_bytes(P: int, total_rows: int, Hk: int, Hv: int, dk: int, dv: int) -> int:
+    """Bytes of workspace gdn_prefill_ws needs for P prompts of total_rows rows (bf16 inputs)."""
+    return int(lib.lrc_gdn_workspace_bytes(P, total_rows, Hk, Hv, dk, dv, BF16))
+
+
+def gdn_workspace(P: int, total_rows: int, Hk: int, Hv: int, dk: int, dv: int, device) -> torch.Tensor:
+    """A workspace for gdn_prefill_ws (uint8; no initial contents needed)."""
+    return torch.empty(gdn_workspace_bytes(P, total_rows, Hk, Hv, dk, dv), dtype=torch.uint8, device=device)
+
+
+def gdn_prefill_ws(q, k, v, beta, g, o, state, lens, ws):
+    """gdn_prefill in its chunk-parallel form (bf16 q, k, v): the state-free part of every chunk at
+    once into ws, then the state products chunk by chunk.  ws from gdn_workspace."""
+    _dev(q, k, v, beta, g, o, state, ws)
+    R, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    arr, P, total = _lens(lens)
+    if total != R:
+        raise ValueError(f"sum(lens) = {total} but q has {R} rows")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("gdn_prefill_ws takes bf16 q, k, v")
+    _need(k, q.dtype, q.shape, "k")
+    _need(v, q.dtype, (R, Hv, dv), "v")
+    _need(beta, torch.float32, (R, Hv), "beta")
+    _need(g, torch.float32, (R, Hv), "g")
+    _need(o, torch.float32, (R, Hv, dv), "o")
+    _need(state, torch.float32, (P, Hv, dk, dv), "state")
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous 1-D uint8 tensor")
+    _check(lib.lrc_gdn_prefill_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o), _ptr(state), arr, P,
+                                  Hk, Hv, dk, dv, BF16, _ptr(ws), ws.numel(), _stream(q)))
 
 
 def unit_lower_inverse(A, T):

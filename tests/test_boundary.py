@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
               "lrc_wkv4_prefill", "lrc_gdn_chunk", "lrc_gdn_prefill", "lrc_unit_lower_inverse",
               "lrc_time_shift_rows", "lrc_time_shift_prefill", "lrc_mamba_mixer_rows", "lrc_mamba_mixer_prefill",
               "lrc_wkv_tdecay_rows", "lrc_wkv_tdecay_prefill", "lrc_scan_prefill_ws", "lrc_scan_workspace_size",
-              "lrc_scan_prefill_static", "lrc_wait_timeouts",
+              "lrc_scan_prefill_static", "lrc_wait_timeouts", "lrc_gdn_prefill_ws", "lrc_gdn_workspace_bytes",
               "lrc_status_string", "lrc_last_error", "lrc_version"]:
         assert n in names
 
@@ -120,6 +120,29 @@ def test_scan_static_rejects_beyond_its_scratch(L):
     assert _st(L, f(None, A1, A2, A3, lens3, 3, 4, 16, None)) == "LRC_ERR_NULL"
     assert _st(L, f(A0, A1, A0, A3, lens3, 3, 4, 16, None)) == "LRC_ERR_ALIAS"
     assert _st(L, f(MIS, A1, A2, A3, lens3, 3, 4, 16, None)) == "LRC_ERR_ALIGN"
+
+
+def test_gdn_chunk_parallel_workspace_and_rejects(L):
+    """The chunk-parallel DeltaNet form: one workspace block per (64-row chunk, value head) of
+    W, K^T, P (bf16), U' (FP32) and two per-row vectors, 72.5 KiB at dk = dv = 128; bf16 only."""
+    blk = 256 * 128 + 64 * 64 * 2 + 256 * 128 + 512
+    assert blk == 74240
+    assert L.gdn_workspace_bytes(1, 2048, 16, 32, 128, 128) == (2048 // 64 + 1) * 32 * blk
+    assert L.gdn_workspace_bytes(1, 64, 1, 1, 32, 32) == 2 * (256 * 32 + 8192 + 256 * 32 + 512)
+    assert L.lib.lrc_gdn_workspace_bytes(1, 64, 1, 1, 32, 32, L.F32) == 0
+    assert L.lib.lrc_gdn_workspace_bytes(1, 64, 2, 3, 32, 32, L.BF16) == 0
+    f = L.lib.lrc_gdn_prefill_ws
+    lens = (ctypes.c_int * 2)(70, 5)  # 3 chunks
+    need = 3 * 4 * (256 * 64 + 8192 + 256 * 64 + 512)
+    args = [A0, A1, A2, A3, A4, A5, A6, lens, 2, 2, 4, 64, 64]
+    assert _st(L, f(*args, L.F32, A7, need, None)) == "LRC_ERR_DTYPE"
+    assert _st(L, f(*args, L.BF16_SPLIT, A7, need, None)) == "LRC_ERR_DTYPE"
+    assert _st(L, f(*args, L.BF16, A7, need - 1, None)) == "LRC_ERR_SHAPE"
+    assert _st(L, f(*args, L.BF16, None, need, None)) == "LRC_ERR_NULL"
+    assert _st(L, f(*args, L.BF16, A7 + 8, need, None)) == "LRC_ERR_ALIGN"
+    assert _st(L, f(*args, L.BF16, A6 + 64, need, None)) == "LRC_ERR_ALIAS"  # inside the state
+    bad = (ctypes.c_int * 2)(70, -5)
+    assert _st(L, f(A0, A1, A2, A3, A4, A5, A6, bad, 2, 2, 4, 64, 64, L.BF16, A7, need, None)) == "LRC_ERR_ROWS"
 
 
 def test_conv_rejects_bad_width_dtype_rows(L):
