@@ -63,19 +63,23 @@ struct CpChunks {
     int off[LRC_MAX_PROMPTS + 1];
 };
 
+// About 78 KiB at dk = dv = 128, so that two workgroups share a compute unit.
+// Q never enters LDS (its fragments are read from memory); V is staged
+// transposed; T diag(beta Gamma) and T diag(beta) take the space of the K rows,
+// which are dead once A and K^T are formed.
 template <int DK, int DV>
 struct CpPrepSmem {
-    static constexpr int LDK = DK + 8, LDV = DV + 8;
-    __bf16 K[64 * LDK];
-    __bf16 Q[64 * LDK];
-    __bf16 V[64 * LDV];
-    __bf16 KT[DK * L64];
-    __bf16 VT[DV * L64];
-    __bf16 Tg[64 * L64];  // T diag(beta Gamma)
-    __bf16 Tb[64 * L64];  // T diag(beta)
+    static constexpr int LDK = DK + 8;
+    static constexpr int R1 = 64 * LDK > 2 * 64 * L64 ? 64 * LDK : 2 * 64 * L64;
+    __bf16 KT_[R1];       // K rows, then T diag(beta Gamma) and T diag(beta)
+    __bf16 KT[DK * L64];  // K^T
+    __bf16 VT[DV * L64];  // V^T
     float M[64 * kTriLd];  // A, then T
     float scratch[kTriScratch];
     float gam[64], Gam[64], beta[64];
+    __device__ __bf16* K() { return KT_; }
+    __device__ __bf16* Tg() { return KT_; }             // T diag(beta Gamma)
+    __device__ __bf16* Tb() { return KT_ + 64 * L64; }  // T diag(beta)
 };
 
 // Rows r = 0 .. 63 of a [64][D] bf16 tile in LDS (row stride ld) into its
@@ -115,42 +119,51 @@ __device__ __forceinline__ void cp_locate(const CpChunks& cm, int P, int c, int&
 
 // ------------------------------------------------------------------ prep
 template <int DK, int DV>
-__global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
+__global__ __launch_bounds__(64 * kCpPrepWaves, 2) void gdn_cp_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ g, Batch bt, CpChunks cm, int Hk, int Hv,
     unsigned char* __restrict__ ws) {
     using Sm = CpPrepSmem<DK, DV>;
     using Blk = CpBlock<DK, DV>;
-    constexpr int LDK = Sm::LDK, LDV = Sm::LDV;
+    constexpr int LDK = Sm::LDK;
     constexpr int NT = 64 * kCpPrepWaves;
+    constexpr int KS = DK / 32;
+    constexpr int NP = 3;  // tile pairs w, w + 4, w + 8 of the 10 below the diagonal
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // grid.x is the chunk count rounded up to a multiple of 8: workgroups go to the 8 XCDs
+    // in launch order, so the value heads of one key head, which read the same K and Q
+    // rows, run on one XCD and share its L2
     const int c = blockIdx.x, h = blockIdx.y, kh = h / (Hv / Hk);
+    if (c >= cm.total) return;
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
+    const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
     int p, j;
     cp_locate(cm, bt.P, c, p, j);
     const long r0 = batch_row0(bt, p) + 64l * j;
     const int S = min(64, batch_len(bt, p) - 64 * j);
     unsigned char* blk = ws + ((long)c * Hv + h) * Blk::BYTES;
 
-    // ---- stage K, Q, V rows (rows past the chunk read as zero), g and beta
+    // ---- stage K rows and V^T (rows past the chunk read as zero), g and beta; the Q
+    //      fragments of this wave's tile pairs go to registers
+    bf16x8 qf[KS][NP];
     {
         const uint32_t rowK = Hk * DK * 2, rowV = Hv * DV * 2;
         const auto krs = buffer_rsrc(k + (r0 * Hk + kh) * DK, (uint32_t)S * rowK);
         const auto qrs = buffer_rsrc(q + (r0 * Hk + kh) * DK, (uint32_t)S * rowK);
         const auto vrs = buffer_rsrc(v + (r0 * Hv + h) * DV, (uint32_t)S * rowV);
         // every load first, then the LDS stores: the loads are in flight together
-        constexpr int NKQ = 8 * DK / NT, NV = 8 * DV / NT;
+        constexpr int NK = 8 * DK / NT, NV = 8 * DV / NT;
         static_assert(8 * DK % NT == 0 && 8 * DV % NT == 0, "whole 16-byte pieces per thread");
-        u32x4 ka[NKQ], qa[NKQ], va[NV];
+        u32x4 ka[NK], va[NV];
 #pragma unroll
-        for (int x = 0; x < NKQ; ++x) {
+        for (int x = 0; x < NK; ++x) {
             const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            const uint32_t off = (uint32_t)r * rowK + c8 * 2;
-            ka[x] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-            qa[x] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+            ka[x] = __builtin_amdgcn_raw_buffer_load_b128(krs, (uint32_t)r * rowK + c8 * 2, 0, 0);
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
@@ -158,15 +171,26 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
             va[x] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (uint32_t)r * rowV + c8 * 2, 0, 0);
         }
 #pragma unroll
-        for (int x = 0; x < NKQ; ++x) {
+        for (int s8 = 0; s8 < KS; ++s8)
+#pragma unroll
+            for (int x = 0; x < NP; ++x) {
+                int ti, tj;
+                tile_pair(min(w + 4 * x, 9), ti, tj);
+                qf[s8][x] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, (uint32_t)(16 * ti + lr) * rowK + (32 * s8 + lk) * 2,
+                                                                  0, 0));
+            }
+#pragma unroll
+        for (int x = 0; x < NK; ++x) {
             const int e = tid + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sm.K[r * LDK + c8]) = make_uint4(ka[x][0], ka[x][1], ka[x][2], ka[x][3]);
-            *reinterpret_cast<uint4*>(&sm.Q[r * LDK + c8]) = make_uint4(qa[x][0], qa[x][1], qa[x][2], qa[x][3]);
+            *reinterpret_cast<u32x4*>(&sm.K()[r * LDK + c8]) = ka[x];
         }
 #pragma unroll
         for (int x = 0; x < NV; ++x) {
             const int e = tid + x * NT, r = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sm.V[r * LDV + c8]) = make_uint4(va[x][0], va[x][1], va[x][2], va[x][3]);
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, va[x]);
+#pragma unroll
+            for (int z = 0; z < 8; ++z) sm.VT[(c8 + z) * L64 + r] = vv[z];
         }
         if (w == kCpPrepWaves - 1) {
             const auto grs = buffer_rsrc(g + r0 * Hv + h, (uint32_t)S * Hv * 4);
@@ -187,25 +211,20 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
     }
     __syncthreads();
 
-    // ---- A (FP32, into M); P (bf16, into the block); K^T, V^T
+    // ---- A (FP32, into M); P (bf16, into the block); K^T
     {
-        int tid_c = tid;
-        asm volatile("" : "+v"(tid_c));
-        const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
-        constexpr int KS = DK / 32;
-        constexpr int NP = 3;  // tile pairs w, w + 4, w + 8 of the 10 below the diagonal
         floatx4 kk[NP], qk[NP];
 #pragma unroll
         for (int x = 0; x < NP; ++x) kk[x] = qk[x] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s8 = 0; s8 < KS; ++s8)
 #pragma unroll
             for (int x = 0; x < NP; ++x) {
                 int ti, tj;
                 tile_pair(min(w + 4 * x, 9), ti, tj);
-                const bf16x8 kj = frag(&sm.K[(16 * tj + lr) * LDK + 32 * s + lk]);
-                kk[x] = mfma(kj, frag(&sm.K[(16 * ti + lr) * LDK + 32 * s + lk]), kk[x]);
-                qk[x] = mfma(kj, frag(&sm.Q[(16 * ti + lr) * LDK + 32 * s + lk]), qk[x]);
+                const bf16x8 kj = frag(&sm.K()[(16 * tj + lr) * LDK + 32 * s8 + lk]);
+                kk[x] = mfma(kj, frag(&sm.K()[(16 * ti + lr) * LDK + 32 * s8 + lk]), kk[x]);
+                qk[x] = mfma(kj, qf[s8][x], qk[x]);
             }
         __bf16* P = reinterpret_cast<__bf16*>(blk + Blk::P);
 #pragma unroll
@@ -232,8 +251,7 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
             const int ti = t < 3 ? 0 : (t < 5 ? 1 : 2), tj = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
             *reinterpret_cast<uint4*>(&P[(16 * ti + r) * 64 + 16 * tj + 8 * half]) = make_uint4(0u, 0u, 0u, 0u);
         }
-        transpose64(sm.K, LDK, sm.KT, DK, tid, NT);
-        transpose64(sm.V, LDV, sm.VT, DV, tid, NT);
+        transpose64(sm.K(), LDK, sm.KT, DK, tid, NT);
     }
 
     // ---- T = (I + A)^-1
@@ -262,8 +280,8 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
                 tb[r] = static_cast<__bf16>(t4[r] * b4[r]);
                 tg[r] = static_cast<__bf16>(t4[r] * (b4[r] * G4[r]));
             }
-            *reinterpret_cast<bf16x4*>(&sm.Tg[i * L64 + cc]) = tg;
-            *reinterpret_cast<bf16x4*>(&sm.Tb[i * L64 + cc]) = tb;
+            *reinterpret_cast<bf16x4*>(&sm.Tg()[i * L64 + cc]) = tg;
+            *reinterpret_cast<bf16x4*>(&sm.Tb()[i * L64 + cc]) = tb;
         }
         __bf16* KT = reinterpret_cast<__bf16*>(blk + Blk::KT);
         for (int e = tid; e < DK * 8; e += NT) {
@@ -276,17 +294,14 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
     // ---- W^T = K^T (T diag(beta Gamma))^T and U'^T = V^T (T diag(beta))^T: lane (column i, rows
     //      d = 16 td + 4 lg .. +3) writes 4 consecutive entries of row i of W and U'
     {
-        int tid_c = tid;
-        asm volatile("" : "+v"(tid_c));
-        const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
         __bf16* W = reinterpret_cast<__bf16*>(blk + Blk::W);
         float* Up = reinterpret_cast<float*>(blk + Blk::U);
         for (int tile = w; tile < (DK / 16) * 4; tile += kCpPrepWaves) {
             const int td = tile >> 2, ti = tile & 3;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(frag(&sm.KT[(16 * td + lr) * L64 + lk]), frag(&sm.Tg[(16 * ti + lr) * L64 + lk]), acc);
+            acc = mfma(frag(&sm.KT[(16 * td + lr) * L64 + lk]), frag(&sm.Tg()[(16 * ti + lr) * L64 + lk]), acc);
             if (ti >= 2)
-                acc = mfma(frag(&sm.KT[(16 * td + lr) * L64 + 32 + lk]), frag(&sm.Tg[(16 * ti + lr) * L64 + 32 + lk]),
+                acc = mfma(frag(&sm.KT[(16 * td + lr) * L64 + 32 + lk]), frag(&sm.Tg()[(16 * ti + lr) * L64 + 32 + lk]),
                            acc);
             bf16x4 wv;
 #pragma unroll
@@ -296,9 +311,9 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
         for (int tile = w; tile < (DV / 16) * 4; tile += kCpPrepWaves) {
             const int tc = tile >> 2, ti = tile & 3;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(frag(&sm.VT[(16 * tc + lr) * L64 + lk]), frag(&sm.Tb[(16 * ti + lr) * L64 + lk]), acc);
+            acc = mfma(frag(&sm.VT[(16 * tc + lr) * L64 + lk]), frag(&sm.Tb()[(16 * ti + lr) * L64 + lk]), acc);
             if (ti >= 2)
-                acc = mfma(frag(&sm.VT[(16 * tc + lr) * L64 + 32 + lk]), frag(&sm.Tb[(16 * ti + lr) * L64 + 32 + lk]),
+                acc = mfma(frag(&sm.VT[(16 * tc + lr) * L64 + 32 + lk]), frag(&sm.Tb()[(16 * ti + lr) * L64 + 32 + lk]),
                            acc);
             *reinterpret_cast<floatx4*>(&Up[(16 * ti + lr) * DV + 16 * tc + lq]) = acc;
         }
@@ -306,37 +321,57 @@ __global__ __launch_bounds__(64 * kCpPrepWaves) void gdn_cp_prep_kernel(
 }
 
 // ------------------------------------------------------------------ state
-template <int DK>
+// LDS of the state kernel: W and K^T (with the state-update decay) of two
+// chunks, Q and P (with Gamma) of two chunks, and the bf16 fragments of S_0
+// and U that each state wave hands to its output wave, by chunk parity.
+template <int DK, int NSW>
 struct CpStateSmem {
     static constexpr int LDK = DK + 8;
+    static constexpr int KS = DK / 32;
     __bf16 W[2][64 * LDK];
-    __bf16 Q[2][64 * LDK];
     __bf16 KT[2][DK * L64];
+    __bf16 Q[2][64 * LDK];
     __bf16 P[2][64 * L64];
-    float Gam[2][64];
-    float dec[2][64];
+    float dec[2][64];  // with W, K^T: e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
+    float Gam[2][64];  // with Q, P: e^{gamma_r}
+    float GS[2];       // with W, K^T: e^{gamma_S}
+    alignas(16) bf16x8 xs[2][NSW][KS][64];  // S_0 as B fragments, per lane
+    alignas(16) bf16x8 xu[2][NSW][2][64];   // U as B fragments, per lane
 };
 
-// Grid (value heads x column slices, prompts); NSW state waves of 16 CGW
-// columns each (a slice is 16 CGW NSW columns), then kCpLoaders loader waves.
-// With CGW = 2 a lane's two 16-column groups are the even and the odd columns
-// of the wave's 32, so that U', O and the state move as column pairs.
-template <int DK, int DV, int NSW, int CGW>
-__global__ __launch_bounds__(64 * (NSW + kCpLoaders), 1) void gdn_cp_state_kernel(
+// Grid (value heads x column slices, prompts).  Waves: NSW state waves of 16
+// columns each, then NSW output waves (one per state wave, same columns),
+// then kCpLoaders loader waves.  In iteration n the state waves run the chain
+// that chunk n + 1 depends on (W S_0, U = U' - W S_0, the state update) and
+// hand S_0 and U of chunk n to the output waves, which form O of chunk n - 1
+// (diag(Gamma) Q S_0 + P U) at the same time; the loaders stage W, K^T of
+// chunk n + 1 and Q, P of chunk n.  One workgroup barrier per iteration.
+template <int DK, int DV, int NSW>
+__global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_kernel(
     const uint16_t* __restrict__ q, float* __restrict__ o, float* state, Batch bt, CpChunks cm, int Hk, int Hv,
     const unsigned char* __restrict__ ws) {
-    using Sm = CpStateSmem<DK>;
+    using Sm = CpStateSmem<DK, NSW>;
     using Blk = CpBlock<DK, DV>;
     constexpr int LDK = Sm::LDK;
     constexpr int KS = DK / 32;  // k-steps over dk
     constexpr int RT = DK / 16;  // state row tiles
-    constexpr int NCW = DV / (16 * CGW * NSW);
+    constexpr int NCW = DV / (16 * NSW);
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Sm& sm = *reinterpret_cast<Sm*>(smem_raw);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = blockIdx.x / NCW, slice = blockIdx.x % NCW;
+    // The NCW column slices of a head read the same W, K^T, Q and P: with Hv a multiple
+    // of 8 they are placed 8 workgroups apart, on one XCD, so that they share its L2.
+    int h, slice;
+    if (NCW > 1 && Hv % 8 == 0) {
+        const int grp = blockIdx.x / (8 * NCW), r = blockIdx.x % (8 * NCW);
+        h = 8 * grp + r % 8;
+        slice = r / 8;
+    } else {
+        h = blockIdx.x / NCW;
+        slice = blockIdx.x % NCW;
+    }
     const int kh = h / (Hv / Hk);
     const int p = batch_prompt(bt, blockIdx.y);
     const int L = batch_len(bt, p);
@@ -344,19 +379,43 @@ __global__ __launch_bounds__(64 * (NSW + kCpLoaders), 1) void gdn_cp_state_kerne
     if (nc == 0) return;  // the state stays as it is
     const long row0 = batch_row0(bt, p);
     const int c0 = cm.off[p];
+    const uint32_t rowV = Hv * DV;
     auto block = [&](int n) { return ws + ((long)(c0 + n) * Hv + h) * Blk::BYTES; };
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
+    const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lq = lg * 4;
 
-    if (w >= NSW) {
-        // ================= loader waves: chunk n into LDS buffer n & 1
-        const int lt = tid - 64 * NSW;
+    if (w >= 2 * NSW) {
+        // ================= loader waves
+        const int lt = tid - 128 * NSW;
         constexpr int NT = 64 * kCpLoaders;
         const uint32_t rowK = Hk * DK * 2;
         constexpr int NP8 = 8 * DK / NT;  // 16-byte pieces of W, Q and K^T per loader thread
         static_assert(8 * DK % NT == 0 && 512 % NT == 0, "whole 16-byte pieces per loader thread");
-        u32x4 rw[NP8], rq[NP8], rk[NP8], rp[512 / NT];
-        float rg = 0.f, rd = 0.f;
-        // all loads of chunk n first (they are in flight together), the LDS stores later
-        auto issue = [&](int n) __attribute__((always_inline)) {
+        u32x4 rw[NP8], rk[NP8], rq[NP8], rp[512 / NT];
+        float rdec = 0.f, rgam = 0.f;
+        // loads into registers (all in flight together), LDS stores one iteration later
+        auto issue_wk = [&](int n) __attribute__((always_inline)) {
+            const auto brs = buffer_rsrc(block(n), (uint32_t)Blk::BYTES);
+#pragma unroll
+            for (int x = 0; x < NP8; ++x) {
+                const int e = lt + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+                rw[x] = __builtin_amdgcn_raw_buffer_load_b128(brs, (uint32_t)(Blk::W + (r * DK + c8) * 2), 0, 0);
+                rk[x] = __builtin_amdgcn_raw_buffer_load_b128(brs, (uint32_t)(Blk::KT + e * 16), 0, 0);  // [DK][64]
+            }
+            rdec = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, (uint32_t)(Blk::DEC + lt * 4), 0, 0));
+        };
+        auto commit_wk = [&](int n) __attribute__((always_inline)) {
+            const int b = n & 1;
+#pragma unroll
+            for (int x = 0; x < NP8; ++x) {
+                const int e = lt + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+                *reinterpret_cast<u32x4*>(&sm.W[b][r * LDK + c8]) = rw[x];
+                *reinterpret_cast<u32x4*>(&sm.KT[b][(e >> 3) * L64 + (e & 7) * 8]) = rk[x];
+            }
+            if (lt < 64) sm.dec[b][lt] = rdec;
+        };
+        auto issue_qp = [&](int n) __attribute__((always_inline)) {
             const int S = min(64, L - 64 * n);
             const auto brs = buffer_rsrc(block(n), (uint32_t)Blk::BYTES);
             const auto qrs = buffer_rsrc(q + ((row0 + 64l * n) * Hk + kh) * DK, (uint32_t)S * rowK);
@@ -364,57 +423,100 @@ __global__ __launch_bounds__(64 * (NSW + kCpLoaders), 1) void gdn_cp_state_kerne
             for (int x = 0; x < NP8; ++x) {
                 const int e = lt + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
                 rq[x] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (uint32_t)r * rowK + c8 * 2, 0, 0);
-                rw[x] = __builtin_amdgcn_raw_buffer_load_b128(brs, (uint32_t)(Blk::W + (r * DK + c8) * 2), 0, 0);
-                rk[x] = __builtin_amdgcn_raw_buffer_load_b128(brs, (uint32_t)(Blk::KT + e * 16), 0, 0);  // [DK][64]
             }
 #pragma unroll
             for (int x = 0; x < 512 / NT; ++x)
                 rp[x] = __builtin_amdgcn_raw_buffer_load_b128(brs, (uint32_t)(Blk::P + (lt + x * NT) * 16), 0, 0);
-            const auto rrs = buffer_rsrc(block(n) + Blk::GAM, 2 * 64 * 4);  // Gamma, then the decay
-            rg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rrs, lt * 4, 0, 0));
-            rd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rrs, (64 + lt) * 4, 0, 0));
+            rgam = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, (uint32_t)(Blk::GAM + lt * 4), 0, 0));
         };
-        auto commit = [&](int n) __attribute__((always_inline)) {
+        auto commit_qp = [&](int n) __attribute__((always_inline)) {
             const int b = n & 1;
 #pragma unroll
             for (int x = 0; x < NP8; ++x) {
                 const int e = lt + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
                 *reinterpret_cast<u32x4*>(&sm.Q[b][r * LDK + c8]) = rq[x];
-                *reinterpret_cast<u32x4*>(&sm.W[b][r * LDK + c8]) = rw[x];
-                *reinterpret_cast<u32x4*>(&sm.KT[b][(e >> 3) * L64 + (e & 7) * 8]) = rk[x];
             }
 #pragma unroll
             for (int x = 0; x < 512 / NT; ++x) {
                 const int e = lt + x * NT;
                 *reinterpret_cast<u32x4*>(&sm.P[b][(e >> 3) * L64 + (e & 7) * 8]) = rp[x];
             }
-            if (lt < 64) {
-                sm.Gam[b][lt] = rg;
-                sm.dec[b][lt] = rd;
+            if (lt < 64) sm.Gam[b][lt] = rgam;
+        };
+        // e^{gamma_S} of chunk n: the Gamma of its last row
+        auto commit_gs = [&](int n) __attribute__((always_inline)) {
+            if (lt == 0) {
+                const int S = min(64, L - 64 * n);
+                sm.GS[n & 1] = reinterpret_cast<const float*>(block(n) + Blk::GAM)[S - 1];
             }
         };
-        // chunk n + 1 goes to LDS while the state waves work on chunk n; the
-        // loads of chunk n + 2 are in flight meanwhile
-        issue(0);
-        commit(0);
-        if (nc > 1) issue(1);
+        issue_wk(0);
+        commit_wk(0);
+        commit_gs(0);
+        if (nc > 1) issue_wk(1);
+        issue_qp(0);
         __syncthreads();
-        for (int n = 0; n < nc; ++n) {
+        for (int n = 0; n <= nc; ++n) {
             if (n + 1 < nc) {
-                commit(n + 1);
-                if (n + 2 < nc) issue(n + 2);
+                commit_wk(n + 1);
+                commit_gs(n + 1);
+            }
+            if (n < nc) commit_qp(n);
+            if (n + 2 < nc) issue_wk(n + 2);
+            if (n + 1 < nc) issue_qp(n + 1);
+            __syncthreads();
+        }
+        return;
+    }
+
+    const int pair = w % NSW;  // the state wave and its output wave share 16 columns
+    const int col0 = 16 * (slice * NSW + pair);
+    if (w >= NSW) {
+        // ================= output waves: O of chunk n - 1 in iteration n
+        __syncthreads();
+        for (int n = 0; n <= nc; ++n) {
+            if (n >= 1) {
+                const int m = n - 1, b = m & 1;
+                const int S = min(64, L - 64 * m);
+                floatx4 qs0[4], pu[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) qs0[t] = pu[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const bf16x8 bs = sm.xs[b][pair][s][lane];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        qs0[t] = mfma(frag_perm(&sm.Q[b][(16 * t + lr) * LDK + 32 * s], lg), bs, qs0[t]);
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const bf16x8 bu = sm.xu[b][pair][s][lane];
+#pragma unroll
+                    for (int t = 2 * s; t < 4; ++t)
+                        pu[t] = mfma(frag_perm(&sm.P[b][(16 * t + lr) * L64 + 32 * s], lg), bu, pu[t]);
+                }
+                const auto orsrc = buffer_rsrc(o + (row0 + 64l * m) * (long)rowV + (long)h * DV + col0,
+                                              (uint32_t)S * rowV * 4);
+                uint32_t o_lane = (__umul24(lq, rowV) + lr) * 4;
+                asm volatile("" : "+v"(o_lane));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[b][16 * t + lq]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(G4[r], qs0[t][r], pu[t][r])), orsrc,
+                                                              o_lane + (16 * t + r) * rowV * 4, 0, 0);
+                }
             }
             __syncthreads();
         }
         return;
     }
 
-    // ================= state waves: 32 columns each
-    const int col0 = 16 * CGW * (slice * NSW + w);
-    const uint32_t rowV = Hv * DV;
-    int s_lane = (lane >> 4) * 4 * DV + CGW * (lane & 15);
+    // ================= state waves: 16 columns each
+    int s_lane = (lane >> 4) * 4 * DV + lr;
     asm volatile("" : "+v"(s_lane));
-    floatx4 sacc[CGW][RT];
+    floatx4 sacc[RT];
     const auto srs = buffer_rsrc(state + ((long)p * Hv + h) * DK * DV + col0, (uint32_t)(DK * DV * 4));
     {
         int sl = s_lane * 4, dv4 = DV * 4;
@@ -422,147 +524,71 @@ __global__ __launch_bounds__(64 * (NSW + kCpLoaders), 1) void gdn_cp_state_kerne
 #pragma unroll
         for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (CGW == 2) {
-                    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(srs, sl, (16 * tr + r) * dv4, 0);
-                    sacc[0][tr][r] = __uint_as_float(x[0]);
-                    sacc[1][tr][r] = __uint_as_float(x[1]);
-                } else {
-                    sacc[0][tr][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, sl, (16 * tr + r) * dv4, 0));
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                sacc[tr][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, sl, (16 * tr + r) * dv4, 0));
     }
-    // U' of a chunk in accumulator layout: rows 16t + 4(l/16) + r, the lane's columns
-    float up[CGW][16];
+    // U' of a chunk in accumulator layout: rows 16t + 4(l/16) + r, the lane's column
+    float up[16];
     auto load_up = [&](int n) __attribute__((always_inline)) {
         const auto urs = buffer_rsrc(block(n) + Blk::U, (uint32_t)(64 * DV * 4));
-        uint32_t u_lane = ((lane >> 4) * 4 * DV + col0 + CGW * (lane & 15)) * 4;
+        uint32_t u_lane = ((lane >> 4) * 4 * DV + col0 + lr) * 4;
         asm volatile("" : "+v"(u_lane));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (CGW == 2) {
-                    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(urs, u_lane + (16 * t + r) * DV * 4, 0, 0);
-                    up[0][4 * t + r] = __uint_as_float(x[0]);
-                    up[1][4 * t + r] = __uint_as_float(x[1]);
-                } else {
-                    up[0][4 * t + r] =
-                        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(urs, u_lane + (16 * t + r) * DV * 4, 0, 0));
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                up[4 * t + r] =
+                    __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(urs, u_lane + (16 * t + r) * DV * 4, 0, 0));
     };
     load_up(0);
-    __syncthreads();  // chunk 0 in LDS
+    __syncthreads();  // chunk 0's W and K^T in LDS
 
-    for (int n = 0; n < nc; ++n) {
-        const int b = n & 1;
-        const int S = min(64, L - 64 * n);
-        int tid_c = tid;
-        asm volatile("" : "+v"(tid_c));
-        const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lq = lg * 4;
-        floatx4 ws0[CGW][4], qs0[CGW][4], u[CGW][4];
-
-        // ---- W S_0 and Q S_0
+    for (int n = 0; n <= nc; ++n) {
+        if (n < nc) {
+            const int b = n & 1;
+            // ---- W S_0, with S_0 handed to the output wave as B fragments
+            floatx4 ws0[4], u[4];
 #pragma unroll
-        for (int c = 0; c < CGW; ++c)
+            for (int t = 0; t < 4; ++t) ws0[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) ws0[c][t] = qs0[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 bh, bl;
+                acc_frag<false>(sacc[2 * s], sacc[2 * s + 1], bh, bl);
+                sm.xs[b][pair][s][lane] = bh;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            bf16x8 bh[CGW], bl[CGW];
-#pragma unroll
-            for (int c = 0; c < CGW; ++c) acc_frag<false>(sacc[c][2 * s], sacc[c][2 * s + 1], bh[c], bl[c]);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bf16x8 aw = frag_perm(&sm.W[b][(16 * t + lr) * LDK + 32 * s], lg);
-                const bf16x8 aq = frag_perm(&sm.Q[b][(16 * t + lr) * LDK + 32 * s], lg);
-#pragma unroll
-                for (int c = 0; c < CGW; ++c) {
-                    ws0[c][t] = mfma(aw, bh[c], ws0[c][t]);
-                    qs0[c][t] = mfma(aq, bh[c], qs0[c][t]);
-                }
+                for (int t = 0; t < 4; ++t)
+                    ws0[t] = mfma(frag_perm(&sm.W[b][(16 * t + lr) * LDK + 32 * s], lg), bh, ws0[t]);
             }
-        }
-        read_ahead<4 * KS, 2, 2 * CGW, 2>();
-        // ---- U = U' - W S_0 (zero past the chunk: W and U' rows are zero there)
+            read_ahead<4 * KS, 1, 1, 2>();
+            // ---- U = U' - W S_0 (zero past the chunk: W and U' rows are zero there)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < CGW; ++c) u[c][t][r] = up[c][4 * t + r] - ws0[c][t][r];
-        if (n + 1 < nc) load_up(n + 1);
-
-        // ---- O = diag(Gamma) Q S_0 + P U
-        {
-            floatx4 pu[CGW][4];
-#pragma unroll
-            for (int c = 0; c < CGW; ++c)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) pu[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int r = 0; r < 4; ++r) u[t][r] = up[4 * t + r] - ws0[t][r];
+            if (n + 1 < nc) load_up(n + 1);
+            // ---- U to the output wave; S_S = e^{gamma_S} S_0 + K^T (decay U)
+            const float GS = sm.GS[b];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                bf16x8 bh[CGW], bl[CGW];
-#pragma unroll
-                for (int c = 0; c < CGW; ++c) acc_frag<false>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
-#pragma unroll
-                for (int t = 2 * s; t < 4; ++t) {
-                    const bf16x8 ah = frag_perm(&sm.P[b][(16 * t + lr) * L64 + 32 * s], lg);
-#pragma unroll
-                    for (int c = 0; c < CGW; ++c) pu[c][t] = mfma(ah, bh[c], pu[c][t]);
-                }
-            }
-            read_ahead<6, 1, CGW, 2>();
-            const auto orsrc = buffer_rsrc(o + (row0 + 64l * n) * (long)rowV + (long)h * DV + col0,
-                                          (uint32_t)S * rowV * 4);
-            uint32_t o_lane = (__umul24(lq, rowV) + CGW * lr) * 4;
-            asm volatile("" : "+v"(o_lane));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[b][16 * t + lq]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (CGW == 2) {
-                        const u32x2 pair = {__float_as_uint(fmaf(G4[r], qs0[0][t][r], pu[0][t][r])),
-                                            __float_as_uint(fmaf(G4[r], qs0[1][t][r], pu[1][t][r]))};
-                        __builtin_amdgcn_raw_buffer_store_b64(pair, orsrc, o_lane + (16 * t + r) * rowV * 4, 0, 0);
-                    } else {
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(G4[r], qs0[0][t][r], pu[0][t][r])),
-                                                              orsrc, o_lane + (16 * t + r) * rowV * 4, 0, 0);
-                    }
-                }
-            }
-        }
-
-        // ---- S_S = e^{gamma_S} S_0 + K^T (decay U)
-        {
-            const float GS = sm.Gam[b][S - 1];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sm.dec[b][16 * t + lq]);
-#pragma unroll
-                for (int c = 0; c < CGW; ++c) u[c][t] *= d4;
+                bf16x8 bh, bl;
+                acc_frag<false>(u[2 * s], u[2 * s + 1], bh, bl);
+                sm.xu[b][pair][s][lane] = bh;
             }
 #pragma unroll
-            for (int c = 0; c < CGW; ++c)
+            for (int t = 0; t < 4; ++t) u[t] *= *reinterpret_cast<const floatx4*>(&sm.dec[b][16 * t + lq]);
 #pragma unroll
-                for (int tr = 0; tr < RT; ++tr) sacc[c][tr] = sacc[c][tr] * GS;
+            for (int tr = 0; tr < RT; ++tr) sacc[tr] = sacc[tr] * GS;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                bf16x8 bh[CGW], bl[CGW];
+                bf16x8 bh, bl;
+                acc_frag<false>(u[2 * s], u[2 * s + 1], bh, bl);
 #pragma unroll
-                for (int c = 0; c < CGW; ++c) acc_frag<false>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
-#pragma unroll
-                for (int tr = 0; tr < RT; ++tr) {
-                    const bf16x8 a = frag_perm(&sm.KT[b][(16 * tr + lr) * L64 + 32 * s], lg);
-#pragma unroll
-                    for (int c = 0; c < CGW; ++c) sacc[c][tr] = mfma(a, bh[c], sacc[c][tr]);
-                }
+                for (int tr = 0; tr < RT; ++tr)
+                    sacc[tr] = mfma(frag_perm(&sm.KT[b][(16 * tr + lr) * L64 + 32 * s], lg), bh, sacc[tr]);
             }
-            read_ahead<2 * RT, 1, CGW, 2>();
+            read_ahead<2 * RT, 1, 1, 2>();
         }
-        __syncthreads();  // chunk n + 1 in LDS; buffer n & 1 free again
+        __syncthreads();
     }
     {
         int sl = s_lane * 4, dv4 = DV * 4;
@@ -570,14 +596,8 @@ __global__ __launch_bounds__(64 * (NSW + kCpLoaders), 1) void gdn_cp_state_kerne
 #pragma unroll
         for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (CGW == 2)
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        u32x2{__float_as_uint(sacc[0][tr][r]), __float_as_uint(sacc[1][tr][r])}, srs, sl,
-                        (16 * tr + r) * dv4, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sacc[0][tr][r]), srs, sl, (16 * tr + r) * dv4, 0);
-            }
+            for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sacc[tr][r]), srs, sl, (16 * tr + r) * dv4, 0);
     }
 }
 
@@ -599,31 +619,40 @@ hipError_t opt_in_lds(K kern, size_t bytes) {
                                (int)bytes);
 }
 
+template <int DK, int DV, int NSW>
+hipError_t launch_state(const void* q, float* o, float* state, const Batch& bt, const CpChunks& cm, int Hk, int Hv,
+                        void* ws, hipStream_t st) {
+    constexpr int NCW = DV / (16 * NSW);
+    auto stk = gdn_cp_state_kernel<DK, DV, NSW>;
+    static const hipError_t e = opt_in_lds(stk, sizeof(CpStateSmem<DK, NSW>));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(stk, dim3((unsigned)(Hv * NCW), (unsigned)bt.P), dim3(64 * (2 * NSW + kCpLoaders)),
+                       sizeof(CpStateSmem<DK, NSW>), st, static_cast<const uint16_t*>(q), o, state, bt, cm, Hk, Hv,
+                       static_cast<const unsigned char*>(ws));
+    return hipGetLastError();
+}
+
 template <int DK, int DV>
 hipError_t launch_cp(const void* q, const void* k, const void* v, const float* beta, const float* g, float* o,
                      float* state, const Batch& bt, int Hk, int Hv, void* ws, hipStream_t st) {
-    // state waves of 16 columns, two per workgroup: the chain of products per chunk is
-    // half as long as with 32-column waves, and dv / 32 workgroups share each head
-    constexpr int CGW = 1, NSW = 2;
-    constexpr int NCW = DV / (16 * CGW * NSW);
     const CpChunks cm = cp_chunks(bt);
     if (cm.total == 0) return hipSuccess;
     auto prep = gdn_cp_prep_kernel<DK, DV>;
-    auto stk = gdn_cp_state_kernel<DK, DV, NSW, CGW>;
     static const hipError_t e1 = opt_in_lds(prep, sizeof(CpPrepSmem<DK, DV>));
-    static const hipError_t e2 = opt_in_lds(stk, sizeof(CpStateSmem<DK>));
     if (e1 != hipSuccess) return e1;
-    if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL(prep, dim3((unsigned)cm.total, (unsigned)Hv), dim3(64 * kCpPrepWaves),
+    hipLaunchKernelGGL(prep, dim3((unsigned)((cm.total + 7) / 8 * 8), (unsigned)Hv), dim3(64 * kCpPrepWaves),
                        sizeof(CpPrepSmem<DK, DV>), st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, g, bt, cm, Hk, Hv,
                        static_cast<unsigned char*>(ws));
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(stk, dim3((unsigned)(Hv * NCW), (unsigned)bt.P), dim3(64 * (NSW + kCpLoaders)),
-                       sizeof(CpStateSmem<DK>), st, static_cast<const uint16_t*>(q), o, state, bt, cm, Hk, Hv,
-                       static_cast<const unsigned char*>(ws));
-    return hipGetLastError();
+    // A workgroup per 16 columns of a head when that fills no more than the compute units
+    // (fewer waves read the same fragments from one CU's LDS); per 32 columns otherwise.
+    int nonempty = 0;
+    for (int p = 0; p < bt.P; ++p) nonempty += batch_len(bt, p) > 0;
+    if ((long)nonempty * Hv * (DV / 16) <= compute_units())
+        return launch_state<DK, DV, 1>(q, o, state, bt, cm, Hk, Hv, ws, st);
+    return launch_state<DK, DV, 2>(q, o, state, bt, cm, Hk, Hv, ws, st);
 }
 
 template <int DK>

@@ -763,13 +763,6 @@ void plan_lanes(const Batch& bt, int k, Batch& out, GdnLanes& lanes) {
     lanes.off[k] = (unsigned short)s;
 }
 
-int compute_units() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return n;
-}
-
 // The lanes of a packed batch (n == 0: one prompt per workgroup row).  The
 // last plan is kept per host thread and reused for the same lengths.
 void lanes_for(const Batch& bt, int Hv, Batch& run, GdnLanes& lanes) {

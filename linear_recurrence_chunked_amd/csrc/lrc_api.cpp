@@ -17,6 +17,13 @@ namespace {
 __device__ unsigned g_wait_timeouts = 0;
 }  // namespace
 
+int compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
 unsigned* wait_timeouts_counter() {
     constexpr int kMaxDevices = 64;
     static std::mutex mu;

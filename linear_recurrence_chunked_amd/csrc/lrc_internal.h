@@ -31,6 +31,9 @@ __host__ __device__ inline int batch_len(const Batch& b, int p) {
     return b.uniform >= 0 ? b.uniform : b.row_off[p + 1] - b.row_off[p];
 }
 
+// Compute units of the current device (0 if the query fails).
+int compute_units();
+
 // Device counter (one per GPU, in the library) of bounded LDS waits that gave
 // up; the WKV kernels add to it.  nullptr if its address cannot be had.
 unsigned* wait_timeouts_counter();

@@ -140,3 +140,23 @@ def test_chunkpar_all_empty_and_rejects(L):
     with pytest.raises(L.LrcError) as ei:
         L.gdn_prefill_ws(q, q, v, b, b, o, st[:1], [70], small)
     assert ei.value.name == "LRC_ERR_SHAPE"
+
+
+def test_chunkpar_many_prompts_two_state_waves(L, orc):
+    """16 ragged prompts at the 9B-like head shape: more (prompt, head, 16-column) slices than compute
+    units, so the state kernel runs two state waves of 16 columns per workgroup."""
+    from linear_recurrence_chunked_amd import inputs
+
+    lens = [300, 0, 64, 65, 1, 257, 130, 190, 17, 128, 45, 99, 200, 33, 70, 150]
+    R, P, Hk, Hv, dk, dv = sum(lens), len(lens), 16, 32, 128, 128
+    assert P * Hv * (dv // 16) > torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(960)
+    q = rng.standard_normal((R, Hk, dk)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((R, Hk, dk)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    t = {"q": torch.from_numpy(q).to(torch.bfloat16), "k": torch.from_numpy(k).to(torch.bfloat16),
+         "v": torch.from_numpy(rng.standard_normal((R, Hv, dv))).to(torch.bfloat16),
+         "beta": torch.from_numpy(1 / (1 + np.exp(-rng.standard_normal((R, Hv))))).float(),
+         "g": torch.from_numpy(inputs.gdn_decays(rng, R, Hv)).float(),
+         "S0": torch.from_numpy(rng.normal(0, 0.1, (P, Hv, dk, dv))).float()}
+    o, s = _run(L, t, lens)
+    _check_prompts(orc, t, lens, o, s, heads=(0, 31))
