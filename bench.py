@@ -15,7 +15,12 @@ Prints ONE JSON line.  `value` is prompt rows per second through the whole
 step.  Per-kernel times come from HIP events on the stream the kernels run
 on; `roofline` covers the kernel with the largest share of the step.
 `cpu_baseline` times the float64 oracle (test infrastructure) on a bounded
-sample of the same workload on the host cores.
+sample of the same workload on the host cores, and on one core.
+`per_config` repeats the measurement for every kernel at each workload of the
+metric (Mamba tiny, RWKV-4 169M-like, DeltaNet small, DeltaNet 9B-like, and
+the mixed step itself): time, rows/s and roofline fraction on the GPU, and, in
+the oracle leg, max rel err of every output and state tensor against the
+float64 oracle run from the same incoming state, plus the oracle's own rows/s.
 """
 from __future__ import annotations
 
@@ -45,6 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="target seconds of oracle work")
     ap.add_argument("--only", default="", help="comma list of kernels to run (profiling aid)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table (cfg1..cfg4)")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="time only the step's own launches: no split-form or FP32-input DeltaNet legs, "
                          "no rows beyond the step (profiling aid)")
@@ -310,6 +316,321 @@ def cpu_baseline(W, lrc_outputs_fresh, budget_s):
     }, err
 
 
+def cpu_baseline_one_thread(W):
+    """The oracle on ONE host thread over a smaller strided sample of the same step (every prompt; one
+    in 16 conv and RWKV channels, one in 64 scan state elements, one key head of DeltaNet with its
+    value heads), each kernel's time scaled by its sampled fraction: whole-step rows/s on one core."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    from linear_recurrence_chunked_amd import inputs
+
+    sh = inputs.MIXED_SHAPES
+    lens, R = W["lens"], W["R"]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    Cm, Cg, Cr = sh["mamba_conv_c"], sh["gdn_conv_c"], sh["rwkv_c"]
+    E = sh["mamba_d_inner"] * sh["mamba_d_state"]
+    Hk, Hv = sh["gdn_hk"], sh["gdn_hv"]
+    grp = Hv // Hk
+    nthreads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    t = {}
+    try:
+        for name, xs, ws, units, stride in [("conv_mamba", "xm", "wm", Cm, 16), ("conv_gdn", "xg", "wg", Cg, 16)]:
+            c = torch.arange(0, units, stride, device=W[xs].device)
+            x, wt = f64(W[xs][:, c]), f64(W[ws][c])
+            t0 = time.perf_counter()
+            for p in range(len(lens)):
+                oracle.conv_rows(x[offs[p]:offs[p + 1]], np.zeros((3, len(c))), wt)
+            t[name] = (time.perf_counter() - t0) * units / len(c)
+        ci = torch.arange(0, E, 64, device=W["a"].device)
+        a, b = f64(W["a"].view(R, -1)[:, ci]), f64(W["b"].view(R, -1)[:, ci])
+        t0 = time.perf_counter()
+        for p in range(len(lens)):
+            oracle.scan(a[offs[p]:offs[p + 1]], b[offs[p]:offs[p + 1]], np.zeros(len(ci)))
+        t["scan"] = (time.perf_counter() - t0) * E / len(ci)
+        ci = torch.arange(0, Cr, 16, device=W["k"].device)
+        k, v, w, u = f64(W["k"][:, ci]), f64(W["v"][:, ci]), f64(W["w"][ci]), f64(W["u"][ci])
+        t0 = time.perf_counter()
+        for p in range(len(lens)):
+            oracle.wkv4(k[offs[p]:offs[p + 1]], v[offs[p]:offs[p + 1]], w, u, *oracle.empty_wkv_state(len(ci)))
+        t["wkv4"] = (time.perf_counter() - t0) * Cr / len(ci)
+        q, kk = f64(W["q"][:, :1]), f64(W["gk"][:, :1])
+        vv, be, gg = f64(W["gv"][:, :grp]), f64(W["beta"][:, :grp]), f64(W["g"][:, :grp])
+        dk, dv = q.shape[2], vv.shape[2]
+        t0 = time.perf_counter()
+        for p in range(len(lens)):
+            sl = slice(offs[p], offs[p + 1])
+            oracle.gdn(q[sl], kk[sl], vv[sl], be[sl], gg[sl], np.zeros((grp, dk, dv)))
+        t["gdn"] = (time.perf_counter() - t0) * Hk
+    finally:
+        oracle.set_num_threads(nthreads)
+    total = sum(t.values())
+    return {"value": R / total, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {len(lens)} prompts; one in 16 conv and RWKV channels, one in 64 scan state elements, "
+                      f"one DeltaNet key head with its {grp} value heads; each kernel's time scaled by its sampled "
+                      f"fraction",
+            "per_kernel_s": {n: round(x, 3) for n, x in t.items()}}
+
+
+# ----------------------------------------------------------------------------- per-config measurement
+def gdn_chunk_flops(lens, Hk, Hv, dk, dv):
+    """Dense-contraction flops of the chunk form over prompts of the given lengths (see algorithmic_work)."""
+    grp = Hv // Hk
+    inv = 8 * 4 * 2 * 8 ** 3 + sum((64 // (2 * s)) * 2 * 2 * s ** 3 for s in (8, 16, 32))
+    fl = 0
+    for L in lens:
+        for c0 in range(0, L, 64):
+            r = min(64, L - c0)
+            fl += ((2 * 2 * r * r * dk) / grp + 3 * 2 * r * dk * dv + 2 * 2 * r * r * dv + inv) * Hv
+    return fl
+
+
+def _time_ms(fn, stream, reps):
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _entry(ms, rows, bound, work, peak):
+    """rows/s and the roofline fraction of one launch (work in bytes for hbm, flops for mfma)."""
+    rate = work / (ms * 1e-3)
+    d = {"ms": round(ms, 5), "rows_per_s": rows / (ms * 1e-3), "bound": bound}
+    if bound == "hbm":
+        d.update({"GBps": rate / 1e9, "peak_GBps": peak, "frac": rate / 1e9 / peak, "algorithmic_bytes": work})
+    else:
+        d.update({"TFLOPs": rate / 1e12, "peak_TFLOPs": peak, "frac": rate / 1e12 / peak, "algorithmic_flops": work})
+    return d
+
+
+CONFIG_NAMES = {
+    "cfg1_mamba_tiny": "Mamba tiny: d_inner 64, d_state 16, one 75-row prompt (64 + 11), fp32; conv K=4 over 64 channels",
+    "cfg2_rwkv4_169m": "RWKV-4 169M-like: 768 x 12 = 9216 channels, one 128-row prompt (2 x 64), fp32, from a 32-step warm state",
+    "cfg3_gdn_small": "Gated DeltaNet small: 8 heads, dk = dv = 64, one 75-row prompt (64 + 11); fp32, bf16, and bf16 with 16 "
+                      "nearly parallel keys and beta = 0.99",
+    "cfg4_gdn_9b": "Gated DeltaNet 9B-like: 32 value heads on 16 key heads, dk = dv = 128, one 2048-row prompt (32 x 64), "
+                   "bf16 q/k/v, fp32 state and decays, g from -1e-3 to -8 per row; conv K=4 over 8192 bf16 channels",
+    "cfg5_mixed": "batched mixed prefill (the step): 16 prompts of U{1..4096} rows through every kernel",
+}
+
+
+def measure_configs(lrc, dev, stream):
+    """GPU times of every kernel at the four single-prompt configs (HIP events on the launch stream).
+    Returns the per-config entries and the inputs, for the oracle leg."""
+    import torch
+
+    from linear_recurrence_chunked_amd import inputs
+
+    out, keep = {}, {}
+    g = lambda t: t.to(dev).contiguous()  # noqa: E731
+    # --- cfg1: Mamba tiny, conv + tiled scan
+    d = inputs.mamba_tiny()
+    R, C, K = d["conv_x"].shape[0], d["conv_x"].shape[1], d["conv_w"].shape[1]
+    E = d["a"].shape[1]
+    x, w, st0 = g(d["conv_x"]), g(d["conv_w"]), g(d["conv_state"])[None]
+    y, st = torch.empty_like(x), st0.clone()
+    a, b = g(d["a"]).view(R, 64, 16), g(d["b"]).view(R, 64, 16)
+    h, hs0 = torch.empty_like(a), g(d["h0"]).view(1, 64, 16)
+    hs = hs0.clone()
+    ws = lrc.scan_workspace(1, 64, 16, dev)
+    k1 = {
+        "conv": _entry(_time_ms(lambda: lrc.conv_prefill(x, y, st, w, [R]), stream, 200), R, "hbm",
+                       R * C * 8 + 2 * (K - 1) * C * 4 + C * K * 4, HBM_PEAK_GBS),
+        "scan": _entry(_time_ms(lambda: lrc.scan_prefill_ws(a, b, h, hs, [R], ws), stream, 200), R, "hbm",
+                       R * E * 12 + E * 8, HBM_PEAK_GBS),
+    }
+    out["cfg1_mamba_tiny"] = {"workload": CONFIG_NAMES["cfg1_mamba_tiny"], "rows": R, "kernels": k1}
+    keep["cfg1"] = d
+    # --- cfg2: RWKV-4 169M-like
+    r = inputs.rwkv_169m()
+    R, C = r["k"].shape
+    k_, v_, w_, u_ = (g(r[n]) for n in ("k", "v", "w", "u"))
+    o2 = torch.empty_like(k_)
+    num, den = torch.zeros((1, C), device=dev), torch.zeros((1, C), device=dev)
+    mx = torch.full((1, C), -1e38, device=dev)
+    k2 = {"wkv4": _entry(_time_ms(lambda: lrc.wkv4_prefill(k_, v_, w_, u_, o2, num, den, mx, [R]), stream, 100),
+                         R, "hbm", R * C * 12 + C * 24 + C * 8, HBM_PEAK_GBS)}
+    out["cfg2_rwkv4_169m"] = {"workload": CONFIG_NAMES["cfg2_rwkv4_169m"], "rows": R, "kernels": k2}
+    keep["cfg2"] = r
+    # --- cfg3: Gated DeltaNet small (fused kernel; fp32 inputs, bf16, bf16 stress; chunk-parallel bf16)
+    k3 = {}
+    keep["cfg3"] = {}
+    for name, dd in [("gdn_f32", inputs.gdn_small(dtype=torch.float32)),
+                     ("gdn_bf16", inputs.gdn_small(dtype=torch.bfloat16)),
+                     ("gdn_bf16_16_parallel_keys",
+                      inputs.gdn_small(dtype=torch.bfloat16, parallel_keys=16, parallel_start=24, beta_const=0.99)),
+                     ("gdn_bf16_chunk_parallel", inputs.gdn_small(dtype=torch.bfloat16))]:
+        q, kk, vv, be, gg = (g(dd[n]) for n in ("q", "k", "v", "beta", "g"))
+        S = g(dd["S0"])[None].clone()
+        R, Hk, dk = q.shape
+        Hv, dv = vv.shape[1], vv.shape[2]
+        o = torch.empty((R, Hv, dv), device=dev)
+        if name.endswith("chunk_parallel"):
+            wsg = lrc.gdn_workspace(1, R, Hk, Hv, dk, dv, dev)
+            fn = lambda: lrc.gdn_prefill_ws(q, kk, vv, be, gg, o, S, [R], wsg)  # noqa: E731
+        else:
+            fn = lambda: lrc.gdn_prefill(q, kk, vv, be, gg, o, S, [R])  # noqa: E731
+        peak = MFMA_FP32_PEAK_TFS if q.dtype == torch.float32 else MFMA_BF16_PEAK_TFS
+        k3[name] = _entry(_time_ms(fn, stream, 100), R, "mfma", gdn_chunk_flops([R], Hk, Hv, dk, dv), peak)
+        keep["cfg3"][name] = dd
+    out["cfg3_gdn_small"] = {"workload": CONFIG_NAMES["cfg3_gdn_small"], "rows": 75, "kernels": k3}
+    # --- cfg4: Gated DeltaNet 9B-like: conv + chunk-parallel form (this config's path), fused and fp32 alongside
+    d4 = inputs.gdn_9b()
+    R, Hk, dk = d4["q"].shape
+    Hv, dv = d4["v"].shape[1], d4["v"].shape[2]
+    cx, cw = g(d4["conv_x"]), g(d4["conv_w"])
+    C, K = cx.shape[1], cw.shape[1]
+    cy, cst = torch.empty_like(cx), g(d4["conv_state"])[None].clone()
+    k4 = {"conv_bf16": _entry(_time_ms(lambda: lrc.conv_prefill(cx, cy, cst, cw, [R]), stream, 50), R, "hbm",
+                              R * C * 4 + 2 * (K - 1) * C * 2 + C * K * 4, HBM_PEAK_GBS)}
+    q, kk, vv, be, gg = (g(d4[n]) for n in ("q", "k", "v", "beta", "g"))
+    S = g(d4["S0"])[None].clone()
+    o = torch.empty((R, Hv, dv), device=dev)
+    wsg = lrc.gdn_workspace(1, R, Hk, Hv, dk, dv, dev)
+    fl = gdn_chunk_flops([R], Hk, Hv, dk, dv)
+    k4["gdn_bf16_chunk_parallel"] = _entry(
+        _time_ms(lambda: lrc.gdn_prefill_ws(q, kk, vv, be, gg, o, S, [R], wsg), stream, 20), R, "mfma", fl,
+        MFMA_BF16_PEAK_TFS)
+    k4["gdn_bf16_fused"] = _entry(_time_ms(lambda: lrc.gdn_prefill(q, kk, vv, be, gg, o, S, [R]), stream, 20), R,
+                                  "mfma", fl, MFMA_BF16_PEAK_TFS)
+    q32, k32, v32 = q.float(), kk.float(), vv.float()
+    k4["gdn_f32"] = _entry(_time_ms(lambda: lrc.gdn_prefill(q32, k32, v32, be, gg, o, S, [R]), stream, 10), R,
+                           "mfma", fl, MFMA_FP32_PEAK_TFS)
+    del q32, k32, v32, wsg
+    out["cfg4_gdn_9b"] = {"workload": CONFIG_NAMES["cfg4_gdn_9b"], "rows": R, "kernels": k4,
+                          "gdn_path": "gdn_bf16_chunk_parallel"}
+    keep["cfg4"] = d4
+    return out, keep
+
+
+def config_errors(lrc, dev, keep, per_config):
+    """Oracle leg of the per-config table: each config runs once more on the GPU from the same
+    incoming state as the float64 oracle, and every output and state tensor gets its max rel err.
+    Also times the oracle on each config, at the default thread count and on one thread."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    g = lambda t: t.to(dev).contiguous()  # noqa: E731
+
+    def rel(got, ref):
+        sc = float(np.max(np.abs(ref)))
+        return float(np.max(np.abs(got - ref))) / (sc if sc else 1.0)
+
+    nthreads = oracle.num_threads()
+
+    def timed(fn):
+        t0 = time.perf_counter(); res = fn(); t = time.perf_counter() - t0
+        oracle.set_num_threads(1)
+        t1 = time.perf_counter(); fn(); t1 = time.perf_counter() - t1
+        oracle.set_num_threads(nthreads)
+        return res, t, t1
+
+    def put(cfg, kern, errs, tol):
+        e = per_config[cfg]["kernels"][kern]
+        e["max_rel_err"] = {n: v for n, v in errs.items()}
+        e["tol"] = tol
+        e["within_tol"] = bool(all(v <= tol for v in errs.values()) and all(np.isfinite(list(errs.values()))))
+
+    orc = {}
+    # cfg1
+    d = keep["cfg1"]
+    R = d["conv_x"].shape[0]
+    (ry, rs), tc, tc1 = timed(lambda: oracle.conv_rows(f64(d["conv_x"]), f64(d["conv_state"]), f64(d["conv_w"])))
+    x, w = g(d["conv_x"]), g(d["conv_w"])
+    y, st = torch.empty_like(x), g(d["conv_state"])[None].clone()
+    lrc.conv_prefill(x, y, st, w, [R])
+    (rh, rhs), ts, ts1 = timed(lambda: oracle.scan(f64(d["a"]), f64(d["b"]), f64(d["h0"])))
+    a, b = g(d["a"]).view(R, 64, 16), g(d["b"]).view(R, 64, 16)
+    h, hs = torch.empty_like(a), g(d["h0"]).view(1, 64, 16).clone()
+    lrc.scan_prefill_ws(a, b, h, hs, [R], lrc.scan_workspace(1, 64, 16, dev))
+    torch.cuda.synchronize()
+    put("cfg1_mamba_tiny", "conv", {"y": rel(f64(y), ry), "state": rel(f64(st[0]), rs)}, 1e-4)
+    put("cfg1_mamba_tiny", "scan", {"h": rel(f64(h).reshape(R, -1), rh), "state": rel(f64(hs).reshape(-1), rhs)}, 1e-4)
+    orc["cfg1_mamba_tiny"] = (R, tc + ts, tc1 + ts1)
+    # cfg2: the incoming state is the oracle's, after 32 warm-up token steps from the empty state
+    r = keep["cfg2"]
+    R, C = r["k"].shape
+    _, wn, wd, wm = oracle.wkv4(f64(r["warm_k"]), f64(r["warm_v"]), f64(r["w"]), f64(r["u"]), *oracle.empty_wkv_state(C))
+    n32, d32, m32 = (torch.from_numpy(z).float() for z in (wn, wd, wm))
+    (ro, rn, rd, rm), tw, tw1 = timed(lambda: oracle.wkv4(f64(r["k"]), f64(r["v"]), f64(r["w"]), f64(r["u"]),
+                                                        f64(n32), f64(d32), f64(m32)))
+    k_, v_, w_, u_ = (g(r[n]) for n in ("k", "v", "w", "u"))
+    o2 = torch.empty_like(k_)
+    num, den, mx = g(n32)[None].clone(), g(d32)[None].clone(), g(m32)[None].clone()
+    lrc.wkv4_prefill(k_, v_, w_, u_, o2, num, den, mx, [R])
+    torch.cuda.synchronize()
+    gm = f64(mx[0])
+    put("cfg2_rwkv4_169m", "wkv4", {"wkv": rel(f64(o2), ro), "num/den": rel(f64(num[0]) / f64(den[0]), rn / rd),
+                                    "num*e^(max-M)": rel(f64(num[0]) * np.exp(gm - rm), rn),
+                                    "den*e^(max-M)": rel(f64(den[0]) * np.exp(gm - rm), rd)}, 1e-4)
+    orc["cfg2_rwkv4_169m"] = (R, tw, tw1)
+    # cfg3 and cfg4 Gated DeltaNet
+    def gdn_case(cfg, kern, dd, tol, chunk_parallel):
+        q, kk, vv, be, gg = (g(dd[n]) for n in ("q", "k", "v", "beta", "g"))
+        S = g(dd["S0"])[None].clone()
+        R, Hk, dk = q.shape
+        Hv, dv = vv.shape[1], vv.shape[2]
+        o = torch.empty((R, Hv, dv), device=dev)
+        if chunk_parallel:
+            lrc.gdn_prefill_ws(q, kk, vv, be, gg, o, S, [R], lrc.gdn_workspace(1, R, Hk, Hv, dk, dv, dev))
+        else:
+            lrc.gdn_prefill(q, kk, vv, be, gg, o, S, [R])
+        torch.cuda.synchronize()
+        return o, S
+
+    ttot = [0.0, 0.0]
+    for kern, dd in keep["cfg3"].items():
+        (ro, rs), t, t1 = timed(lambda: oracle.gdn(*(f64(dd[n]) for n in ("q", "k", "v", "beta", "g", "S0"))))
+        ttot[0] += t; ttot[1] += t1
+        o, S = gdn_case("cfg3_gdn_small", kern, dd, None, kern.endswith("chunk_parallel"))
+        tol = 1e-4 if dd["q"].dtype == torch.float32 else 2e-2
+        put("cfg3_gdn_small", kern, {"o": rel(f64(o), ro), "state": rel(f64(S[0]), rs)}, tol)
+    orc["cfg3_gdn_small"] = (75, ttot[0] / len(keep["cfg3"]), ttot[1] / len(keep["cfg3"]))
+    d4 = keep["cfg4"]
+    args = [f64(d4[n]) for n in ("q", "k", "v", "beta", "g", "S0")]
+    t0 = time.perf_counter(); ro, rs = oracle.gdn(*args); t4 = time.perf_counter() - t0
+    # one thread on 4 of the 32 value heads (2 key heads), scaled to all heads
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter(); oracle.gdn(args[0][:, :2], args[1][:, :2], args[2][:, :4], args[3][:, :4], args[4][:, :4],
+                                         args[5][:4]); t41 = (time.perf_counter() - t0) * 8
+    oracle.set_num_threads(nthreads)
+    R = args[0].shape[0]
+    for kern, cp in [("gdn_bf16_chunk_parallel", True), ("gdn_bf16_fused", False)]:
+        o, S = gdn_case("cfg4_gdn_9b", kern, d4, None, cp)
+        put("cfg4_gdn_9b", kern, {"o": rel(f64(o), ro), "state": rel(f64(S[0]), rs),
+                                  "o_head31_g=-8": rel(f64(o[:, 31]), ro[:, 31]),
+                                  "state_head31_g=-8": rel(f64(S[0, 31]), rs[31])}, 2e-2)
+    d32 = dict(d4)
+    for n in ("q", "k", "v"):
+        d32[n] = d4[n].float()
+    o, S = gdn_case("cfg4_gdn_9b", "gdn_f32", d32, None, False)
+    put("cfg4_gdn_9b", "gdn_f32", {"o": rel(f64(o), ro), "state": rel(f64(S[0]), rs)}, 1e-4)
+    cx, cw = d4["conv_x"], d4["conv_w"]
+    (ry, rst), tcv, tcv1 = timed(lambda: oracle.conv_rows(f64(cx), f64(d4["conv_state"]), f64(cw)))
+    x, w = g(cx), g(cw)
+    y, st = torch.empty_like(x), g(d4["conv_state"])[None].clone()
+    lrc.conv_prefill(x, y, st, w, [R])
+    torch.cuda.synchronize()
+    put("cfg4_gdn_9b", "conv_bf16", {"y": rel(f64(y), ry), "state": rel(f64(st[0]), rst)}, 2e-2)
+    orc["cfg4_gdn_9b"] = (R, t4 + tcv, t41 + tcv1)
+    for cfg, (rows, t, t1) in orc.items():
+        per_config[cfg]["oracle"] = {"rows_per_s": rows / t, "cores": nthreads, "rows_per_s_1_thread": rows / t1}
+
+
 # ALU peak for the fused mixer rows: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz issue 39.3 T lane-slots/s;
 # one (t, d, n) step costs 4 full-rate VALU slots (dt*A', dt x * B, the state FMA, the readout FMA) plus one
 # exp at a quarter of that rate (4 slots), so 8 slots per step.
@@ -538,12 +859,29 @@ def main():
         # rows beyond the step (not in `value`): the RWKV-4 time shift and the fused Mamba mixer rows
         "next_rows": nxt,
     }
+    per_config = None
+    if not args.only and not args.no_configs:
+        per_config, keep = measure_configs(lrc, dev, stream)
+        per_config["cfg5_mixed"] = {"workload": CONFIG_NAMES["cfg5_mixed"], "rows": R, "kernels": {
+            k: {"ms": kern[k]["ms"], "rows_per_s": kern[k]["rows_per_s"],
+                **({"bound": "mfma", "TFLOPs": kern[k]["TFLOPs"], "peak_TFLOPs": MFMA_BF16_PEAK_TFS,
+                    "frac": kern[k]["mfma_bf16_frac"]} if k == "gdn" else
+                   {"bound": "hbm", "GBps": kern[k]["GBps"], "peak_GBps": HBM_PEAK_GBS, "frac": kern[k]["hbm_frac"]})}
+            for k in kernels}}
     if not args.no_cpu_baseline and set(kernels) == set(KERNELS):
         cb, err = cpu_baseline(W, fresh, args.cpu_budget)
+        cb["one_thread"] = cpu_baseline_one_thread(W)
         out["cpu_baseline"] = cb
         out["max_rel_err_sample"] = err
+        if per_config:
+            config_errors(lrc, dev, keep, per_config)
+            for k, e in err.items():
+                per_config["cfg5_mixed"]["kernels"][k]["max_rel_err_sampled"] = e
+            per_config["cfg5_mixed"]["oracle"] = {"rows_per_s": cb["value"], "cores": cb["cores"],
+                                                  "rows_per_s_1_thread": cb["one_thread"]["value"]}
     else:
         out["cpu_baseline"] = None
+    out["per_config"] = per_config
     print(json.dumps(out), flush=True)
 
 
