@@ -44,7 +44,10 @@ constexpr int kCpPrepWaves = 4;
 constexpr int kCpLoaders = 2;  // loader waves of the state kernel
 
 // One (chunk, value head) block of the workspace: W [64][DK] bf16, K^T [DK][64]
-// bf16, P [64][64] bf16, U' [64][DV] f32, Gamma [64] f32, decay [64] f32.
+// bf16, P [64][64] bf16, U' [64][DV] f32, Gamma [64] f32, decay [64] f32.  The
+// rows of W, K^T and P are stored k-permuted along their contraction index
+// (kperm), so that the state kernel reads each operand fragment as one
+// 16-byte run.
 template <int DK, int DV>
 struct CpBlock {
     static constexpr size_t W = 0;
@@ -84,6 +87,7 @@ struct CpPrepSmem {
 
 // Rows r = 0 .. 63 of a [64][D] bf16 tile in LDS (row stride ld) into its
 // transpose [D][L64]: blocks of 4 rows x 8 columns, by byte permutes.
+// The destination's columns (rows of the source) are stored k-permuted (kperm).
 __device__ __forceinline__ void transpose64(const __bf16* src, int ld, __bf16* dst, int D, int t0, int nt) {
     for (int b = t0; b < 2 * D; b += nt) {
         const int nn = b & 15, m = b >> 4;  // rows 4nn .. 4nn+3, columns 8m .. 8m+7
@@ -100,7 +104,7 @@ __device__ __forceinline__ void transpose64(const __bf16* src, int ld, __bf16* d
             uint2 out;
             out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
             out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
-            *reinterpret_cast<uint2*>(&dst[(8 * m + e) * L64 + 4 * nn]) = out;
+            *reinterpret_cast<uint2*>(&dst[(8 * m + e) * L64 + kperm(4 * nn)]) = out;
         }
     }
 }
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(64 * kCpPrepWaves, 2) void gdn_cp_prep_kernel(
             const int e = tid + x * NT, r = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
             const bf16x8 vv = __builtin_bit_cast(bf16x8, va[x]);
 #pragma unroll
-            for (int z = 0; z < 8; ++z) sm.VT[(c8 + z) * L64 + r] = vv[z];
+            for (int z = 0; z < 8; ++z) sm.VT[(c8 + z) * L64 + kperm(r)] = vv[z];
         }
         if (w == kCpPrepWaves - 1) {
             const auto grs = buffer_rsrc(g + r0 * Hv + h, (uint32_t)S * Hv * 4);
@@ -243,13 +247,13 @@ __global__ __launch_bounds__(64 * kCpPrepWaves, 2) void gdn_cp_prep_kernel(
                 bf16x4 ph;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ph[r] = static_cast<__bf16>(pv[r]);
-                *reinterpret_cast<bf16x4*>(&P[i * 64 + 16 * tj + lq]) = ph;
+                *reinterpret_cast<bf16x4*>(&P[i * 64 + kperm(16 * tj + lq)]) = ph;
             }
-        // the 6 tiles of P above the diagonal: zeros, 16 rows x 32 bytes each
-        for (int e = tid; e < 6 * 16 * 2; e += NT) {
-            const int t = e >> 5, r = (e >> 1) & 15, half = e & 1;
+        // the 6 tiles of P above the diagonal: zeros, 16 rows x 4 runs of 4 keys each
+        for (int e = tid; e < 6 * 16 * 4; e += NT) {
+            const int t = e >> 6, r = (e >> 2) & 15, run = e & 3;
             const int ti = t < 3 ? 0 : (t < 5 ? 1 : 2), tj = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
-            *reinterpret_cast<uint4*>(&P[(16 * ti + r) * 64 + 16 * tj + 8 * half]) = make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint2*>(&P[(16 * ti + r) * 64 + kperm(16 * tj + 4 * run)]) = make_uint2(0u, 0u);
         }
         transpose64(sm.K(), LDK, sm.KT, DK, tid, NT);
     }
@@ -280,8 +284,8 @@ __global__ __launch_bounds__(64 * kCpPrepWaves, 2) void gdn_cp_prep_kernel(
                 tb[r] = static_cast<__bf16>(t4[r] * b4[r]);
                 tg[r] = static_cast<__bf16>(t4[r] * (b4[r] * G4[r]));
             }
-            *reinterpret_cast<bf16x4*>(&sm.Tg()[i * L64 + cc]) = tg;
-            *reinterpret_cast<bf16x4*>(&sm.Tb()[i * L64 + cc]) = tb;
+            *reinterpret_cast<bf16x4*>(&sm.Tg()[i * L64 + kperm(cc)]) = tg;
+            *reinterpret_cast<bf16x4*>(&sm.Tb()[i * L64 + kperm(cc)]) = tb;
         }
         __bf16* KT = reinterpret_cast<__bf16*>(blk + Blk::KT);
         for (int e = tid; e < DK * 8; e += NT) {
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(64 * kCpPrepWaves, 2) void gdn_cp_prep_kernel(
             bf16x4 wv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) wv[r] = static_cast<__bf16>(acc[r]);
-            *reinterpret_cast<bf16x4*>(&W[(16 * ti + lr) * DK + 16 * td + lq]) = wv;
+            *reinterpret_cast<bf16x4*>(&W[(16 * ti + lr) * DK + kperm(16 * td + lq)]) = wv;
         }
         for (int tile = w; tile < (DV / 16) * 4; tile += kCpPrepWaves) {
             const int tc = tile >> 2, ti = tile & 3;
@@ -434,7 +438,8 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
 #pragma unroll
             for (int x = 0; x < NP8; ++x) {
                 const int e = lt + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-                *reinterpret_cast<u32x4*>(&sm.Q[b][r * LDK + c8]) = rq[x];
+                *reinterpret_cast<u32x2*>(&sm.Q[b][r * LDK + kperm(c8)]) = u32x2{rq[x][0], rq[x][1]};
+                *reinterpret_cast<u32x2*>(&sm.Q[b][r * LDK + kperm(c8 + 4)]) = u32x2{rq[x][2], rq[x][3]};
             }
 #pragma unroll
             for (int x = 0; x < 512 / NT; ++x) {
@@ -486,14 +491,14 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                     const bf16x8 bs = sm.xs[b][pair][s][lane];
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        qs0[t] = mfma(frag_perm(&sm.Q[b][(16 * t + lr) * LDK + 32 * s], lg), bs, qs0[t]);
+                        qs0[t] = mfma(frag(&sm.Q[b][(16 * t + lr) * LDK + 32 * s + 8 * lg]), bs, qs0[t]);
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const bf16x8 bu = sm.xu[b][pair][s][lane];
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t)
-                        pu[t] = mfma(frag_perm(&sm.P[b][(16 * t + lr) * L64 + 32 * s], lg), bu, pu[t]);
+                        pu[t] = mfma(frag(&sm.P[b][(16 * t + lr) * L64 + 32 * s + 8 * lg]), bu, pu[t]);
                 }
                 const auto orsrc = buffer_rsrc(o + (row0 + 64l * m) * (long)rowV + (long)h * DV + col0,
                                               (uint32_t)S * rowV * 4);
@@ -557,7 +562,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 sm.xs[b][pair][s][lane] = bh;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    ws0[t] = mfma(frag_perm(&sm.W[b][(16 * t + lr) * LDK + 32 * s], lg), bh, ws0[t]);
+                    ws0[t] = mfma(frag(&sm.W[b][(16 * t + lr) * LDK + 32 * s + 8 * lg]), bh, ws0[t]);
             }
             read_ahead<4 * KS, 1, 1, 2>();
             // ---- U = U' - W S_0 (zero past the chunk: W and U' rows are zero there)
@@ -584,7 +589,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 acc_frag<false>(u[2 * s], u[2 * s + 1], bh, bl);
 #pragma unroll
                 for (int tr = 0; tr < RT; ++tr)
-                    sacc[tr] = mfma(frag_perm(&sm.KT[b][(16 * tr + lr) * L64 + 32 * s], lg), bh, sacc[tr]);
+                    sacc[tr] = mfma(frag(&sm.KT[b][(16 * tr + lr) * L64 + 32 * s + 8 * lg]), bh, sacc[tr]);
             }
             read_ahead<2 * RT, 1, 1, 2>();
         }

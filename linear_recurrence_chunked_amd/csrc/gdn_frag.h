@@ -33,6 +33,21 @@ __device__ __forceinline__ bf16x8 frag_perm(const __bf16* row_ks, int g) {
     const bf16x4 b = *reinterpret_cast<const bf16x4*>(row_ks + 16 + 4 * g);
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+// A k-permuted layout of a row: within each block of 32 k-values, positions
+// 8g .. 8g+3 hold k = 4g .. 4g+3 and positions 8g+4 .. 8g+7 hold
+// k = 16+4g .. 16+4g+3 (g = 0 .. 3).  Rows stored this way give the frag_perm
+// operand of lane group g as one contiguous 16-byte read at position 8g
+// (a single ds_read_b128 instead of two 8-byte reads 32 bytes apart).  A run of
+// 4 k-values starting at a multiple of 4 stays contiguous.  Products whose two
+// operands are both stored this way (K K^T, Q K^T) are unchanged by it.
+__device__ __forceinline__ int kperm(int k) {
+    const int x = k & 31;
+    return (k & ~31) + ((x & 15) >> 2) * 8 + (x >> 4) * 4 + (x & 3);
+}
+__device__ __forceinline__ int kperm_inv(int pos) {
+    const int x = pos & 31;
+    return (pos & ~31) + ((x >> 2) & 1) * 16 + (x >> 3) * 4 + (x & 3);
+}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Two FP32 values as packed bf16 hi = bf16(x) and lo = bf16(x - hi) (round to
 // nearest even both times): one conversion for each pair, the hi parts
