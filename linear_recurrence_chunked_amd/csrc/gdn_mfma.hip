@@ -40,8 +40,10 @@
 // same 8 k-values, and the accumulator holds column l%16, rows 4(l/16) .. +3.
 // A wave's own [rows x 16] accumulators serve directly as B operands when
 // the k-values of lane group g are taken as rows {4g .. 4g+3} of one 16-row
-// tile and {16+4g .. 16+4g+3} of the next; the A operand then reads the same
-// two 4-element runs of its row from LDS.  The masked products are computed
+// tile and {16+4g .. 16+4g+3} of the next; the A operands (K, Q, K^T, T, P)
+// are stored in LDS with their contraction index permuted to match (kperm),
+// so each A fragment is one 16-byte read.  K K^T and Q K^T take both operands
+// from the same permuted rows, which leaves their sums unchanged.  The masked products are computed
 // transposed (keys as rows), so each lane holds 4 consecutive keys of one
 // query and writes them as one packed store.
 // Accumulation is FP32 throughout.  An FP32 operand (S_0, the right-hand
@@ -146,8 +148,8 @@ __device__ __forceinline__ void split_tile(const float* M, __bf16* hi, __bf16* l
     const floatx4 x = *reinterpret_cast<const floatx4*>(&M[r * kTriLd + c]);
     bf16x4 h, l;
     split4(x, h, l);
-    *reinterpret_cast<bf16x4*>(&hi[r * L64 + c]) = h;
-    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&lo[r * L64 + c]) = l;
+    *reinterpret_cast<bf16x4*>(&hi[r * L64 + kperm(c)]) = h;
+    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&lo[r * L64 + kperm(c)]) = l;
 }
 
 // Masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M: tile
@@ -307,8 +309,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(sacc[c][2 * s], sacc[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const bf16x8 ak = frag_perm(&sm.K[cb][(16 * t + lr) * LDK + 32 * s], lg);
-                        const bf16x8 aq = frag_perm(&sm.Q[cb][(16 * t + lr) * LDK + 32 * s], lg);
+                        const bf16x8 ak = frag(&sm.K[cb][(16 * t + lr) * LDK + 32 * s + 8 * lg]);
+                        const bf16x8 aq = frag(&sm.Q[cb][(16 * t + lr) * LDK + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             ks0[c][t] = mfma(ak, bh[c], ks0[c][t]);
@@ -349,9 +351,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(ks0[c][2 * s], ks0[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
-                        const bf16x8 ah = frag_perm(&sm.T_hi[(16 * t + lr) * L64 + 32 * s], lg);
+                        const bf16x8 ah = frag(&sm.T_hi[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
                         bf16x8 al;
-                        if constexpr (SPLIT) al = frag_perm(&sm.T_lo[(16 * t + lr) * L64 + 32 * s], lg);
+                        if constexpr (SPLIT) al = frag(&sm.T_lo[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             u[c][t] = mfma(ah, bh[c], u[c][t]);
@@ -380,9 +382,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
-                        const bf16x8 ah = frag_perm(&sm.P_hi[(16 * t + lr) * L64 + 32 * s], lg);
+                        const bf16x8 ah = frag(&sm.P_hi[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
                         bf16x8 al;
-                        if constexpr (SPLIT) al = frag_perm(&sm.P_lo[(16 * t + lr) * L64 + 32 * s], lg);
+                        if constexpr (SPLIT) al = frag(&sm.P_lo[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             pu[c][t] = mfma(ah, bh[c], pu[c][t]);
@@ -434,7 +436,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int tr = 0; tr < RT; ++tr) {
-                        const bf16x8 a = frag_perm(&sm.KT[(16 * tr + lr) * L64 + 32 * s], lg);
+                        const bf16x8 a = frag(&sm.KT[(16 * tr + lr) * L64 + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             sacc[c][tr] = mfma(a, bh[c], sacc[c][tr]);
@@ -472,7 +474,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (n + 2 < nc && w < 2) masked_kk<DK, (NS == 1 ? 2 : 1)>(sm, cb, (n + 5) % 3, 8 + w, NS);
             if (do_next) {
                 for (int b = tid; b < 2 * DK; b += 64 * NS) {
-                    const int nn = b & 15, m = b >> 4;  // rows 4nn .. 4nn+3, columns 8m .. 8m+7
+                    // rows 4nn .. 4nn+3, stored columns 8m .. 8m+7 (dk indices kperm_inv of them)
+                    const int nn = b & 15, m = b >> 4;
                     uint4 rw[4];
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
@@ -487,7 +490,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                         uint2 out;
                         out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
                         out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
-                        *reinterpret_cast<uint2*>(&sm.KT[(8 * m + e) * L64 + 4 * nn]) = out;
+                        *reinterpret_cast<uint2*>(&sm.KT[kperm_inv(8 * m + e) * L64 + kperm(4 * nn)]) = out;
                     }
                 }
             }
@@ -549,7 +552,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 const int e = pt + x * PT;
                 const bool isq = x * PT >= PK;
                 const int ee = isq ? e - PK : e, r = ee / (DK / 8), c8 = (ee % (DK / 8)) * 8;
-                *reinterpret_cast<uint4*>(&(isq ? sm.Q[b] : sm.K[b])[r * LDK + c8]) = pf[x];
+                __bf16* row = &(isq ? sm.Q[b] : sm.K[b])[r * LDK];
+                *reinterpret_cast<uint2*>(&row[kperm(c8)]) = make_uint2(pf[x].x, pf[x].y);
+                *reinterpret_cast<uint2*>(&row[kperm(c8 + 4)]) = make_uint2(pf[x].z, pf[x].w);
             }
             if (pw == kPrep - 1) {
                 const float x = wave_prefix_sum(pg);  // gamma, inclusive over the chunk rows
@@ -588,8 +593,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     const int i = 16 * ti + lr;
                     bf16x4 ph, pl;
                     split4(pv4, ph, pl);
-                    *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + 16 * tj + lq]) = ph;
-                    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + 16 * tj + lq]) = pl;
+                    *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + kperm(16 * tj + lq)]) = ph;
+                    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + kperm(16 * tj + lq)]) = pl;
                 }
         };
 
