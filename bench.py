@@ -710,6 +710,39 @@ def measure_next_rows(lrc, dev, lens, reps=10):
     return res
 
 
+def measure_skew(lrc, dev, stream, reps=10):
+    """WKV (2560 channels) and the fused Mamba mixer rows (5120 x 16) on equal totals of rows with a few
+    long prompts -- 8 x 3832 and 4 x 7664 rows -- beside the mixed lengths: the sequential chunk chain of
+    the longest prompt and the number of (prompt, channel block) workgroups set these times."""
+    import torch
+
+    from linear_recurrence_chunked_amd import inputs
+
+    sh = inputs.MIXED_SHAPES
+    res = {}
+    for name, lens in [("8x3832", [3832] * 8), ("4x7664", [7664] * 4)]:
+        R, P = sum(lens), len(lens)
+        r = inputs.mixed_rwkv(lens, dev)
+        C = r["k"].shape[1]
+        o = torch.empty_like(r["k"])
+        ms = _time_ms(lambda: lrc.wkv4_prefill(r["k"], r["v"], r["w"], r["u"], o, r["num"], r["den"], r["max"], lens),
+                      stream, reps)
+        wkv = _entry(ms, R, "hbm", R * C * 12 + P * C * 24 + C * 8, HBM_PEAK_GBS)
+        del r, o
+        m = inputs.mixed_mamba_mixer(lens, dev)
+        Dm, N = sh["mamba_d_inner"], sh["mamba_d_state"]
+        y = torch.empty_like(m["x"])
+        ms = _time_ms(lambda: lrc.mamba_mixer_prefill(m["x"], m["dt"], m["A"], m["B"], m["C"], m["D"], y, m["h0"], lens),
+                      stream, reps)
+        rate = R * Dm * N / (ms * 1e-3)
+        peak = ALU_LANE_SLOTS / MIXER_SLOTS_PER_STEP
+        mixer = {"ms": round(ms, 5), "rows_per_s": R / (ms * 1e-3), "bound": "alu", "state_steps_per_s": rate,
+                 "frac": rate / peak}
+        del m, y
+        res[name] = {"rows": R, "wkv4": wkv, "mamba_mixer": mixer}
+    return res
+
+
 def fresh_outputs_sample(lrc, W):
     """Run one step from fresh states and keep host copies of the sampled outputs."""
     import numpy as np
@@ -827,6 +860,8 @@ def main():
     nxt = measure_next_rows(lrc, dev, W["lens"]) if not (args.only or args.no_extra_legs) else None
     if nxt:  # the token-dependent decay's waits, counted with those of the step's WKV
         nxt["wkv_tdecay"]["lds_wait_timeouts"] = lrc.wait_timeouts()
+    if nxt:
+        nxt["skewed_lengths"] = measure_skew(lrc, dev, stream)
     if nxt and "scan" in per_k:
         nxt["mamba_mixer"]["vs_scan_kernel_alone"] = per_k["scan"] / nxt["mamba_mixer"]["ms"]
     dom = max(kernels, key=lambda k: per_k[k])
