@@ -253,7 +253,9 @@ lrc_status lrc_gdn_prefill_ws(const void* q, const void* k, const void* v, const
 
 /* The triangular inverse of K3 on its own, at the precision K3 uses (FP32):
    T = (I + strictly_lower(A))^-1 for `batch` matrices of n x n, n <= 64,
-   padded to 64 rows with identity.  A, T [batch, n, n] float; T must not
+   padded to 64 rows with identity: the diagonal 16x16 tiles as 8x8
+   products on the vector ALUs, the level products on the FP32 matrix cores,
+   as in the bf16 chunk kernel.  A, T [batch, n, n] float; T must not
    overlap A.  [qwen] */
 lrc_status lrc_unit_lower_inverse(const float* A, float* T, int batch, int n, void* stream);
 

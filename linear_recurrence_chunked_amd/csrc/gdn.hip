@@ -302,17 +302,30 @@ hipError_t dispatch_dk(const void* q, const void* k, const void* v, const float*
     return hipErrorInvalidValue;
 }
 
-// Standalone inverse: one workgroup per matrix.
+// Standalone inverse: one workgroup per matrix, the phases of the bf16 chunk
+// kernel (diagonal tiles on the vector ALUs) with the level products on the
+// FP32 matrix cores.
 __global__ __launch_bounds__(kThreads) void tri_inverse_kernel(const float* __restrict__ A, float* __restrict__ T,
                                                               int n) {
+    constexpr int NW = kThreads / 64;
     __shared__ __align__(16) float M[64 * kTriLd];
     __shared__ __align__(16) float scratch[kTriScratch];
+    __shared__ __align__(16) float dscratch[NW * tri::kDiagScratch];
     const long base = (long)blockIdx.x * n * n;
     for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
         const int r = e >> 6, c = e & 63;
         M[r * kTriLd + c] = (r < n && c < r) ? A[base + (long)r * n + c] : 0.f;
     }
-    tri_inverse64<kThreads / 64>(M, scratch);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __syncthreads();
+    tri::diag_valu<NW>(M, dscratch, w);
+    __syncthreads();
+    tri::lvl16<NW>(M, w);
+    __syncthreads();
+    tri::lvl32a<NW>(M, scratch, w);
+    __syncthreads();
+    tri::lvl32b<NW>(M, scratch, w);
+    __syncthreads();
     for (int e = threadIdx.x; e < n * n; e += kThreads) {
         const int r = e / n, c = e % n;
         T[base + e] = M[r * kTriLd + c];

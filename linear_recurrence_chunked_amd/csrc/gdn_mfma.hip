@@ -59,8 +59,9 @@
 // per element; below them it is the product e^{gamma_i - gamma_c}
 // e^{gamma_c - gamma_j} through the tile's first row c, both factors <= 1.
 // The 64-row inverse (8x8 Neumann blocks, then 2x2 block levels) keeps T in
-// FP32; its tile products run as hi/lo bf16 pairs on the bf16 matrix cores,
-// or, with SPLIT, on the FP32 matrix cores.
+// FP32: the diagonal 16x16 tiles as 8x8 products on the vector ALUs, the
+// level products as hi/lo bf16 pairs on the bf16 matrix cores or, with SPLIT,
+// on the FP32 matrix cores.
 #include <algorithm>
 #include <cstddef>
 #include <cstring>
@@ -89,6 +90,7 @@ struct PipeSmem {
     __bf16 P_lo[LO];
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
+    alignas(16) float dscratch[kPrep * tri::kDiagScratch];  // the diagonal tiles' 8x8 products
     float gam[3][64];       // per-row values, by chunk index mod 3
     float Gam[3][64];       // e^gamma
     float beta[3][64];
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             const int nb = (n + 1) & 1, nrb = (n + 4) % 3;  // buffers of chunk n+1
 
             // ---- A: diagonal tiles of the inverse of chunk n+1
-            if (do_next) tri::diag<kPrep, InvMM>(sm.M, sm.scratch, pw);
+            if (do_next) tri::diag_valu<kPrep>(sm.M, sm.dscratch, pw);
             __syncthreads();
 
             // ---- B: level 16

@@ -168,6 +168,102 @@ __device__ inline void diag(float* M, float* /*scratch*/, int w) {
     }
 }
 
+// The diagonal phase on the vector ALUs in FP32, one 16x16 tile per wave, for
+// callers with kDiagScratch floats of LDS per wave: the 8x8 Neumann products
+// and the level-8 step as 8x8 products.  Lane l holds entries (i, j), (i, j+1)
+// of block b = l/32 of the tile's two 8x8 diagonal blocks, i = (l/4) % 8,
+// j = 2 (l%4); an 8x8 product is 16 FMAs per lane over the left operand's row
+// (two 16-byte LDS reads) and the right operand's two columns (eight 8-byte
+// reads).  Per wave that is six products in five dependent steps, against the
+// nine 16x16 tile products of diag().
+//   N2 = N N;  N3 = N N2, N4 = N2 N2;  X = I - N + N2 - N3;  D = X + X N4;
+//   level 8:  T21 = -D1 (L D0).
+constexpr int kDiagScratch = 4 * 128 + 64;  // N2, N3, N4, D (two blocks each), L D0
+
+// Row i of a row-major 8x8 block with row stride ld (16-byte aligned rows).
+__device__ __forceinline__ void row8(const float* m, int ld, int i, float (&r)[8]) {
+    const tri_f4 a = *reinterpret_cast<const tri_f4*>(m + i * ld);
+    const tri_f4 b = *reinterpret_cast<const tri_f4*>(m + i * ld + 4);
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+}
+// Columns j, j+1 of a row-major 8x8 block.
+__device__ __forceinline__ void cols8(const float* m, int ld, int j, float (&c0)[8], float (&c1)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float2 x = *reinterpret_cast<const float2*>(m + k * ld + j);
+        c0[k] = x.x;
+        c1[k] = x.y;
+    }
+}
+__device__ __forceinline__ float2 dot8(const float (&r)[8], const float (&c0)[8], const float (&c1)[8]) {
+    float2 z = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        z.x = fmaf(r[k], c0[k], z.x);
+        z.y = fmaf(r[k], c1[k], z.y);
+    }
+    return z;
+}
+
+template <int NW>
+__device__ inline void diag_valu(float* M, float* scratch, int w) {
+    constexpr int ld = kTriLd;
+    int tl = threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const int lane = tl & 63, b = lane >> 5, i = (lane >> 2) & 7, j = 2 * (lane & 3);
+    float* S = scratch + w * kDiagScratch;
+    float* N2 = S + 64 * b;  // this lane's block of each buffer, row stride 8
+    float* N3 = S + 128 + 64 * b;
+    float* N4 = S + 256 + 64 * b;
+    float* Db = S + 384;     // both blocks: D0 at 0, D1 at 64
+    float* Y = S + 512;      // L D0
+    for (int t = w; t < 4; t += NW) {
+        float* Mt = M + 16 * t * ld + 16 * t;
+        const float* Mb = Mt + 8 * b * ld + 8 * b;  // block b of the tile in A
+        float n[8], c0[8], c1[8];
+        row8(Mb, ld, i, n);
+        cols8(Mb, ld, j, c0, c1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {  // N: the block's strictly lower part
+            n[k] = k < i ? n[k] : 0.f;
+            c0[k] = j < k ? c0[k] : 0.f;
+            c1[k] = j + 1 < k ? c1[k] : 0.f;
+        }
+        *reinterpret_cast<float2*>(&N2[8 * i + j]) = dot8(n, c0, c1);
+        wave_sync();
+        float r2[8];
+        row8(N2, 8, i, r2);
+        cols8(N2, 8, j, c0, c1);
+        *reinterpret_cast<float2*>(&N3[8 * i + j]) = dot8(n, c0, c1);
+        *reinterpret_cast<float2*>(&N4[8 * i + j]) = dot8(r2, c0, c1);
+        wave_sync();
+        float x[8];
+        row8(N3, 8, i, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = ((k == i ? 1.f : 0.f) - n[k]) + (r2[k] - x[k]);
+        cols8(N4, 8, j, c0, c1);
+        const float2 xn4 = dot8(x, c0, c1);
+        const float2 d = make_float2(x[j] + xn4.x, x[j + 1] + xn4.y);
+        *reinterpret_cast<float2*>(&Db[64 * b + 8 * i + j]) = d;
+        *reinterpret_cast<float2*>(&Mt[(8 * b + i) * ld + 8 * b + j]) = d;
+        wave_sync();
+        // level 8 (both halves of the wave compute it; block 1's lanes keep it)
+        float l[8];
+        row8(Mt + 8 * ld, ld, i, l);
+        cols8(Db, 8, j, c0, c1);
+        const float2 y = dot8(l, c0, c1);
+        if (b) *reinterpret_cast<float2*>(&Y[8 * i + j]) = y;
+        wave_sync();
+        float d1[8];
+        row8(Db + 64, 8, i, d1);
+        cols8(Y, 8, j, c0, c1);
+        const float2 z = dot8(d1, c0, c1);
+        if (b) *reinterpret_cast<float2*>(&Mt[(8 + i) * ld + j]) = make_float2(-z.x, -z.y);
+        wave_sync();  // the scratch is reused by the next tile
+    }
+}
+
 // level 16: blocks b = 0, 1 (rows 32b+16 .., columns 32b ..)
 template <int NW, class MM = MmF32>
 __device__ inline void lvl16(float* M, int w) {
