@@ -33,7 +33,7 @@
 // Gamma, beta and state-update decay of three, where the rows of four are
 // and which prompt they belong to, and one copy of A -> T (FP32),
 // T and P (bf16) and K^T: each is written in a segment where no wave
-// reads the copy it replaces.  About 147 KiB, one workgroup per CU.
+// reads the copy it replaces.  About 146 KiB (156 KiB in the split form), one workgroup per CU.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
 // of lane l is row l%16 with 8 k-values, the B operand column l%16 with the
@@ -77,16 +77,21 @@ namespace {
 
 constexpr int kPrep = 4;     // waves that prepare the next chunk
 
+// Row strides (bf16) of the operands read as fragments: a 16-byte read by 16
+// rows is free of LDS bank conflicts when rows start 32 bytes apart modulo 128
+// (row strides of 144 or 80 bf16; 136 and 72 cost about a quarter more per
+// read).  The split form, whose lo copies need the room, keeps the narrower ones.
 template <int DK, bool SPLIT>
 struct PipeSmem {
-    static constexpr int LDK = DK + 8;
-    static constexpr int LO = SPLIT ? 64 * L64 : 8;  // the lo copies are used with SPLIT only
+    static constexpr int LDK = SPLIT ? DK + 8 : DK + 16;  // K, Q rows
+    static constexpr int LT = SPLIT ? 72 : 80;            // T, P, K^T rows (64 columns)
+    static constexpr int LO = SPLIT ? 64 * LT : 8;  // the lo copies are used with SPLIT only
     __bf16 K[2][64 * LDK];  // chunk rows, by parity of the chunk index
     __bf16 Q[2][64 * LDK];
-    __bf16 KT[DK * L64];    // K^T of the chunk whose state update comes next
-    __bf16 T_hi[64 * L64];  // (I + A)^-1 in bf16 (with SPLIT: hi and lo parts)
+    __bf16 KT[DK * LT];     // K^T of the chunk whose state update comes next
+    __bf16 T_hi[64 * LT];   // (I + A)^-1 in bf16 (with SPLIT: hi and lo parts)
     __bf16 T_lo[LO];
-    __bf16 P_hi[64 * L64];  // masked decayed Q K^T
+    __bf16 P_hi[64 * LT];   // masked decayed Q K^T
     __bf16 P_lo[LO];
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
@@ -144,14 +149,14 @@ struct ChunkCursor {
 };
 
 // One 16x16 tile of the FP32 matrix into its bf16 copy (with SPLIT: hi and lo copies).
-template <bool SPLIT>
+template <bool SPLIT, int LT>
 __device__ __forceinline__ void split_tile(const float* M, __bf16* hi, __bf16* lo, int ti, int tj, int lane) {
     const int r = 16 * ti + (lane >> 2), c = 16 * tj + 4 * (lane & 3);
     const floatx4 x = *reinterpret_cast<const floatx4*>(&M[r * kTriLd + c]);
     bf16x4 h, l;
     split4(x, h, l);
-    *reinterpret_cast<bf16x4*>(&hi[r * L64 + kperm(c)]) = h;
-    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&lo[r * L64 + kperm(c)]) = l;
+    *reinterpret_cast<bf16x4*>(&hi[r * LT + kperm(c)]) = h;
+    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&lo[r * LT + kperm(c)]) = l;
 }
 
 // Masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M: tile
@@ -205,6 +210,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
     static_assert(CG == 2, "a lane's column pair is one even and one odd column");
     using Sm = PipeSmem<DK, SPLIT>;
     constexpr int LDK = Sm::LDK;
+    constexpr int LT = Sm::LT;
     constexpr int KS = DK / 32;             // k-steps over dk
     constexpr int RT = DK / 16;             // state row tiles
     constexpr int PS = SPLIT ? 2 : 1;       // passes of a product with one FP32 operand
@@ -353,9 +359,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(ks0[c][2 * s], ks0[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
-                        const bf16x8 ah = frag(&sm.T_hi[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
+                        const bf16x8 ah = frag(&sm.T_hi[(16 * t + lr) * LT + 32 * s + 8 * lg]);
                         bf16x8 al;
-                        if constexpr (SPLIT) al = frag(&sm.T_lo[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
+                        if constexpr (SPLIT) al = frag(&sm.T_lo[(16 * t + lr) * LT + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             u[c][t] = mfma(ah, bh[c], u[c][t]);
@@ -384,9 +390,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
-                        const bf16x8 ah = frag(&sm.P_hi[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
+                        const bf16x8 ah = frag(&sm.P_hi[(16 * t + lr) * LT + 32 * s + 8 * lg]);
                         bf16x8 al;
-                        if constexpr (SPLIT) al = frag(&sm.P_lo[(16 * t + lr) * L64 + 32 * s + 8 * lg]);
+                        if constexpr (SPLIT) al = frag(&sm.P_lo[(16 * t + lr) * LT + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             pu[c][t] = mfma(ah, bh[c], pu[c][t]);
@@ -438,7 +444,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int tr = 0; tr < RT; ++tr) {
-                        const bf16x8 a = frag(&sm.KT[(16 * tr + lr) * L64 + 32 * s + 8 * lg]);
+                        const bf16x8 a = frag(&sm.KT[(16 * tr + lr) * LT + 32 * s + 8 * lg]);
 #pragma unroll
                         for (int c = 0; c < CG; ++c) {
                             sacc[c][tr] = mfma(a, bh[c], sacc[c][tr]);
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                         uint2 out;
                         out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
                         out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
-                        *reinterpret_cast<uint2*>(&sm.KT[kperm_inv(8 * m + e) * L64 + kperm(4 * nn)]) = out;
+                        *reinterpret_cast<uint2*>(&sm.KT[kperm_inv(8 * m + e) * LT + kperm(4 * nn)]) = out;
                     }
                 }
             }
@@ -595,8 +601,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     const int i = 16 * ti + lr;
                     bf16x4 ph, pl;
                     split4(pv4, ph, pl);
-                    *reinterpret_cast<bf16x4*>(&sm.P_hi[i * L64 + kperm(16 * tj + lq)]) = ph;
-                    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&sm.P_lo[i * L64 + kperm(16 * tj + lq)]) = pl;
+                    *reinterpret_cast<bf16x4*>(&sm.P_hi[i * LT + kperm(16 * tj + lq)]) = ph;
+                    if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&sm.P_lo[i * LT + kperm(16 * tj + lq)]) = pl;
                 }
         };
 
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         using InvMM = typename std::conditional<SPLIT, tri::MmF32, tri::MmBf16Split>::type;
         // Tiles above the diagonal stay zero for the whole prompt.
         for (int e = pt; e < 64 * kTriLd; e += PT) sm.M[e] = 0.f;
-        for (int e = pt; e < 64 * L64; e += PT) {
+        for (int e = pt; e < 64 * LT; e += PT) {
             sm.T_hi[e] = sm.P_hi[e] = static_cast<__bf16>(0.f);
             if constexpr (SPLIT) sm.T_lo[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
         }
@@ -635,9 +641,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             //      chunk n+2 into the buffers chunk n used, chunk n+3 in flight
             if (do_next) {
                 tri::lvl32a<kPrep, InvMM>(sm.M, sm.scratch, pw);
-                split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
-                if (pw == 0) split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
-                if (pw == 1) split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
+                split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
+                if (pw == 0) split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
+                if (pw == 1) split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
             }
             if (do_stage) {
                 stage(n & 1, (n + 5) % 3);
@@ -649,7 +655,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (do_next) {
                 tri::lvl32b<kPrep, InvMM>(sm.M, sm.scratch, pw);
                 tri::wave_sync();
-                split_tile<SPLIT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
+                split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
                 masked_qk(nb, nrb);
             }
             __syncthreads();
