@@ -72,7 +72,7 @@ struct CpChunks {
 // which are dead once A and K^T are formed.
 template <int DK, int DV>
 struct CpPrepSmem {
-    static constexpr int LDK = DK + 8;
+    static constexpr int LDK = DK + 16;  // K rows: 16-byte fragment reads free of bank conflicts
     static constexpr int R1 = 64 * LDK > 2 * 64 * L64 ? 64 * LDK : 2 * 64 * L64;
     __bf16 KT_[R1];       // K rows, then T diag(beta Gamma) and T diag(beta)
     __bf16 KT[DK * L64];  // K^T
@@ -330,12 +330,15 @@ __global__ __launch_bounds__(64 * kCpPrepWaves, 2) void gdn_cp_prep_kernel(
 // and U that each state wave hands to its output wave, by chunk parity.
 template <int DK, int NSW>
 struct CpStateSmem {
-    static constexpr int LDK = DK + 8;
+    // Row strides (bf16) at which 16-byte fragment reads by 16 rows are free of
+    // LDS bank conflicts (rows start 32 bytes apart modulo 128).
+    static constexpr int LDK = DK + 16;  // W, Q rows
+    static constexpr int LT = 80;        // K^T, P rows (64 columns)
     static constexpr int KS = DK / 32;
     __bf16 W[2][64 * LDK];
-    __bf16 KT[2][DK * L64];
+    __bf16 KT[2][DK * LT];
     __bf16 Q[2][64 * LDK];
-    __bf16 P[2][64 * L64];
+    __bf16 P[2][64 * LT];
     float dec[2][64];  // with W, K^T: e^{min(gamma_S - gamma_r, 0)}, 0 past the chunk
     float Gam[2][64];  // with Q, P: e^{gamma_r}
     float GS[2];       // with W, K^T: e^{gamma_S}
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
             for (int x = 0; x < NP8; ++x) {
                 const int e = lt + x * NT, r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
                 *reinterpret_cast<u32x4*>(&sm.W[b][r * LDK + c8]) = rw[x];
-                *reinterpret_cast<u32x4*>(&sm.KT[b][(e >> 3) * L64 + (e & 7) * 8]) = rk[x];
+                *reinterpret_cast<u32x4*>(&sm.KT[b][(e >> 3) * Sm::LT + (e & 7) * 8]) = rk[x];
             }
             if (lt < 64) sm.dec[b][lt] = rdec;
         };
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
 #pragma unroll
             for (int x = 0; x < 512 / NT; ++x) {
                 const int e = lt + x * NT;
-                *reinterpret_cast<u32x4*>(&sm.P[b][(e >> 3) * L64 + (e & 7) * 8]) = rp[x];
+                *reinterpret_cast<u32x4*>(&sm.P[b][(e >> 3) * Sm::LT + (e & 7) * 8]) = rp[x];
             }
             if (lt < 64) sm.Gam[b][lt] = rgam;
         };
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                     const bf16x8 bu = sm.xu[b][pair][s][lane];
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t)
-                        pu[t] = mfma(frag(&sm.P[b][(16 * t + lr) * L64 + 32 * s + 8 * lg]), bu, pu[t]);
+                        pu[t] = mfma(frag(&sm.P[b][(16 * t + lr) * Sm::LT + 32 * s + 8 * lg]), bu, pu[t]);
                 }
                 const auto orsrc = buffer_rsrc(o + (row0 + 64l * m) * (long)rowV + (long)h * DV + col0,
                                               (uint32_t)S * rowV * 4);
@@ -589,7 +592,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 acc_frag<false>(u[2 * s], u[2 * s + 1], bh, bl);
 #pragma unroll
                 for (int tr = 0; tr < RT; ++tr)
-                    sacc[tr] = mfma(frag(&sm.KT[b][(16 * tr + lr) * L64 + 32 * s + 8 * lg]), bh, sacc[tr]);
+                    sacc[tr] = mfma(frag(&sm.KT[b][(16 * tr + lr) * Sm::LT + 32 * s + 8 * lg]), bh, sacc[tr]);
             }
             read_ahead<2 * RT, 1, 1, 2>();
         }
