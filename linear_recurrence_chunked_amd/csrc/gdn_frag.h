@@ -6,8 +6,8 @@
 // accumulator holds column l%16, rows 4(l/16) .. +3.  A wave's own [rows x 16]
 // accumulators serve directly as B operands when the k-values of lane group g
 // are taken as rows {4g .. 4g+3} of one 16-row tile and {16+4g .. 16+4g+3} of
-// the next (acc_frag); the A operand then reads the same two 4-element runs
-// of its row (frag_perm).
+// the next (acc_frag); the A operand then needs the same two 4-element runs
+// of its row, which the k-permuted row layout below keeps in one 16-byte run.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,22 +22,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int L64 = 64 + 8;  // row stride (bf16) of 64-column operands
+// Row stride (bf16) of 64-column operands where LDS is short (the chunk-parallel
+// prep kernel); 16-byte reads by 16 such rows meet some bank conflicts, which
+// a stride of 80 avoids where the room allows.
+constexpr int L64 = 64 + 8;
 constexpr int CG = 2;        // 16-column groups of a state wave: its even and its odd columns
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 frag(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x8 frag_perm(const __bf16* row_ks, int g) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row_ks + 4 * g);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(row_ks + 16 + 4 * g);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
 // A k-permuted layout of a row: within each block of 32 k-values, positions
 // 8g .. 8g+3 hold k = 4g .. 4g+3 and positions 8g+4 .. 8g+7 hold
-// k = 16+4g .. 16+4g+3 (g = 0 .. 3).  Rows stored this way give the frag_perm
-// operand of lane group g as one contiguous 16-byte read at position 8g
-// (a single ds_read_b128 instead of two 8-byte reads 32 bytes apart).  A run of
+// k = 16+4g .. 16+4g+3 (g = 0 .. 3).  Rows stored this way give the A operand
+// of lane group g as one contiguous 16-byte read at position 8g (a single
+// ds_read_b128 instead of two 8-byte reads 32 bytes apart).  A run of
 // 4 k-values starting at a multiple of 4 stays contiguous.  Products whose two
 // operands are both stored this way (K K^T, Q K^T) are unchanged by it.
 __device__ __forceinline__ int kperm(int k) {
