@@ -17,8 +17,8 @@
 //  * dv/32 state waves, each owning 32 columns of the [dk x dv] state in MFMA
 //    accumulators, swapped at each prompt boundary.  In step n they run the
 //    chain that depends on the state for chunk n: K S_0, Q S_0 and the
-//    right-hand side (A), U (B), O (C), the state update and the loads of V
-//    of chunk n+1 (D), and they build K^T of chunk n+1 and two tile pairs of
+//    right-hand side, then the loads of V of chunk n+1 (A), U (B), O (C), the
+//    state update (D), and they build K^T of chunk n+1 and two tile pairs of
 //    chunk n+2's A (E).  A lane's two 16-column groups are the even and the
 //    odd columns of the wave's 32, so that V, O and the state move as column
 //    pairs.  V, O and the state go through buffer resources; those of V and O
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lq = lg * 4;
             floatx4 ks0[CG][4], qs0[CG][4], u[CG][4];
 
-            // ---- A: K S_0, Q S_0 and RHS = diag(beta) V - diag(beta Gamma) K S_0
+            // ---- A: K S_0, Q S_0 and RHS = diag(beta) V - diag(beta Gamma) K S_0; V of chunk n+1
             if (do_state) {
 #pragma unroll
                 for (int c = 0; c < CG; ++c)
@@ -343,6 +343,22 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                             ks0[c][t][r] = b4[r] * (vv - G4[r] * ks0[c][t][r]);
                         }
                 }
+            }
+            if (do_next) {
+                // V of chunk n+1, as soon as this chunk's RHS has used V of chunk n:
+                // four segments ahead of its use.  Through a buffer resource that ends
+                // after the chunk's S rows: rows past it read as zero (beta is zero
+                // there too).  V is read once and O written once: both streaming.
+                const int S = meta(n + 1, 1);
+                const auto vrsrc = buffer_rsrc(v + meta(n + 1, 0) * (long)rowV + (long)h * dv + col0,
+                                              (uint32_t)S * rowV * 2);
+                uint32_t v_lane = (__umul24(lq, rowV) + 2 * lr) * 2;
+                asm volatile("" : "+v"(v_lane));
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pv[4 * t + r] = __builtin_amdgcn_raw_buffer_load_b32(vrsrc, v_lane + (16 * t + r) * rowV * 2, 0, kNontemporal);
             }
             __syncthreads();
 
@@ -418,13 +434,13 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int r = 0; r < 4; ++r) {
                         const u32x2 pair = {__float_as_uint(fmaf(G4[r], qs0[0][t][r], pu[0][t][r])),
                                             __float_as_uint(fmaf(G4[r], qs0[1][t][r], pu[1][t][r]))};
-                        __builtin_amdgcn_raw_buffer_store_b64(pair, orsrc, o_lane + (16 * t + r) * rowV * 4, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(pair, orsrc, o_lane + (16 * t + r) * rowV * 4, 0, kNontemporal);
                     }
                 }
             }
             __syncthreads();
 
-            // ---- D: S_S = e^{gamma_S} S_0 + K^T (decS U); V of chunk n+1
+            // ---- D: S_S = e^{gamma_S} S_0 + K^T (decS U)
             if (do_state) {
                 const float GS = sm.Gam[rb][Sn - 1];
 #pragma unroll
@@ -453,20 +469,6 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     }
                 }
                 read_ahead<2 * RT, SPLIT ? 2 : 1, PS * CG, 2>();
-            }
-            if (do_next) {
-                // Through a buffer resource that ends after the chunk's S rows: rows
-                // past it read as zero (beta is zero there too).
-                const int S = meta(n + 1, 1);
-                const auto vrsrc = buffer_rsrc(v + meta(n + 1, 0) * (long)rowV + (long)h * dv + col0,
-                                              (uint32_t)S * rowV * 2);
-                uint32_t v_lane = (__umul24(lq, rowV) + 2 * lr) * 2;
-                asm volatile("" : "+v"(v_lane));
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        pv[4 * t + r] = __builtin_amdgcn_raw_buffer_load_b32(vrsrc, v_lane + (16 * t + r) * rowV * 2, 0, 0);
             }
             __syncthreads();
 
