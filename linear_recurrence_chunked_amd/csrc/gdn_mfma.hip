@@ -19,21 +19,26 @@
 //    chain that depends on the state for chunk n: K S_0, Q S_0 and the
 //    right-hand side, then the loads of V of chunk n+1 (A), U (B), O (C), the
 //    state update (D), and they build K^T of chunk n+1 and two tile pairs of
-//    chunk n+2's A (E).  A lane's two 16-column groups are the even and the
+//    chunk n+2's A (E).  In the default form they also form the masked
+//    decayed Q K^T (P) of chunk n+1 after U (B), into the P buffer that chunk
+//    n does not use.  A lane's two 16-column groups are the even and the
 //    odd columns of the wave's 32, so that V, O and the state move as column
 //    pairs.  V, O and the state go through buffer resources; those of V and O
 //    end after the chunk's rows, so rows past it need no test.
 //  * 4 prep waves, which in step n prepare chunk n+1, the part that does not
 //    depend on the state: the inverse (diagonal tiles in A, level 16 in B,
-//    level 32 in C and D, each tile of T rounded to bf16 once final) and
-//    the masked decayed Q K^T (D); they stage chunk n+2 into LDS (C) and form
-//    the rest of its masked K K^T (E), and keep the rows of chunk n+3 in
-//    flight.
+//    level 32 in C and D, each tile of T rounded to bf16 once final) and, in
+//    the split form, P (D).  They stage chunk n+2 into LDS and keep the rows
+//    of chunk n+3 in flight: in the default form prep waves 2 and 3, idle
+//    during level 16, in B and waves 0 and 1, whose level-32 tiles are the
+//    lighter ones, in D; in the split form all four in C.  They form the rest
+//    of chunk n+2's masked K K^T (E).
 // LDS holds K and Q of two chunks (by chunk parity), the per-row gamma,
 // Gamma, beta and state-update decay of three, where the rows of four are
-// and which prompt they belong to, and one copy of A -> T (FP32),
-// T and P (bf16) and K^T: each is written in a segment where no wave
-// reads the copy it replaces.  About 146 KiB (156 KiB in the split form), one workgroup per CU.
+// and which prompt they belong to, one copy of A -> T (FP32), T (bf16) and
+// K^T, and P (bf16) by chunk parity (one copy, with its lo parts, in the
+// split form): each is written in a segment where no wave reads the copy it
+// replaces.  About 156 KiB in either form, one workgroup per CU.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
 // of lane l is row l%16 with 8 k-values, the B operand column l%16 with the
@@ -86,12 +91,13 @@ struct PipeSmem {
     static constexpr int LDK = SPLIT ? DK + 8 : DK + 16;  // K, Q rows
     static constexpr int LT = SPLIT ? 72 : 80;            // T, P, K^T rows (64 columns)
     static constexpr int LO = SPLIT ? 64 * LT : 8;  // the lo copies are used with SPLIT only
+    static constexpr int NPB = SPLIT ? 1 : 2;      // P buffers: by chunk parity in the default form
     __bf16 K[2][64 * LDK];  // chunk rows, by parity of the chunk index
     __bf16 Q[2][64 * LDK];
     __bf16 KT[DK * LT];     // K^T of the chunk whose state update comes next
     __bf16 T_hi[64 * LT];   // (I + A)^-1 in bf16 (with SPLIT: hi and lo parts)
     __bf16 T_lo[LO];
-    __bf16 P_hi[64 * LT];   // masked decayed Q K^T
+    __bf16 P_hi[NPB][64 * LT];  // masked decayed Q K^T
     __bf16 P_lo[LO];
     float M[64 * kTriLd];   // A, then T, in FP32
     float scratch[kTriScratch];
@@ -195,6 +201,65 @@ __device__ __forceinline__ void masked_kk(Sm& sm, int b, int rbuf, int first, in
             for (int r = 0; r < 4; ++r) av[r] = i > 16 * tj + lq + r ? bi * dec[r] * kk[x][r] : 0.f;
             *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
         }
+}
+
+// Masked decayed Q K^T of the chunk in buffers (b, rbuf), key tile TJ with
+// query tiles TI0 .. TI1, into P (bf16, queries as rows).  Computed transposed
+// (keys as rows), so that one key fragment per k-step serves every query
+// tile of the group.
+template <int DK, int TJ, int TI0, int TI1, class Sm>
+__device__ __forceinline__ void qk_group(Sm& sm, int b, int rbuf, __bf16* P) {
+    constexpr int LDK = Sm::LDK, LT = Sm::LT, KS = DK / 32, NT = TI1 - TI0 + 1;
+    int tid_c = threadIdx.x;
+    asm volatile("" : "+v"(tid_c));
+    const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
+    floatx4 acc[NT];
+#pragma unroll
+    for (int x = 0; x < NT; ++x) acc[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const bf16x8 a = frag(&sm.K[b][(16 * TJ + lr) * LDK + 32 * s + lk]);
+#pragma unroll
+        for (int x = 0; x < NT; ++x) acc[x] = mfma(a, frag(&sm.Q[b][(16 * (TI0 + x) + lr) * LDK + 32 * s + lk]), acc[x]);
+    }
+    read_ahead<KS, NT + 1, NT, (KS < 2 ? KS : 2)>();
+#pragma unroll
+    for (int x = 0; x < NT; ++x) {
+        const floatx4 pv4 = tile_decay(sm.gam[rbuf], TI0 + x, TJ, lr, lq) * acc[x];
+        bf16x4 ph, pl;
+        split4(pv4, ph, pl);
+        *reinterpret_cast<bf16x4*>(&P[(16 * (TI0 + x) + lr) * LT + kperm(16 * TJ + lq)]) = ph;
+    }
+}
+
+// All ten tiles of P, dealt to NS state waves by key tile: 3, 3, 2, 2 tiles
+// for four waves (the last one takes the first and the last diagonal tile),
+// 5 and 5 for two.
+template <int DK, int NS, class Sm>
+__device__ __forceinline__ void state_qk(Sm& sm, int b, int rbuf, __bf16* P, int w) {
+    if constexpr (NS == 4) {
+        if (w == 0) qk_group<DK, 0, 1, 3>(sm, b, rbuf, P);
+        else if (w == 1) qk_group<DK, 1, 1, 3>(sm, b, rbuf, P);
+        else if (w == 2) qk_group<DK, 2, 2, 3>(sm, b, rbuf, P);
+        else {
+            qk_group<DK, 0, 0, 0>(sm, b, rbuf, P);
+            qk_group<DK, 3, 3, 3>(sm, b, rbuf, P);
+        }
+    } else if constexpr (NS == 2) {
+        if (w == 0) {
+            qk_group<DK, 0, 0, 3>(sm, b, rbuf, P);
+            qk_group<DK, 3, 3, 3>(sm, b, rbuf, P);
+        } else {
+            qk_group<DK, 1, 1, 3>(sm, b, rbuf, P);
+            qk_group<DK, 2, 2, 3>(sm, b, rbuf, P);
+        }
+    } else {
+        static_assert(NS == 1, "one, two or four state waves");
+        qk_group<DK, 0, 0, 3>(sm, b, rbuf, P);
+        qk_group<DK, 1, 1, 3>(sm, b, rbuf, P);
+        qk_group<DK, 2, 2, 3>(sm, b, rbuf, P);
+        qk_group<DK, 3, 3, 3>(sm, b, rbuf, P);
+    }
 }
 
 // Grid (value heads, prompts); NS = dv / 32 state waves, then kPrep prep waves.
@@ -390,6 +455,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 }
                 read_ahead<6, SPLIT ? 2 : 1, (SPLIT ? 3 : 1) * CG, 2>();
             }
+            // P of chunk n+1 into the other P buffer (the split form's prep waves
+            // form it in D)
+            if constexpr (!SPLIT)
+                if (do_next) state_qk<DK, NS>(sm, nb, (n + 4) % 3, sm.P_hi[nb], w);
             __syncthreads();
 
             // ---- C: O = diag(Gamma) Q S_0 + P U
@@ -406,7 +475,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     for (int c = 0; c < CG; ++c) acc_frag<SPLIT>(u[c][2 * s], u[c][2 * s + 1], bh[c], bl[c]);
 #pragma unroll
                     for (int t = 2 * s; t < 4; ++t) {
-                        const bf16x8 ah = frag(&sm.P_hi[(16 * t + lr) * LT + 32 * s + 8 * lg]);
+                        const bf16x8 ah = frag(&sm.P_hi[SPLIT ? 0 : cb][(16 * t + lr) * LT + 32 * s + 8 * lg]);
                         bf16x8 al;
                         if constexpr (SPLIT) al = frag(&sm.P_lo[(16 * t + lr) * LT + 32 * s + 8 * lg]);
 #pragma unroll
@@ -603,7 +672,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     const int i = 16 * ti + lr;
                     bf16x4 ph, pl;
                     split4(pv4, ph, pl);
-                    *reinterpret_cast<bf16x4*>(&sm.P_hi[i * LT + kperm(16 * tj + lq)]) = ph;
+                    *reinterpret_cast<bf16x4*>(&sm.P_hi[0][i * LT + kperm(16 * tj + lq)]) = ph;
                     if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&sm.P_lo[i * LT + kperm(16 * tj + lq)]) = pl;
                 }
         };
@@ -615,7 +684,9 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
         // Tiles above the diagonal stay zero for the whole prompt.
         for (int e = pt; e < 64 * kTriLd; e += PT) sm.M[e] = 0.f;
         for (int e = pt; e < 64 * LT; e += PT) {
-            sm.T_hi[e] = sm.P_hi[e] = static_cast<__bf16>(0.f);
+            sm.T_hi[e] = static_cast<__bf16>(0.f);
+#pragma unroll
+            for (int x = 0; x < Sm::NPB; ++x) sm.P_hi[x][e] = static_cast<__bf16>(0.f);
             if constexpr (SPLIT) sm.T_lo[e] = sm.P_lo[e] = static_cast<__bf16>(0.f);
         }
         if (nc > 0) {
@@ -635,31 +706,46 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             if (do_next) tri::diag_valu<kPrep>(sm.M, sm.dscratch, pw);
             __syncthreads();
 
-            // ---- B: level 16
+            // ---- B: level 16 (prep waves 0, 1); in the default form prep waves 2, 3
+            //      stage their part of chunk n+2 into the buffers chunk n used, and
+            //      put their part of chunk n+3 in flight
             if (do_next) tri::lvl16<kPrep, InvMM>(sm.M, pw);
+            if constexpr (!SPLIT)
+                if (do_stage && pw >= 2) {
+                    stage(n & 1, (n + 5) % 3);
+                    if (n + 3 < nc) fetch(n + 3);
+                }
             __syncthreads();
 
             // ---- C: level 32 (first half); the tiles of T that are final go to bf16;
-            //      chunk n+2 into the buffers chunk n used, chunk n+3 in flight
+            //      in the split form, chunk n+2 into the buffers chunk n used and
+            //      chunk n+3 in flight (in D in the default form)
             if (do_next) {
                 tri::lvl32a<kPrep, InvMM>(sm.M, sm.scratch, pw);
                 split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
                 if (pw == 0) split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
                 if (pw == 1) split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
             }
-            if (do_stage) {
-                stage(n & 1, (n + 5) % 3);
-                if (n + 3 < nc) fetch(n + 3);
-            }
+            if constexpr (SPLIT)
+                if (do_stage) {
+                    stage(n & 1, (n + 5) % 3);
+                    if (n + 3 < nc) fetch(n + 3);
+                }
             __syncthreads();
 
-            // ---- D: level 32 (second half) and its tile of T; P of chunk n+1
+            // ---- D: level 32 (second half) and its tile of T; in the split form P
+            //      of chunk n+1, in the default form the other half of the staging
             if (do_next) {
                 tri::lvl32b<kPrep, InvMM>(sm.M, sm.scratch, pw);
                 tri::wave_sync();
                 split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
-                masked_qk(nb, nrb);
+                if constexpr (SPLIT) masked_qk(nb, nrb);
             }
+            if constexpr (!SPLIT)
+                if (do_stage && pw < 2) {
+                    stage(n & 1, (n + 5) % 3);
+                    if (n + 3 < nc) fetch(n + 3);
+                }
             __syncthreads();
 
             // ---- E: A of chunk n+2 into M (T of chunk n+1 is in bf16 now)
