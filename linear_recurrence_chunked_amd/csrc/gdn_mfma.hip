@@ -18,8 +18,8 @@
 //    accumulators, swapped at each prompt boundary.  In step n they run the
 //    chain that depends on the state for chunk n: K S_0, Q S_0 and the
 //    right-hand side, then the loads of V of chunk n+1 (A), U (B), O (C), the
-//    state update (D), and they build K^T of chunk n+1 and two tile pairs of
-//    chunk n+2's A (E).  In the default form they also form the masked
+//    state update (D), and they build K^T of chunk n+1 and the diagonal tiles
+//    of chunk n+2's A (E).  In the default form they also form the masked
 //    decayed Q K^T (P) of chunk n+1 after U (B), into the P buffer that chunk
 //    n does not use.  A lane's two 16-column groups are the even and the
 //    odd columns of the wave's 32, so that V, O and the state move as column
@@ -31,8 +31,8 @@
 //    the split form, P (D).  They stage chunk n+2 into LDS and keep the rows
 //    of chunk n+3 in flight: in the default form prep waves 2 and 3, idle
 //    during level 16, in B and waves 0 and 1, whose level-32 tiles are the
-//    lighter ones, in D; in the split form all four in C.  They form the rest
-//    of chunk n+2's masked K K^T (E).
+//    lighter ones, in D; in the split form all four in C.  They form the six
+//    tiles of chunk n+2's masked K K^T below the diagonal (E).
 // LDS holds K and Q of two chunks (by chunk parity), the per-row gamma,
 // Gamma, beta and state-update decay of three, where the rows of four are
 // and which prompt they belong to, one copy of A -> T (FP32), T (bf16) and
@@ -201,6 +201,65 @@ __device__ __forceinline__ void masked_kk(Sm& sm, int b, int rbuf, int first, in
             for (int r = 0; r < 4; ++r) av[r] = i > 16 * tj + lq + r ? bi * dec[r] * kk[x][r] : 0.f;
             *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * tj + lq]) = av;
         }
+}
+
+// Masked decayed K K^T tiles (TI0, TJ0) and, if TI1 >= 0, (TI1, TJ1) of the
+// chunk in buffers (b, rbuf) -> A in M, with the tile indices known at compile
+// time: a key fragment used by both tiles is read once per k-step, and a
+// diagonal tile reads one fragment for both operands.
+template <int DK, int TI0, int TJ0, int TI1, int TJ1, class Sm>
+__device__ __forceinline__ void kk_tiles(Sm& sm, int b, int rbuf) {
+    constexpr int LDK = Sm::LDK, KS = DK / 32, NP = TI1 >= 0 ? 2 : 1;
+    constexpr int TI[2] = {TI0, TI1 >= 0 ? TI1 : TI0}, TJ[2] = {TJ0, TI1 >= 0 ? TJ1 : TJ0};
+    int tid_c = threadIdx.x;
+    asm volatile("" : "+v"(tid_c));
+    const int lr = tid_c & 15, lg = (tid_c >> 4) & 3, lk = lg * 8, lq = lg * 4;
+    floatx4 kk[NP];
+#pragma unroll
+    for (int x = 0; x < NP; ++x) kk[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int x = 0; x < NP; ++x)
+            kk[x] = mfma(frag(&sm.K[b][(16 * TJ[x] + lr) * LDK + 32 * s + lk]),
+                         frag(&sm.K[b][(16 * TI[x] + lr) * LDK + 32 * s + lk]), kk[x]);
+#pragma unroll
+    for (int x = 0; x < NP; ++x) {
+        const floatx4 dec = tile_decay(sm.gam[rbuf], TI[x], TJ[x], lr, lq);
+        const int i = 16 * TI[x] + lr;
+        const float bi = sm.beta[rbuf][i];
+        floatx4 av;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = i > 16 * TJ[x] + lq + r ? bi * dec[r] * kk[x][r] : 0.f;
+        *reinterpret_cast<floatx4*>(&sm.M[i * kTriLd + 16 * TJ[x] + lq]) = av;
+    }
+}
+
+// The ten tiles of A for the next chunk but one, in segment E: the six below
+// the diagonal on the four prep waves (two, two, one, one; the pairs share a
+// key fragment), the four diagonal ones on the state waves.
+template <int DK, class Sm>
+__device__ __forceinline__ void kk_prep(Sm& sm, int b, int rbuf, int pw) {
+    if (pw == 0) kk_tiles<DK, 1, 0, 2, 0>(sm, b, rbuf);
+    else if (pw == 1) kk_tiles<DK, 3, 0, 3, 1>(sm, b, rbuf);
+    else if (pw == 2) kk_tiles<DK, 2, 1, -1, -1>(sm, b, rbuf);
+    else kk_tiles<DK, 3, 2, -1, -1>(sm, b, rbuf);
+}
+template <int DK, int NS, class Sm>
+__device__ __forceinline__ void kk_state(Sm& sm, int b, int rbuf, int w) {
+    if constexpr (NS == 4) {
+        if (w == 0) kk_tiles<DK, 0, 0, -1, -1>(sm, b, rbuf);
+        else if (w == 1) kk_tiles<DK, 1, 1, -1, -1>(sm, b, rbuf);
+        else if (w == 2) kk_tiles<DK, 2, 2, -1, -1>(sm, b, rbuf);
+        else kk_tiles<DK, 3, 3, -1, -1>(sm, b, rbuf);
+    } else if constexpr (NS == 2) {
+        if (w == 0) kk_tiles<DK, 0, 0, 1, 1>(sm, b, rbuf);
+        else kk_tiles<DK, 2, 2, 3, 3>(sm, b, rbuf);
+    } else {
+        static_assert(NS == 1, "one, two or four state waves");
+        kk_tiles<DK, 0, 0, 1, 1>(sm, b, rbuf);
+        kk_tiles<DK, 2, 2, 3, 3>(sm, b, rbuf);
+    }
 }
 
 // Masked decayed Q K^T of the chunk in buffers (b, rbuf), key tile TJ with
@@ -541,7 +600,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             }
             __syncthreads();
 
-            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks; tile pairs 8, 9 of A of chunk n+2;
+            // ---- E: K^T of chunk n+1 by 4-row x 8-column blocks; the diagonal tiles of A of chunk n+2;
             //      after a prompt's last chunk, its state goes out and the next prompt's comes in
             if (do_state) {
                 const int pn = meta(n, 2), pnext = do_next ? meta(n + 1, 2) : -1;
@@ -550,7 +609,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     if (do_next) load_state(pnext);
                 }
             }
-            if (n + 2 < nc && w < 2) masked_kk<DK, (NS == 1 ? 2 : 1)>(sm, cb, (n + 5) % 3, 8 + w, NS);
+            if (n + 2 < nc) kk_state<DK, NS>(sm, cb, (n + 5) % 3, w);
             if (do_next) {
                 for (int b = tid; b < 2 * DK; b += 64 * NS) {
                     // rows 4nn .. 4nn+3, stored columns 8m .. 8m+7 (dk indices kperm_inv of them)
@@ -749,7 +808,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             __syncthreads();
 
             // ---- E: A of chunk n+2 into M (T of chunk n+1 is in bf16 now)
-            if (do_stage) masked_kk<DK, 2>(sm, n & 1, (n + 5) % 3, pw, kPrep);  // tile pairs 0 .. 7
+            if (do_stage) kk_prep<DK>(sm, n & 1, (n + 5) % 3, pw);
             __syncthreads();
         }
     }
