@@ -94,11 +94,14 @@ __device__ __forceinline__ void st_acc(float* t, int ld, int lr, int g, tri_f4 v
 #pragma unroll
     for (int r = 0; r < 4; ++r) t[(4 * g + r) * ld + lr] = v[r];
 }
-// Order this wave's LDS writes before its later LDS reads of other lanes' data.
+// Order this wave's LDS writes before its later LDS reads of other lanes'
+// data.  A wave's LDS operations execute in order, so fences at wavefront
+// scope only keep the compiler from moving the accesses across this point;
+// no wait is needed.
 __device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace tri
@@ -172,13 +175,16 @@ __device__ inline void diag(float* M, float* /*scratch*/, int w) {
 // callers with kDiagScratch floats of LDS per wave: the 8x8 Neumann products
 // and the level-8 step as 8x8 products.  Lane l holds entries (i, j), (i, j+1)
 // of block b = l/32 of the tile's two 8x8 diagonal blocks, i = (l/4) % 8,
-// j = 2 (l%4); an 8x8 product is 16 FMAs per lane over the left operand's row
-// (two 16-byte LDS reads) and the right operand's two columns (eight 8-byte
-// reads).  Per wave that is six products in five dependent steps, against the
-// nine 16x16 tile products of diag().
+// j = 2 (l%4), so the four lanes of a quad hold one row.  An 8x8 product is
+// 16 FMAs per lane over a row of the left operand and two columns of the
+// right one.  The left operand's row comes from LDS once (N, and L for level
+// 8) and otherwise from the quad's own results through DPP quad broadcasts;
+// each right operand is written to LDS transposed, so its two columns read
+// back as four 16-byte rows.  Per wave that is six products in five
+// dependent steps, against the nine 16x16 tile products of diag():
 //   N2 = N N;  N3 = N N2, N4 = N2 N2;  X = I - N + N2 - N3;  D = X + X N4;
 //   level 8:  T21 = -D1 (L D0).
-constexpr int kDiagScratch = 4 * 128 + 64;  // N2, N3, N4, D (two blocks each), L D0
+constexpr int kDiagScratch = 6 * 64;  // N2, N4 (two blocks each), D0, L D0: 8x8 blocks, transposed
 
 // Row i of a row-major 8x8 block with row stride ld (16-byte aligned rows).
 __device__ __forceinline__ void row8(const float* m, int ld, int i, float (&r)[8]) {
@@ -206,6 +212,28 @@ __device__ __forceinline__ float2 dot8(const float (&r)[8], const float (&c0)[8]
     return z;
 }
 
+// Lane Q of this lane's quad, through a DPP quad broadcast.
+template <int Q>
+__device__ __forceinline__ float quad_lane(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Q * 0x55, 0xf, 0xf, false));
+}
+// Row i of an 8x8 block whose entries (i, 2q), (i, 2q+1) sit in lane q of the quad.
+__device__ __forceinline__ void quad_row(float2 c, float (&r)[8]) {
+    r[0] = quad_lane<0>(c.x);
+    r[1] = quad_lane<0>(c.y);
+    r[2] = quad_lane<1>(c.x);
+    r[3] = quad_lane<1>(c.y);
+    r[4] = quad_lane<2>(c.x);
+    r[5] = quad_lane<2>(c.y);
+    r[6] = quad_lane<3>(c.x);
+    r[7] = quad_lane<3>(c.y);
+}
+// Entries (i, j), (i, j+1) into the transposed copy bt (row stride 8).
+__device__ __forceinline__ void put_t(float* bt, int i, int j, float2 v) {
+    bt[j * 8 + i] = v.x;
+    bt[(j + 1) * 8 + i] = v.y;
+}
+
 template <int NW>
 __device__ inline void diag_valu(float* M, float* scratch, int w) {
     constexpr int ld = kTriLd;
@@ -213,54 +241,59 @@ __device__ inline void diag_valu(float* M, float* scratch, int w) {
     asm volatile("" : "+v"(tl));
     const int lane = tl & 63, b = lane >> 5, i = (lane >> 2) & 7, j = 2 * (lane & 3);
     float* S = scratch + w * kDiagScratch;
-    float* N2 = S + 64 * b;  // this lane's block of each buffer, row stride 8
-    float* N3 = S + 128 + 64 * b;
-    float* N4 = S + 256 + 64 * b;
-    float* Db = S + 384;     // both blocks: D0 at 0, D1 at 64
-    float* Y = S + 512;      // L D0
+    float* N2t = S + 64 * b;        // this lane's block of N2 and N4, transposed
+    float* N4t = S + 128 + 64 * b;
+    float* D0t = S + 256;           // D0, transposed
+    float* Yt = S + 320;            // L D0, transposed
     for (int t = w; t < 4; t += NW) {
         float* Mt = M + 16 * t * ld + 16 * t;
         const float* Mb = Mt + 8 * b * ld + 8 * b;  // block b of the tile in A
-        float n[8], c0[8], c1[8];
+        float n[8], c0[8], c1[8], l[8];
         row8(Mb, ld, i, n);
         cols8(Mb, ld, j, c0, c1);
+        row8(Mt + 8 * ld, ld, i, l);  // row i of the tile's lower-left block
 #pragma unroll
         for (int k = 0; k < 8; ++k) {  // N: the block's strictly lower part
             n[k] = k < i ? n[k] : 0.f;
             c0[k] = j < k ? c0[k] : 0.f;
             c1[k] = j + 1 < k ? c1[k] : 0.f;
         }
-        *reinterpret_cast<float2*>(&N2[8 * i + j]) = dot8(n, c0, c1);
+        const float2 nown = make_float2(c0[i], c1[i]);  // N_ij, N_i,j+1
+        const float2 n2 = dot8(n, c0, c1);
+        put_t(N2t, i, j, n2);
         wave_sync();
         float r2[8];
-        row8(N2, 8, i, r2);
-        cols8(N2, 8, j, c0, c1);
-        *reinterpret_cast<float2*>(&N3[8 * i + j]) = dot8(n, c0, c1);
-        *reinterpret_cast<float2*>(&N4[8 * i + j]) = dot8(r2, c0, c1);
+        quad_row(n2, r2);
+        row8(N2t, 8, j, c0);
+        row8(N2t, 8, j + 1, c1);
+        const float2 n3 = dot8(n, c0, c1);
+        const float2 n4 = dot8(r2, c0, c1);
+        put_t(N4t, i, j, n4);
         wave_sync();
-        float x[8];
-        row8(N3, 8, i, x);
+        float r3[8], x[8];
+        quad_row(n3, r3);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = ((k == i ? 1.f : 0.f) - n[k]) + (r2[k] - x[k]);
-        cols8(N4, 8, j, c0, c1);
+        for (int k = 0; k < 8; ++k) x[k] = ((k == i ? 1.f : 0.f) - n[k]) + (r2[k] - r3[k]);
+        row8(N4t, 8, j, c0);
+        row8(N4t, 8, j + 1, c1);
         const float2 xn4 = dot8(x, c0, c1);
-        const float2 d = make_float2(x[j] + xn4.x, x[j + 1] + xn4.y);
-        *reinterpret_cast<float2*>(&Db[64 * b + 8 * i + j]) = d;
+        const float2 d = make_float2((((i == j ? 1.f : 0.f) - nown.x) + (n2.x - n3.x)) + xn4.x,
+                                     (((i == j + 1 ? 1.f : 0.f) - nown.y) + (n2.y - n3.y)) + xn4.y);
         *reinterpret_cast<float2*>(&Mt[(8 * b + i) * ld + 8 * b + j]) = d;
+        if (!b) put_t(D0t, i, j, d);
         wave_sync();
-        // level 8 (both halves of the wave compute it; block 1's lanes keep it)
-        float l[8];
-        row8(Mt + 8 * ld, ld, i, l);
-        cols8(Db, 8, j, c0, c1);
-        const float2 y = dot8(l, c0, c1);
-        if (b) *reinterpret_cast<float2*>(&Y[8 * i + j]) = y;
+        row8(D0t, 8, j, c0);
+        row8(D0t, 8, j + 1, c1);
+        const float2 y = dot8(l, c0, c1);  // L D0 (both halves; block 1's lanes keep it)
+        if (b) put_t(Yt, i, j, y);
         wave_sync();
-        float d1[8];
-        row8(Db + 64, 8, i, d1);
-        cols8(Y, 8, j, c0, c1);
-        const float2 z = dot8(d1, c0, c1);
+        float dr[8];
+        quad_row(d, dr);                   // row i of D1 on block 1's lanes
+        row8(Yt, 8, j, c0);
+        row8(Yt, 8, j + 1, c1);
+        const float2 z = dot8(dr, c0, c1);
         if (b) *reinterpret_cast<float2*>(&Mt[(8 + i) * ld + j]) = make_float2(-z.x, -z.y);
-        wave_sync();  // the scratch is reused by the next tile
+        if constexpr (NW < 4) wave_sync();  // the scratch is reused by the next tile
     }
 }
 
