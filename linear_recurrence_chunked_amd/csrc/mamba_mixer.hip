@@ -22,7 +22,7 @@
 //   * B and C of a 64-row chunk are staged in LDS by the workgroup (the next
 //     chunk's rows load into registers while the current chunk computes);
 //     every lane of a part reads the same LDS address (a broadcast).
-//   * x and dt move through a register ring of two 4-row groups, loaded one
+//   * x and dt move through a register ring of two 16-row groups, loaded one
 //     group ahead; loads past the prompt re-read its last row and those rows
 //     are never computed, so the state stops at the prompt's last row.
 #include "lrc_device.h"
@@ -37,7 +37,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanes = LRC_MIXER_LANES;  // lanes per channel when d_state allows (2 or 4)
 constexpr int kChunk = 64;             // rows of B and C staged per chunk
-constexpr int kGroup = 4;              // rows of x and dt per register group
+// Rows of x and dt per register group; a full group is straight-line code,
+// so the longer it is, the more rows' reads and exponentials are in flight
+// while the state chain runs (two groups per chunk at most: the ring
+// alternates within a chunk).
+constexpr int kGroup = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Sum over the LPD lanes (1, 2 or 4 consecutive lanes of a quad) that share a channel.
@@ -117,40 +121,58 @@ __global__ __launch_bounds__(kThreads) void mamba_mixer_kernel(const float* __re
             ts[i] = tp[off];
         }
     };
-    // Rows g0 .. g0+n-1 of the prompt; their B, C sit at rows rb .. of LDS buffer buf.
-    auto rows = [&](int g0, int n, int buf, int rb, const float (&xs)[kGroup], const float (&ts)[kGroup]) {
-        float* yp = y + (row0 + g0) * Dm + d;
+    // Row i of a group (its B, C at row rb + i of LDS buffer buf): advances the
+    // lane's states and returns the channel's output y (complete on part 0).
+    auto row = [&](int i, int buf, int rb, const float (&xs)[kGroup], const float (&ts)[kGroup]) {
+        const float* bcr = &bc[buf][rb + i][0];
+        float bv[NP], cv[NP];
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-            if (i >= n) break;
-            const float* bcr = &bc[buf][rb + i][0];
-            float bv[NP], cv[NP];
+        for (int n4 = 0; n4 < NP; n4 += (NP >= 4 ? 4 : NP)) {
+            if (NP >= 4) {
+                const float4 b4 = *reinterpret_cast<const float4*>(bcr + part * NP + n4);
+                const float4 c4 = *reinterpret_cast<const float4*>(bcr + N + part * NP + n4);
+                bv[n4] = b4.x; bv[n4 + 1] = b4.y; bv[n4 + 2] = b4.z; bv[n4 + 3] = b4.w;
+                cv[n4] = c4.x; cv[n4 + 1] = c4.y; cv[n4 + 2] = c4.z; cv[n4 + 3] = c4.w;
+            } else {
 #pragma unroll
-            for (int n4 = 0; n4 < NP; n4 += (NP >= 4 ? 4 : NP)) {
-                if (NP >= 4) {
-                    const float4 b4 = *reinterpret_cast<const float4*>(bcr + part * NP + n4);
-                    const float4 c4 = *reinterpret_cast<const float4*>(bcr + N + part * NP + n4);
-                    bv[n4] = b4.x; bv[n4 + 1] = b4.y; bv[n4 + 2] = b4.z; bv[n4 + 3] = b4.w;
-                    cv[n4] = c4.x; cv[n4 + 1] = c4.y; cv[n4 + 2] = c4.z; cv[n4 + 3] = c4.w;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < NP; ++q) {
-                        bv[q] = bcr[part * NP + q];
-                        cv[q] = bcr[N + part * NP + q];
-                    }
+                for (int q = 0; q < NP; ++q) {
+                    bv[q] = bcr[part * NP + q];
+                    cv[q] = bcr[N + part * NP + q];
                 }
             }
-            const float dtv = ts[i], xv = xs[i];
-            const float dtx = dtv * xv;
-            float acc = 0.f;
+        }
+        const float dtv = ts[i], xv = xs[i];
+        const float dtx = dtv * xv;
+        float acc = 0.f;
 #pragma unroll
-            for (int q = 0; q < NP; ++q) {
-                const float a = __builtin_amdgcn_exp2f(dtv * a2[q]);
-                h[q] = fmaf(a, h[q], dtx * bv[q]);
-                acc = fmaf(cv[q], h[q], acc);
+        for (int q = 0; q < NP; ++q) {
+            const float a = __builtin_amdgcn_exp2f(dtv * a2[q]);
+            h[q] = fmaf(a, h[q], dtx * bv[q]);
+            acc = fmaf(cv[q], h[q], acc);
+        }
+        acc = lanes_sum<LPD>(acc);
+        return fmaf(dd, xv, acc);
+    };
+    // Rows g0 .. g0+n-1 of the prompt.  A full group is straight-line code with
+    // its stores at the end, so the reads and exponentials of later rows can be
+    // issued while the earlier rows' chains run; only a prompt's last group can
+    // be partial.
+    auto rows = [&](int g0, int n, int buf, int rb, const float (&xs)[kGroup], const float (&ts)[kGroup]) {
+        float* yp = y + (row0 + g0) * Dm + d;
+        if (n == kGroup) {
+            float out[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) out[i] = row(i, buf, rb, xs, ts);
+            if (part == 0 && valid)
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) yp[(long)i * Dm] = out[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                if (i >= n) break;
+                const float o = row(i, buf, rb, xs, ts);
+                if (part == 0 && valid) yp[(long)i * Dm] = o;
             }
-            acc = lanes_sum<LPD>(acc);
-            if (part == 0 && valid) yp[(long)i * Dm] = fmaf(dd, xv, acc);
         }
     };
 
