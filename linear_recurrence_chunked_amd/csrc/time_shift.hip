@@ -22,15 +22,23 @@
 namespace lrc {
 namespace {
 
-constexpr int kThreads = 256;
+// One wave per workgroup: at C = 2560 a row is 640 threads of 4 channels, ten
+// whole workgroups of 64 where workgroups of 256 left half of the third idle,
+// and the tiles of short and long prompts spread more evenly (0.263 -> 0.251 ms
+// on the mixed prefill lengths).
+constexpr int kThreads = 64;
 constexpr int kTile = 16;
 constexpr int kUnroll = 8;
+
+// The 16-byte accesses are nontemporal: each row is read, and each output row
+// written, once.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int VEC>
 __device__ __forceinline__ void ld(const float* p, int nc, float* v) {
     if (VEC == 4) {
-        const float4 q = *reinterpret_cast<const float4*>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
     } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[i] = i < nc ? p[i] : 0.f;
@@ -40,7 +48,7 @@ __device__ __forceinline__ void ld(const float* p, int nc, float* v) {
 template <int VEC>
 __device__ __forceinline__ void st(float* p, int nc, const float* v) {
     if (VEC == 4) {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
     } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i)
