@@ -400,7 +400,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
         constexpr int NP8 = 8 * DK / NT;  // 16-byte pieces of W, Q and K^T per loader thread
         static_assert(8 * DK % NT == 0 && 512 % NT == 0, "whole 16-byte pieces per loader thread");
         u32x4 rw[NP8], rk[NP8], rq[NP8], rp[512 / NT];
-        float rdec = 0.f, rgam = 0.f;
+        float rdec = 0.f, rgam = 0.f, rgs = 0.f;
         // loads into registers (all in flight together), LDS stores one iteration later
         auto issue_wk = [&](int n) __attribute__((always_inline)) {
             const auto brs = buffer_rsrc(block(n), (uint32_t)Blk::BYTES);
@@ -411,6 +411,9 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 rk[x] = __builtin_amdgcn_raw_buffer_load_b128(brs, (uint32_t)(Blk::KT + e * 16), 0, 0);  // [DK][64]
             }
             rdec = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, (uint32_t)(Blk::DEC + lt * 4), 0, 0));
+            // e^{gamma_S} of chunk n: the Gamma of its last row
+            const int S = min(64, L - 64 * n);
+            rgs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(brs, (uint32_t)(Blk::GAM + (S - 1) * 4), 0, 0));
         };
         auto commit_wk = [&](int n) __attribute__((always_inline)) {
             const int b = n & 1;
@@ -421,6 +424,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 *reinterpret_cast<u32x4*>(&sm.KT[b][(e >> 3) * Sm::LT + (e & 7) * 8]) = rk[x];
             }
             if (lt < 64) sm.dec[b][lt] = rdec;
+            if (lt == 0) sm.GS[b] = rgs;
         };
         auto issue_qp = [&](int n) __attribute__((always_inline)) {
             const int S = min(64, L - 64 * n);
@@ -451,24 +455,13 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
             }
             if (lt < 64) sm.Gam[b][lt] = rgam;
         };
-        // e^{gamma_S} of chunk n: the Gamma of its last row
-        auto commit_gs = [&](int n) __attribute__((always_inline)) {
-            if (lt == 0) {
-                const int S = min(64, L - 64 * n);
-                sm.GS[n & 1] = reinterpret_cast<const float*>(block(n) + Blk::GAM)[S - 1];
-            }
-        };
         issue_wk(0);
         commit_wk(0);
-        commit_gs(0);
         if (nc > 1) issue_wk(1);
         issue_qp(0);
         __syncthreads();
         for (int n = 0; n <= nc; ++n) {
-            if (n + 1 < nc) {
-                commit_wk(n + 1);
-                commit_gs(n + 1);
-            }
+            if (n + 1 < nc) commit_wk(n + 1);
             if (n < nc) commit_qp(n);
             if (n + 2 < nc) issue_wk(n + 2);
             if (n + 1 < nc) issue_qp(n + 1);
@@ -554,6 +547,22 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
     for (int n = 0; n <= nc; ++n) {
         if (n < nc) {
             const int b = n & 1;
+            // All fragments of W and K^T of chunk n, and its decays, are in LDS since
+            // the last barrier: one wave per SIMD has the registers to read them all
+            // at once, W's first, so that the chain below waits for LDS only once.
+            bf16x8 wf[KS][4], kt[2][RT];
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) wf[s][t] = frag(&sm.W[b][(16 * t + lr) * LDK + 32 * s + 8 * lg]);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int tr = 0; tr < RT; ++tr) kt[s][tr] = frag(&sm.KT[b][(16 * tr + lr) * Sm::LT + 32 * s + 8 * lg]);
+            floatx4 dec4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) dec4[t] = *reinterpret_cast<const floatx4*>(&sm.dec[b][16 * t + lq]);
+            const float GS = sm.GS[b];
             // ---- W S_0, with S_0 handed to the output wave as B fragments
             floatx4 ws0[4], u[4];
 #pragma unroll
@@ -564,10 +573,8 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 acc_frag<false>(sacc[2 * s], sacc[2 * s + 1], bh, bl);
                 sm.xs[b][pair][s][lane] = bh;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    ws0[t] = mfma(frag(&sm.W[b][(16 * t + lr) * LDK + 32 * s + 8 * lg]), bh, ws0[t]);
+                for (int t = 0; t < 4; ++t) ws0[t] = mfma(wf[s][t], bh, ws0[t]);
             }
-            read_ahead<4 * KS, 1, 1, 2>();
             // ---- U = U' - W S_0 (zero past the chunk: W and U' rows are zero there)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -575,7 +582,6 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 for (int r = 0; r < 4; ++r) u[t][r] = up[4 * t + r] - ws0[t][r];
             if (n + 1 < nc) load_up(n + 1);
             // ---- U to the output wave; S_S = e^{gamma_S} S_0 + K^T (decay U)
-            const float GS = sm.GS[b];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 bf16x8 bh, bl;
@@ -583,7 +589,7 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 sm.xu[b][pair][s][lane] = bh;
             }
 #pragma unroll
-            for (int t = 0; t < 4; ++t) u[t] *= *reinterpret_cast<const floatx4*>(&sm.dec[b][16 * t + lq]);
+            for (int t = 0; t < 4; ++t) u[t] *= dec4[t];
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) sacc[tr] = sacc[tr] * GS;
 #pragma unroll
@@ -591,10 +597,8 @@ __global__ __launch_bounds__(64 * (2 * NSW + kCpLoaders), 1) void gdn_cp_state_k
                 bf16x8 bh, bl;
                 acc_frag<false>(u[2 * s], u[2 * s + 1], bh, bl);
 #pragma unroll
-                for (int tr = 0; tr < RT; ++tr)
-                    sacc[tr] = mfma(frag(&sm.KT[b][(16 * tr + lr) * Sm::LT + 32 * s + 8 * lg]), bh, sacc[tr]);
+                for (int tr = 0; tr < RT; ++tr) sacc[tr] = mfma(kt[s][tr], bh, sacc[tr]);
             }
-            read_ahead<2 * RT, 1, 1, 2>();
         }
         __syncthreads();
     }
