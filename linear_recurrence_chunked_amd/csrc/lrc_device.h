@@ -39,14 +39,8 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// bf16 <-> fp32.  The narrowing rounds to nearest even (NaN stays NaN).
+// bf16 -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
-}
 
 // Raw buffer resource over `bytes` bytes from p (stride 0, 32-bit data
 // format, the gfx9 descriptor word).  Loads whose per-lane offset lies past
