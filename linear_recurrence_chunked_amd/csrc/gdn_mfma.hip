@@ -13,7 +13,8 @@
 // Work split.  One workgroup owns a whole value head of one prompt, or of a
 // lane of prompts run back to back (see the launcher), and walks their
 // chunks.  It holds two kinds of waves, which run the same sequence of
-// workgroup barriers, five per step (segments A .. E):
+// workgroup barriers, five per step in the split form (segments A .. E) and
+// four in the default form, where C and D are one segment:
 //  * dv/32 state waves, each owning 32 columns of the [dk x dv] state in MFMA
 //    accumulators, swapped at each prompt boundary.  In step n they run the
 //    chain that depends on the state for chunk n: K S_0, Q S_0 and the
@@ -28,7 +29,9 @@
 //  * 4 prep waves, which in step n prepare chunk n+1, the part that does not
 //    depend on the state: the inverse (diagonal tiles in A, level 16 in B,
 //    level 32 in C and D, each tile of T rounded to bf16 once final) and, in
-//    the split form, P (D).  They stage chunk n+2 into LDS and keep the rows
+//    the split form, P (D).  In the default form each prep wave forms the
+//    tiles of level 32's Y that its tile of T needs itself, in registers, so
+//    level 32 needs no barrier inside.  They stage chunk n+2 into LDS and keep the rows
 //    of chunk n+3 in flight: in the default form prep waves 2 and 3, idle
 //    during level 16, in B and waves 0 and 1, whose level-32 tiles are the
 //    lighter ones, in D; in the split form all four in C.  They form the six
@@ -38,7 +41,8 @@
 // and which prompt they belong to, one copy of A -> T (FP32), T (bf16) and
 // K^T, and P (bf16) by chunk parity (one copy, with its lo parts, in the
 // split form): each is written in a segment where no wave reads the copy it
-// replaces.  About 156 KiB in either form, one workgroup per CU.
+// replaces.  About 148 KiB (156 KiB in the split form, which keeps Y in
+// LDS), one workgroup per CU.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16, FP32 accumulation.  The A operand
 // of lane l is row l%16 with 8 k-values, the B operand column l%16 with the
@@ -100,7 +104,7 @@ struct PipeSmem {
     __bf16 P_hi[NPB][64 * LT];  // masked decayed Q K^T
     __bf16 P_lo[LO];
     float M[64 * kTriLd];   // A, then T, in FP32
-    float scratch[kTriScratch];
+    float scratch[SPLIT ? kTriScratch : 4];  // Y of level 32 (the default form keeps it in registers)
     alignas(16) float dscratch[kPrep * tri::kDiagScratch];  // the diagonal tiles' 8x8 products
     float gam[3][64];       // per-row values, by chunk index mod 3
     float Gam[3][64];       // e^gamma
@@ -163,6 +167,71 @@ __device__ __forceinline__ void split_tile(const float* M, __bf16* hi, __bf16* l
     split4(x, h, l);
     *reinterpret_cast<bf16x4*>(&hi[r * LT + kperm(c)]) = h;
     if constexpr (SPLIT) *reinterpret_cast<bf16x4*>(&lo[r * LT + kperm(c)]) = l;
+}
+
+// Level 32 of the inverse, tile (TA, TB) of T21 = -T22 Y, Y = L21 T11, for
+// one wave with no barrier: the wave forms the tiles of Y it needs itself and
+// keeps them in registers (accumulator layout), then forms its tile of T21 as
+// the transposed product Y^T T22^T, whose accumulator layout is T21's row
+// layout, and writes it to T in bf16.  M is only read, so the four tiles need
+// no ordering between waves; the FP32 T21 is never stored.
+template <int TA, int TB, int LT>
+__device__ __forceinline__ void lvl32_tile(const float* M, __bf16* T_hi) {
+    using MM = tri::MmBf16Split;
+    constexpr int ld = kTriLd;
+    int lr, g;
+    tri::lanes(lr, g);
+    const tri_f4 zero = {0.f, 0.f, 0.f, 0.f};
+    tri_f4 y[TA + 1];
+#pragma unroll
+    for (int c = 0; c <= TA; ++c) {  // Y(c, TB); T11 is block lower triangular
+        y[c] = zero;
+#pragma unroll
+        for (int l = TB; l < 2; ++l)
+            y[c] = MM::mm(y[c], tri::ld_row(M + (32 + 16 * c) * ld + 16 * l, ld, lr, g),
+                          tri::ld_acc(M + 16 * l * ld + 16 * TB, ld, lr, g));
+    }
+    tri_f4 acc = zero;
+#pragma unroll
+    for (int c = 0; c <= TA; ++c)  // T22 is block lower triangular
+        acc = MM::mm(acc, y[c], tri::ld_row(M + (32 + 16 * TA) * ld + 32 + 16 * c, ld, lr, g));
+    bf16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = static_cast<__bf16>(-acc[r]);
+    *reinterpret_cast<bf16x4*>(&T_hi[(32 + 16 * TA + lr) * LT + kperm(16 * TB + 4 * g)]) = h;
+}
+template <int LT>
+__device__ __forceinline__ void lvl32_direct(const float* M, __bf16* T_hi, int pw) {
+    if (pw == 0) lvl32_tile<0, 0, LT>(M, T_hi);
+    else if (pw == 1) lvl32_tile<0, 1, LT>(M, T_hi);
+    else if (pw == 2) lvl32_tile<1, 0, LT>(M, T_hi);
+    else lvl32_tile<1, 1, LT>(M, T_hi);
+}
+
+// K^T of the chunk in K buffer b into KT, by blocks of 4 rows x 8 stored
+// columns, blocks t, t + stride, ...
+template <int DK, class Sm>
+__device__ __forceinline__ void build_kt(Sm& sm, int b, int t, int stride) {
+    constexpr int LDK = Sm::LDK, LT = Sm::LT;
+    for (int x = t; x < 2 * DK; x += stride) {
+        // rows 4nn .. 4nn+3, stored columns 8m .. 8m+7 (dk indices kperm_inv of them)
+        const int nn = x & 15, m = x >> 4;
+        uint4 rw[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) rw[a] = *reinterpret_cast<const uint4*>(&sm.K[b][(4 * nn + a) * LDK + 8 * m]);
+        const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
+        const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
+        const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
+        const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
+            uint2 out;
+            out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
+            out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
+            *reinterpret_cast<uint2*>(&sm.KT[kperm_inv(8 * m + e) * LT + kperm(4 * nn)]) = out;
+        }
+    }
 }
 
 // Masked decayed K K^T of the chunk in buffers (b, rbuf) -> A in M: tile
@@ -566,7 +635,8 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                     }
                 }
             }
-            __syncthreads();
+            // the default form runs C and D as one segment (the prep waves' level 32 needs no barrier there)
+            if constexpr (SPLIT) __syncthreads();
 
             // ---- D: S_S = e^{gamma_S} S_0 + K^T (decS U)
             if (do_state) {
@@ -610,28 +680,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 }
             }
             if (n + 2 < nc) kk_state<DK, NS>(sm, cb, (n + 5) % 3, w);
-            if (do_next) {
-                for (int b = tid; b < 2 * DK; b += 64 * NS) {
-                    // rows 4nn .. 4nn+3, stored columns 8m .. 8m+7 (dk indices kperm_inv of them)
-                    const int nn = b & 15, m = b >> 4;
-                    uint4 rw[4];
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        rw[a] = *reinterpret_cast<const uint4*>(&sm.K[nb][(4 * nn + a) * LDK + 8 * m]);
-                    const uint32_t d0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
-                    const uint32_t d1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
-                    const uint32_t d2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
-                    const uint32_t d3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two dwords
-                        uint2 out;
-                        out.x = __builtin_amdgcn_perm(d1[e >> 1], d0[e >> 1], sel);
-                        out.y = __builtin_amdgcn_perm(d3[e >> 1], d2[e >> 1], sel);
-                        *reinterpret_cast<uint2*>(&sm.KT[kperm_inv(8 * m + e) * LT + kperm(4 * nn)]) = out;
-                    }
-                }
-            }
+            if (do_next) build_kt<DK>(sm, nb, tid, 64 * NS);
             __syncthreads();
         }
         // Prompts without rows keep their state.
@@ -776,35 +825,38 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 }
             __syncthreads();
 
-            // ---- C: level 32 (first half); the tiles of T that are final go to bf16;
-            //      in the split form, chunk n+2 into the buffers chunk n used and
-            //      chunk n+3 in flight (in D in the default form)
+            // ---- C: level 32 (in the split form its first half); the tiles of T that
+            //      are final go to bf16; in the split form, chunk n+2 into the buffers
+            //      chunk n used and chunk n+3 in flight
             if (do_next) {
-                tri::lvl32a<kPrep, InvMM>(sm.M, sm.scratch, pw);
+                if constexpr (SPLIT) tri::lvl32a<kPrep, InvMM>(sm.M, sm.scratch, pw);
+                else lvl32_direct<LT>(sm.M, sm.T_hi, pw);
                 split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, pw, pw, lane);
                 if (pw == 0) split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 1, 0, lane);
                 if (pw == 1) split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 3, 2, lane);
             }
-            if constexpr (SPLIT)
+            if constexpr (SPLIT) {
                 if (do_stage) {
                     stage(n & 1, (n + 5) % 3);
                     if (n + 3 < nc) fetch(n + 3);
                 }
-            __syncthreads();
+                __syncthreads();
 
-            // ---- D: level 32 (second half) and its tile of T; in the split form P
-            //      of chunk n+1, in the default form the other half of the staging
-            if (do_next) {
-                tri::lvl32b<kPrep, InvMM>(sm.M, sm.scratch, pw);
-                tri::wave_sync();
-                split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
-                if constexpr (SPLIT) masked_qk(nb, nrb);
-            }
-            if constexpr (!SPLIT)
+                // ---- D (split form): level 32 (second half) and its tile of T; P of chunk n+1
+                if (do_next) {
+                    tri::lvl32b<kPrep, InvMM>(sm.M, sm.scratch, pw);
+                    tri::wave_sync();
+                    split_tile<SPLIT, LT>(sm.M, sm.T_hi, sm.T_lo, 2 + (pw >> 1), pw & 1, lane);
+                    masked_qk(nb, nrb);
+                }
+            } else {
+                // the default form's D is this same segment: prep waves 0 and 1 stage their
+                // half of chunk n+2 and put their part of chunk n+3 in flight
                 if (do_stage && pw < 2) {
                     stage(n & 1, (n + 5) % 3);
                     if (n + 3 < nc) fetch(n + 3);
                 }
+            }
             __syncthreads();
 
             // ---- E: A of chunk n+2 into M (T of chunk n+1 is in bf16 now)
