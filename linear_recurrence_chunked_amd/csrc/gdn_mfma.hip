@@ -535,6 +535,10 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                                                : __uint_as_float(pv[4 * t + r] << 16);
                             ks0[c][t][r] = b4[r] * (vv - G4[r] * ks0[c][t][r]);
                         }
+                    // diag(Gamma) Q S_0 is where the accumulation of O starts (segment C)
+                    if constexpr (!SPLIT)
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) qs0[c][t] *= G4;
                 }
             }
             if (do_next) {
@@ -591,11 +595,17 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
 
             // ---- C: O = diag(Gamma) Q S_0 + P U
             if (do_state) {
-                floatx4 pu[CG][4];
+                // the default form accumulates P U onto diag(Gamma) Q S_0 (scaled in A)
+                floatx4 pu_split[SPLIT ? CG : 1][4];
+                auto& pu = [&]() -> auto& {
+                    if constexpr (SPLIT) return pu_split;
+                    else return qs0;
+                }();
+                if constexpr (SPLIT)
 #pragma unroll
-                for (int c = 0; c < CG; ++c)
+                    for (int c = 0; c < CG; ++c)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) pu[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                        for (int t = 0; t < 4; ++t) pu[c][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     bf16x8 bh[CG], bl[CG];
@@ -626,11 +636,20 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                 asm volatile("" : "+v"(o_lane));
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[rb][16 * t + lq]);
+                    floatx4 o4[CG];
+                    if constexpr (SPLIT) {
+                        const floatx4 G4 = *reinterpret_cast<const floatx4*>(&sm.Gam[rb][16 * t + lq]);
+#pragma unroll
+                        for (int c = 0; c < CG; ++c)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) o4[c][r] = fmaf(G4[r], qs0[c][t][r], pu[c][t][r]);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < CG; ++c) o4[c] = pu[c][t];
+                    }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const u32x2 pair = {__float_as_uint(fmaf(G4[r], qs0[0][t][r], pu[0][t][r])),
-                                            __float_as_uint(fmaf(G4[r], qs0[1][t][r], pu[1][t][r]))};
+                        const u32x2 pair = {__float_as_uint(o4[0][r]), __float_as_uint(o4[1][r])};
                         __builtin_amdgcn_raw_buffer_store_b64(pair, orsrc, o_lane + (16 * t + r) * rowV * 4, 0, kNontemporal);
                     }
                 }
@@ -640,17 +659,19 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
 
             // ---- D: S_S = e^{gamma_S} S_0 + K^T (decS U)
             if (do_state) {
-                const float GS = sm.Gam[rb][Sn - 1];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sm.decS[rb][16 * t + lq]);
 #pragma unroll
                     for (int c = 0; c < CG; ++c) u[c][t] *= d4;
                 }
+                {
+                    const float GS = sm.Gam[rb][Sn - 1];
 #pragma unroll
-                for (int c = 0; c < CG; ++c)
+                    for (int c = 0; c < CG; ++c)
 #pragma unroll
-                    for (int tr = 0; tr < RT; ++tr) sacc[c][tr] = sacc[c][tr] * GS;
+                        for (int tr = 0; tr < RT; ++tr) sacc[c][tr] = sacc[c][tr] * GS;
+                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     bf16x8 bh[CG], bl[CG];
