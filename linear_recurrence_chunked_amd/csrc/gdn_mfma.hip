@@ -350,7 +350,7 @@ __device__ __forceinline__ void qk_group(Sm& sm, int b, int rbuf, __bf16* P) {
 #pragma unroll
         for (int x = 0; x < NT; ++x) acc[x] = mfma(a, frag(&sm.Q[b][(16 * (TI0 + x) + lr) * LDK + 32 * s + lk]), acc[x]);
     }
-    read_ahead<KS, NT + 1, NT, (KS < 2 ? KS : 2)>();
+    read_ahead<KS, NT + 1, NT, (KS < 3 ? KS : 3)>();
 #pragma unroll
     for (int x = 0; x < NT; ++x) {
         const floatx4 pv4 = tile_decay(sm.gam[rbuf], TI0 + x, TJ, lr, lq) * acc[x];
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                         }
                     }
                 }
-                read_ahead<4 * KS, 2, 2 * PS * CG, 2>();
+                read_ahead<4 * KS, 2, 2 * PS * CG, SPLIT ? 2 : 3>();
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     const floatx4 b4 = *reinterpret_cast<const floatx4*>(&sm.beta[rb][16 * t + lq]);
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                         }
                     }
                 }
-                read_ahead<6, SPLIT ? 2 : 1, (SPLIT ? 3 : 1) * CG, 2>();
+                read_ahead<6, SPLIT ? 2 : 1, (SPLIT ? 3 : 1) * CG, SPLIT ? 2 : 3>();
                 // Through a buffer resource that ends after the chunk's Sn rows: the
                 // stores of rows past it are dropped, with no per-row test.
                 Sn = meta(n, 1);
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
                         }
                     }
                 }
-                read_ahead<2 * RT, SPLIT ? 2 : 1, PS * CG, 2>();
+                read_ahead<2 * RT, SPLIT ? 2 : 1, PS * CG, SPLIT ? 2 : 4>();
             }
             __syncthreads();
 
