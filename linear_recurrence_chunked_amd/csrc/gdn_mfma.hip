@@ -832,7 +832,7 @@ __global__ __launch_bounds__(64 * (NS + kPrep), 1) void gdn_pipe_kernel(const ui
             const int nb = (n + 1) & 1, nrb = (n + 4) % 3;  // buffers of chunk n+1
 
             // ---- A: diagonal tiles of the inverse of chunk n+1
-            if (do_next) tri::diag_valu<kPrep>(sm.M, sm.dscratch, pw);
+            if (do_next) tri::diag_valu<kPrep, true>(sm.M, sm.dscratch, pw);  // A is zero on and above its diagonal
             __syncthreads();
 
             // ---- B: level 16 (prep waves 0, 1); in the default form prep waves 2, 3

@@ -234,7 +234,10 @@ __device__ __forceinline__ void put_t(float* bt, int i, int j, float2 v) {
     bt[(j + 1) * 8 + i] = v.y;
 }
 
-template <int NW>
+//   With ZERO_UPPER the caller guarantees that each diagonal tile of M is zero
+//   on and above its diagonal (A as the masked products write it), so N is
+//   the 8x8 block as it stands and the masking is skipped.
+template <int NW, bool ZERO_UPPER = false>
 __device__ inline void diag_valu(float* M, float* scratch, int w) {
     constexpr int ld = kTriLd;
     int tl = threadIdx.x;
@@ -252,12 +255,13 @@ __device__ inline void diag_valu(float* M, float* scratch, int w) {
         row8(Mb, ld, i, n);
         cols8(Mb, ld, j, c0, c1);
         row8(Mt + 8 * ld, ld, i, l);  // row i of the tile's lower-left block
+        if constexpr (!ZERO_UPPER)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {  // N: the block's strictly lower part
-            n[k] = k < i ? n[k] : 0.f;
-            c0[k] = j < k ? c0[k] : 0.f;
-            c1[k] = j + 1 < k ? c1[k] : 0.f;
-        }
+            for (int k = 0; k < 8; ++k) {  // N: the block's strictly lower part
+                n[k] = k < i ? n[k] : 0.f;
+                c0[k] = j < k ? c0[k] : 0.f;
+                c1[k] = j + 1 < k ? c1[k] : 0.f;
+            }
         const float2 nown = make_float2(c0[i], c1[i]);  // N_ij, N_i,j+1
         const float2 n2 = dot8(n, c0, c1);
         put_t(N2t, i, j, n2);
