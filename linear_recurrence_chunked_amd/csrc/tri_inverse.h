@@ -262,7 +262,12 @@ __device__ inline void diag_valu(float* M, float* scratch, int w) {
                 c0[k] = j < k ? c0[k] : 0.f;
                 c1[k] = j + 1 < k ? c1[k] : 0.f;
             }
-        const float2 nown = make_float2(c0[i], c1[i]);  // N_ij, N_i,j+1
+        // N_ij, N_i,j+1 as one read (indexing c0, c1 by the lane's i would be a chain of selects)
+        float2 nown = *reinterpret_cast<const float2*>(Mb + i * ld + j);
+        if constexpr (!ZERO_UPPER) {
+            nown.x = j < i ? nown.x : 0.f;
+            nown.y = j + 1 < i ? nown.y : 0.f;
+        }
         const float2 n2 = dot8(n, c0, c1);
         put_t(N2t, i, j, n2);
         wave_sync();
